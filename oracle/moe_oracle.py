@@ -1,0 +1,370 @@
+"""CPU oracle of the MoE-layer forward token path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or links
+this module: only the tests, the package smoke check and the benchmark's CPU
+baseline leg use it.  It shares no code with the HIP library (no kernels,
+headers, helpers, tables or pre/post-processing); the only thing both sides
+consume is the seeded input generator, which holds none of the method's
+arithmetic.
+
+Everything is plain NumPy in float64 (inputs given as bf16 or fp32 are widened
+exactly), written step by step in the order the method is stated, with no
+blocking, fusion or reordering.  The one deliberate fp32 operation is the
+score add s = fp32(z) + fp32(b) (see `scores`), because the routing decision is
+defined on fp32 scores and both sides must take it in the same precision.
+
+Pages cited (by title and section):
+  [EP-V4]    "DeepSeek-V4的Expert Parallelism与计算通信遮掩实战解析" (tqpw.cn)
+  [ThunderEP] ThunderEP article on MoE expert parallelism over PCIe (discosf.com),
+             section 2 "MoE专家并行的通信本质"
+  [V4-overlap] "DeepSeek-v4 Parallel comp-comm overlap" (recsys-frontier blog),
+             sections "先让 EP 在 IB 网络上跑起来" and "V4 的 Waved-EP 通信计算遮掩"
+  [SyncTax]  "Deepseek-MoE同步税本质与四层实战优化指南" (qwbw.cn)
+
+Readings taken where the pages are silent or disagree (each is also listed in
+the design notes): ties go to the lowest expert / group index; selection is on
+fp32 scores, -0 equal to +0; the group score is the max over the group;
+groups and expert-to-rank blocks are contiguous; the order inside an expert's
+segment is ascending token index; no capacity limit (dropless); SwiGLU is
+SiLU(x Wg^T) * (x Wu^T) then W_down; without renormalisation and without
+pre-selection the gate denominator runs over all E experts.
+
+Parity pins: every function here is pinned by `-m "not gpu"` tests against
+closed forms, hand-worked cases, brute force or library routines; none is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import itertools
+from fractions import Fraction
+
+import numpy as np
+
+__all__ = [
+    "widen_bf16", "router_logits", "scores", "select", "gates", "margins", "route",
+    "permute", "silu", "expert_ffn", "grouped_ffn", "combine", "layer",
+    "select_bruteforce", "dense_bruteforce",
+]
+
+
+# ----------------------------------------------------------------------------
+# input widening
+# ----------------------------------------------------------------------------
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64, exactly (bf16 is the top half of fp32)."""
+    b = np.asarray(bits)
+    if b.dtype != np.uint16:
+        raise TypeError("widen_bf16 expects uint16 bit patterns")
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _f64(a) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return widen_bf16(a)
+    return a.astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# a1: router gate GEMM
+# ----------------------------------------------------------------------------
+def router_logits(x, w_router) -> np.ndarray:
+    """z[t, e] = sum_i x[t, i] * Wr[e, i], in float64.
+
+    Every machine computes the gate logits of a token over the experts before
+    choosing top-k ([EP-V4] §2.1; [SyncTax] §2.1 gating network).
+    """
+    return _f64(x) @ _f64(w_router).T
+
+
+# ----------------------------------------------------------------------------
+# a2: scores, selection, gates
+# ----------------------------------------------------------------------------
+def scores(z32, bias=None) -> np.ndarray:
+    """s = fp32(z) + fp32(b) as one IEEE single-precision add, then -0 -> +0.
+
+    The per-expert bias is added to the router logits before selection and
+    softmax (the workloads' "router logits given a per-expert bias").  The
+    result stays float32: the routing decision is defined on these values.
+    """
+    s = np.asarray(z32, dtype=np.float32)
+    if bias is not None:
+        s = s + np.asarray(bias, dtype=np.float32)[None, :]
+    return s + np.float32(0.0)  # -0.0 + +0.0 = +0.0 under round-to-nearest
+
+
+def _order_desc(v: np.ndarray) -> np.ndarray:
+    """Per row, indices ordered by (value descending, index ascending)."""
+    return np.argsort(-v, axis=-1, kind="stable")
+
+
+def _eligible(s: np.ndarray, n_group: int, topk_group: int) -> np.ndarray:
+    """Mask of experts inside the kept groups (group-limited routing).
+
+    Experts form n_group contiguous groups; a group's score is the max of its
+    experts' scores; the `topk_group` best groups by (score desc, group asc)
+    are kept and all other experts are excluded ([V4-overlap], "先让 EP 在 IB
+    网络上跑起来": the 8 experts may only come from the best 4 nodes).
+    """
+    T, E = s.shape
+    if n_group <= 1 or topk_group >= n_group:
+        return np.ones((T, E), dtype=bool)
+    gs = E // n_group
+    group_score = s.reshape(T, n_group, gs).max(axis=2)
+    kept = _order_desc(group_score)[:, :topk_group]
+    gmask = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(gmask, kept, True, axis=1)
+    return np.repeat(gmask, gs, axis=1)
+
+
+def select(s, k: int, n_group: int = 1, topk_group: int = 1, presel: int = 0) -> np.ndarray:
+    """Experts in order (s desc, e asc) among the eligible ones.
+
+    Returns the first max(k, presel) indices per token, best first: the first k
+    are the chosen experts, the first `presel` the partial top-P set over which
+    the softmax is taken ([EP-V4] §3.2: partial sort to the top-8 logits).
+    """
+    s = np.asarray(s, dtype=np.float32)
+    elig = _eligible(s, n_group, topk_group)
+    key = np.where(elig, s.astype(np.float64), -np.inf)
+    return _order_desc(key)[:, : max(k, presel)]
+
+
+def gates(s, sel, k: int, presel: int = 0, renorm: int = 1) -> np.ndarray:
+    """Softmax gate weights of the k chosen experts, float64.
+
+    m is the best score (max subtraction before the exponential, [EP-V4] §3.2);
+    e_j = exp(s_j - m).  renorm=1: g_j = e_j / sum over the k chosen.
+    presel=P, renorm=0: g_j = e_j / sum over the P pre-selected ([EP-V4] §3.2:
+    exact softmax over only the top-8, then take the top-2).
+    presel=0, renorm=0: the denominator runs over all E experts.
+    """
+    s64 = np.asarray(s, dtype=np.float32).astype(np.float64)
+    top = np.take_along_axis(s64, sel, axis=1)
+    m = top[:, :1]
+    e = np.exp(top - m)
+    if renorm:
+        denom = e[:, :k].sum(axis=1)
+    elif presel:
+        denom = e[:, :presel].sum(axis=1)
+    else:
+        denom = np.exp(s64 - m).sum(axis=1)
+    return e[:, :k] / denom[:, None]
+
+
+def margins(s64, k: int, n_group: int = 1, topk_group: int = 1) -> np.ndarray:
+    """Per token, the smallest gap at a selection boundary, in float64.
+
+    The k-th minus (k+1)-th eligible score, and with group-limited routing also
+    the topk_group-th minus (topk_group+1)-th group score.  A token whose gap is
+    below the flip threshold may legitimately be routed differently by an fp32
+    computation of the logits.
+    """
+    s64 = np.asarray(s64, dtype=np.float64)
+    T, E = s64.shape
+    elig = _eligible(s64, n_group, topk_group)
+    srt = -np.sort(-np.where(elig, s64, -np.inf), axis=1)
+    gap = np.full(T, np.inf)
+    if k < E:
+        gap = srt[:, k - 1] - srt[:, k]  # finite - (-inf) = +inf when too few are eligible
+    if n_group > 1 and topk_group < n_group:
+        gsc = -np.sort(-s64.reshape(T, n_group, E // n_group).max(axis=2), axis=1)
+        gap = np.minimum(gap, gsc[:, topk_group - 1] - gsc[:, topk_group])
+    return gap
+
+
+def route(logits32, bias, *, k, n_group=1, topk_group=1, presel=0, renorm=1):
+    """Scores -> selection -> gates.  Returns (topk_idx int32 [T,k], topk_w f64 [T,k], s f32)."""
+    s = scores(logits32, bias)
+    sel = select(s, k, n_group, topk_group, presel)
+    w = gates(s, sel, k, presel, renorm)
+    return sel[:, :k].astype(np.int32), w, s
+
+
+# ----------------------------------------------------------------------------
+# a3 + a4: histogram, offsets, stable permutation (dispatch layout)
+# ----------------------------------------------------------------------------
+def permute(topk_idx, E: int, ep_ranks: int = 1) -> dict:
+    """Expert-contiguous dispatch layout.
+
+    c_e = number of (token, choice) pairs routed to e; o = exclusive prefix sum
+    of c (the count identity sum c_e = T*k: [ThunderEP] §2, 1024 tokens with
+    top-2 are 2048 expert calls).  The rows of expert e are its tokens in
+    ascending token order: p(t, j) = o_e + #{t' < t routed to e}.  Rows are
+    packed per destination with one chunk per expert in expert-ID order
+    ([EP-V4] §3.3), and experts are placed on ranks in contiguous blocks of
+    E/R ([EP-V4] §3.1 example: experts 0-7 on machine 0, 8-15 on machine 1),
+    so rank r's send chunk starts at rank_offsets[r] = o[r * E/R].
+    """
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    T, k = idx.shape
+    flat = idx.reshape(-1)  # entry i = t*k + j
+    counts = np.bincount(flat, minlength=E)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    slot_of = np.empty(T * k, dtype=np.int64)
+    for e in range(E):
+        # ascending entry index == ascending token, since a token picks e at most once
+        entries = np.flatnonzero(flat == e)
+        slot_of[entries] = offsets[e] + np.arange(entries.size)
+    src_of = np.empty(T * k, dtype=np.int64)
+    src_of[slot_of] = np.arange(T * k)
+    per_rank = E // ep_ranks
+    rank_offsets = offsets[np.arange(ep_ranks + 1) * per_rank]
+    return {
+        "counts": counts.astype(np.int32),
+        "offsets": offsets.astype(np.int32),
+        "rank_offsets": rank_offsets.astype(np.int32),
+        "slot_of": slot_of.astype(np.int32),
+        "src_of": src_of.astype(np.int32),
+    }
+
+
+def gather_rows(x, src_of, k: int) -> np.ndarray:
+    """x_perm[p] = x[src_of[p] // k]: a plain row copy (bit patterns kept)."""
+    return np.asarray(x)[np.asarray(src_of) // k]
+
+
+# ----------------------------------------------------------------------------
+# a5 + a6: per-expert SwiGLU FFN
+# ----------------------------------------------------------------------------
+def silu(a):
+    """SiLU(a) = a * sigmoid(a) = a / (1 + exp(-a))."""
+    with np.errstate(over="ignore"):
+        return a / (1.0 + np.exp(-a))
+
+
+def expert_ffn(X, w_gate_e, w_up_e, w_down_e):
+    """One expert on its rows: h = SiLU(X Wg^T) * (X Wu^T); y = h Wd^T (float64).
+
+    The expert FFN is "L1 + Act + L2" ([V4-overlap], Waved-EP section); the
+    gated (SwiGLU) form and the [f,d] / [f,d] / [d,f] per-expert layouts are
+    this path's reading.  Returns (y, h).
+    """
+    X = _f64(X)
+    a = X @ _f64(w_gate_e).T
+    u = X @ _f64(w_up_e).T
+    h = silu(a) * u
+    return h @ _f64(w_down_e).T, h
+
+
+def grouped_ffn(x_perm, offsets, w_gate, w_up, w_down):
+    """Run every expert on its segment [o_e, o_{e+1}) of the permuted rows."""
+    x_perm = np.asarray(x_perm)
+    A = x_perm.shape[0]
+    E = len(offsets) - 1
+    f = np.asarray(w_gate).shape[1]
+    d = np.asarray(w_down).shape[1]
+    y = np.zeros((A, d))
+    h = np.zeros((A, f))
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            y[r0:r1], h[r0:r1] = expert_ffn(x_perm[r0:r1], w_gate[e], w_up[e], w_down[e])
+    return y, h
+
+
+# ----------------------------------------------------------------------------
+# a7: weighted combine
+# ----------------------------------------------------------------------------
+def combine(y_perm, slot_of, topk_w) -> np.ndarray:
+    """out[t] = sum over j ascending of g[t, j] * y[p(t, j)] (float64).
+
+    Each token's k expert outputs are summed with their gate weights back on
+    the token's home device ([SyncTax] §2.3).
+    """
+    g = np.asarray(topk_w, dtype=np.float64)
+    T, k = g.shape
+    y = _f64(y_perm)
+    slots = np.asarray(slot_of).reshape(T, k)
+    out = np.zeros((T, y.shape[1]))
+    for j in range(k):
+        out += g[:, j : j + 1] * y[slots[:, j]]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# the whole layer
+# ----------------------------------------------------------------------------
+def layer(x, w_router, bias, w_gate, w_up, w_down, *, k, n_group=1, topk_group=1,
+          presel=0, renorm=1, ep_ranks=1, logits32=None) -> dict:
+    """router -> permute -> grouped FFN -> combine, serial as the method states
+    ([V4-overlap]: dispatch, expert compute and combine are three serial steps;
+    [SyncTax] §2.1-§2.3).
+
+    `logits32` (fp32) replaces the oracle's own logits when given, so that the
+    rest of the path can be checked on another implementation's routing inputs.
+    """
+    E = np.asarray(w_router).shape[0]
+    z = router_logits(x, w_router)
+    z32 = z.astype(np.float32) if logits32 is None else np.asarray(logits32, np.float32)
+    idx, w, s = route(z32, bias, k=k, n_group=n_group, topk_group=topk_group,
+                      presel=presel, renorm=renorm)
+    s64 = z + (0.0 if bias is None else np.asarray(bias, np.float32).astype(np.float64)[None, :])
+    perm = permute(idx, E, ep_ranks)
+    x_perm = gather_rows(x, perm["src_of"], k)
+    y, h = grouped_ffn(x_perm, perm["offsets"], w_gate, w_up, w_down)
+    out = combine(y, perm["slot_of"], w)
+    return dict(logits=z, s=s, topk_idx=idx, topk_w=w, margin=margins(s64, k, n_group, topk_group),
+                x_perm=x_perm, h=h, y_perm=y, out=out, **perm)
+
+
+# ----------------------------------------------------------------------------
+# brute-force forms used to pin the above
+# ----------------------------------------------------------------------------
+def _best_subset(values, candidates, size):
+    """The size-subset of `candidates` with the largest exact sum of `values`;
+    among equal sums the lexicographically smallest sorted index tuple."""
+    best, best_key = None, None
+    for sub in itertools.combinations(sorted(candidates), size):
+        tot = sum(Fraction(float(values[i])) for i in sub)
+        key = (-tot, sub)
+        if best_key is None or key < best_key:
+            best, best_key = sub, key
+    return best
+
+
+def select_bruteforce(s, k: int, n_group: int = 1, topk_group: int = 1):
+    """Chosen expert sets by exhaustive enumeration (tiny E only).
+
+    With groups: first the topk_group-subset of groups with the largest sum of
+    group maxima, then the k-subset of their experts with the largest score
+    sum.  Returns a list of sorted index tuples.
+    """
+    s = np.asarray(s, dtype=np.float32)
+    T, E = s.shape
+    out = []
+    for t in range(T):
+        row = s[t]
+        cand = range(E)
+        if n_group > 1 and topk_group < n_group:
+            gs = E // n_group
+            gmax = [max(row[g * gs:(g + 1) * gs], key=float) for g in range(n_group)]
+            keep = _best_subset(gmax, range(n_group), topk_group)
+            cand = [g * gs + i for g in keep for i in range(gs)]
+        out.append(_best_subset(row, cand, k))
+    return out
+
+
+def dense_bruteforce(x, w_router, bias, w_gate, w_up, w_down, *, k, n_group=1,
+                     topk_group=1, presel=0, renorm=1):
+    """out[t] = sum_e G[t, e] * FFN_e(x[t]) with a dense gate matrix G.
+
+    Runs every expert on every token and forms no permutation, offsets or
+    gather; only the routing decision is shared with `layer`.
+    """
+    T = np.asarray(x).shape[0]
+    E = np.asarray(w_router).shape[0]
+    z32 = router_logits(x, w_router).astype(np.float32)
+    idx, w, _ = route(z32, bias, k=k, n_group=n_group, topk_group=topk_group,
+                      presel=presel, renorm=renorm)
+    G = np.zeros((T, E))
+    for t in range(T):
+        for j in range(k):
+            G[t, idx[t, j]] += w[t, j]
+    xf = _f64(x)
+    out = np.zeros((T, np.asarray(w_down).shape[1]))
+    for e in range(E):
+        y_e, _ = expert_ffn(xf, w_gate[e], w_up[e], w_down[e])
+        out += G[:, e : e + 1] * y_e
+    return out

@@ -1,0 +1,401 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each pin is a plain function so that the mutation tests at the bottom can plant
+a plausible mistake in the oracle and show that some pin catches it.
+Sources of truth used here: hand-worked closed forms (tests/golden/), exhaustive
+enumeration, library routines (scipy softmax, numpy stable sort, torch
+SiLU/matmul), exact identities, and the pages' size/statistics statements.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle import moe_oracle as om
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+def _tied_scores(rng, T, E, levels=5):
+    """float32 scores drawn from a few levels so that exact ties are common."""
+    return rng.integers(-levels, levels + 1, size=(T, E)).astype(np.float32) * np.float32(0.25)
+
+
+def _random_topk(rng, T, E, k):
+    return np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+
+
+# ----------------------------------------------------------------------------- pins
+def pin_scores_single_add():
+    rng = np.random.default_rng(0)
+    z = rng.standard_normal((50, 9)).astype(np.float32)
+    b = rng.standard_normal(9).astype(np.float32)
+    s = om.scores(z, b)
+    # fp32 + fp32 is exact in fp64; one rounding to fp32 is the IEEE single add
+    ref = (z.astype(np.float64) + b.astype(np.float64)[None, :]).astype(np.float32)
+    assert s.dtype == np.float32
+    assert np.array_equal(s.view(np.uint32), ref.view(np.uint32))
+    neg0 = om.scores(np.array([[-0.0, 1.0]], np.float32), None)
+    assert not np.signbit(neg0[0, 0])
+
+
+def pin_selection_bruteforce():
+    rng = np.random.default_rng(1)
+    for E, k in [(4, 1), (4, 2), (6, 3), (8, 2), (8, 3)]:
+        s = _tied_scores(rng, 64, E)
+        sel = om.select(s, k)[:, :k]
+        brute = om.select_bruteforce(s, k)
+        for t in range(s.shape[0]):
+            assert tuple(sorted(sel[t].tolist())) == brute[t], (E, k, t, s[t], sel[t])
+            # best first, ties by index ascending
+            vals = s[t, sel[t]]
+            assert np.all(vals[:-1] >= vals[1:])
+            for j in range(k - 1):
+                if vals[j] == vals[j + 1]:
+                    assert sel[t, j] < sel[t, j + 1]
+
+
+def pin_group_bruteforce():
+    rng = np.random.default_rng(2)
+    s = _tied_scores(rng, 64, 16, levels=4)
+    sel = om.select(s, 3, n_group=4, topk_group=2)[:, :3]
+    brute = om.select_bruteforce(s, 3, n_group=4, topk_group=2)
+    for t in range(64):
+        assert tuple(sorted(sel[t].tolist())) == brute[t], (t, s[t])
+
+
+def pin_group_all_kept_is_plain():
+    rng = np.random.default_rng(3)
+    s = rng.standard_normal((100, 32)).astype(np.float32)
+    assert np.array_equal(om.select(s, 4, n_group=8, topk_group=8), om.select(s, 4))
+
+
+def pin_hand_cases():
+    g = _golden("hand_routing_cases.json")
+    for case in g["cases"]:
+        if "s" in case:
+            s = np.array([case["s"]], np.float32)
+            bias = None
+        else:
+            s = np.log(np.array([case["p"]], np.float64)).astype(np.float32)
+            bias = None if case["bias_p"] is None else np.log(np.array(case["bias_p"], np.float64)).astype(np.float32)
+        idx, w, _ = om.route(s, bias, k=case["k"], n_group=case["n_group"],
+                             topk_group=case["topk_group"], presel=case["presel"],
+                             renorm=case["renorm"])
+        assert idx[0].tolist() == case["topk_idx"], case["name"]
+        if "gates" in case:
+            want = np.array([a / b for a, b in case["gates"]])
+            assert np.max(np.abs(w[0] - want)) < 1e-6, (case["name"], w[0], want)
+
+
+def pin_presel_all_is_full_softmax():
+    rng = np.random.default_rng(4)
+    z = rng.standard_normal((40, 12)).astype(np.float32)
+    idx, w, s = om.route(z, None, k=3, presel=12, renorm=0)
+    p = scipy.special.softmax(s.astype(np.float64), axis=1)
+    assert np.allclose(w, np.take_along_axis(p, idx.astype(np.int64), axis=1), rtol=0, atol=1e-14)
+
+
+def pin_renorm_is_softmax_then_renorm():
+    rng = np.random.default_rng(5)
+    for k in (1, 2, 4, 8):
+        z = (2 * rng.standard_normal((30, 16))).astype(np.float32)
+        idx, w, s = om.route(z, None, k=k, renorm=1)
+        p = scipy.special.softmax(s.astype(np.float64), axis=1)
+        pk = np.take_along_axis(p, idx.astype(np.int64), axis=1)
+        assert np.allclose(w, pk / pk.sum(1, keepdims=True), rtol=1e-13, atol=0)
+        assert np.allclose(w.sum(1), 1.0, rtol=0, atol=1e-14)
+
+
+def pin_gate_closed_forms():
+    rng = np.random.default_rng(6)
+    z = rng.standard_normal((64, 8)).astype(np.float32)
+    idx, w, s = om.route(z, None, k=2, renorm=1)
+    s0 = np.take_along_axis(s, idx[:, :1].astype(np.int64), 1)[:, 0].astype(np.float64)
+    s1 = np.take_along_axis(s, idx[:, 1:2].astype(np.int64), 1)[:, 0].astype(np.float64)
+    logistic = 1.0 / (1.0 + np.exp(s1 - s0))
+    assert np.allclose(w[:, 0], logistic, rtol=1e-14, atol=0)
+    assert np.allclose(w[:, 1], 1.0 - logistic, rtol=0, atol=1e-14)
+    idx1, w1, _ = om.route(z, None, k=1, renorm=1)
+    assert np.array_equal(w1, np.ones_like(w1))
+    assert np.array_equal(idx1[:, 0], np.argmax(z, axis=1))
+
+
+def pin_permute_invariants():
+    rng = np.random.default_rng(7)
+    T, E, k, R = 1000, 16, 4, 4
+    idx = _random_topk(rng, T, E, k)
+    p = om.permute(idx, E, R)
+    A = T * k
+    assert p["counts"].sum() == A
+    assert p["offsets"][0] == 0 and p["offsets"][-1] == A
+    assert np.array_equal(np.diff(p["offsets"]), p["counts"])
+    assert sorted(p["slot_of"].tolist()) == list(range(A))          # bijection
+    assert np.array_equal(p["src_of"][p["slot_of"]], np.arange(A))  # slot_of o src_of = id
+    assert np.array_equal(p["slot_of"][p["src_of"]], np.arange(A))
+    flat = idx.reshape(-1)
+    for e in range(E):
+        seg = p["src_of"][p["offsets"][e]:p["offsets"][e + 1]]
+        assert np.all(flat[seg] == e)
+        assert np.all(np.diff(seg // k) > 0)  # ascending token order within an expert
+    assert np.array_equal(p["rank_offsets"], p["offsets"][[0, 4, 8, 12, 16]])
+
+
+def pin_permute_is_stable_sort():
+    rng = np.random.default_rng(8)
+    for T, E, k in [(7, 3, 2), (300, 8, 2), (257, 64, 8)]:
+        idx = _random_topk(rng, T, E, k)
+        p = om.permute(idx, E)
+        # a stable sort of the flattened expert ids lists the entries in slot order
+        assert np.array_equal(p["src_of"], np.argsort(idx.reshape(-1), kind="stable"))
+
+
+def pin_call_count():
+    g = _golden("routing_call_count.json")
+    rng = np.random.default_rng(9)
+    idx = _random_topk(rng, g["T"], g["E"], g["k"])
+    p = om.permute(idx, g["E"], g["ep_ranks"])
+    assert int(p["counts"].sum()) == g["expected_expert_calls"]
+    assert idx.astype(np.int32).nbytes == g["expected_index_bytes"]
+    assert len(p["rank_offsets"]) == g["ep_ranks"] + 1
+    assert p["rank_offsets"][1] == p["offsets"][g["E"] // g["ep_ranks"]]
+
+
+def pin_swiglu_unit():
+    g = _golden("swiglu_unit_case.json")
+    y, h = om.expert_ffn(np.array(g["x"]), np.array(g["w_gate"])[0], np.array(g["w_up"])[0],
+                         np.array(g["w_down"])[0])
+    assert np.allclose(h, g["h"], rtol=1e-15, atol=0)
+    assert np.allclose(y, g["y"], rtol=1e-15, atol=0)
+
+
+def _torch_mlp(x, wg, wu, wd):
+    x, wg, wu, wd = (torch.from_numpy(np.asarray(a, np.float64)) for a in (x, wg, wu, wd))
+    return (torch.nn.functional.silu(x @ wg.T) * (x @ wu.T) @ wd.T).numpy()
+
+
+def pin_single_expert_is_dense_mlp():
+    rng = np.random.default_rng(10)
+    T, d, f = 33, 24, 40
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((1, d))
+    wg, wu, wd = (0.2 * rng.standard_normal(s) for s in ((1, f, d), (1, f, d), (1, d, f)))
+    r = om.layer(x, wr, None, wg, wu, wd, k=1)
+    assert np.allclose(r["out"], _torch_mlp(x, wg[0], wu[0], wd[0]), rtol=1e-12, atol=1e-12)
+
+
+def pin_identical_experts():
+    rng = np.random.default_rng(11)
+    T, d, f, E, k = 50, 16, 24, 6, 3
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d))
+    one = [0.3 * rng.standard_normal(s) for s in ((f, d), (f, d), (d, f))]
+    wg, wu, wd = (np.repeat(a[None], E, axis=0) for a in one)
+    r = om.layer(x, wr, None, wg, wu, wd, k=k, renorm=1)
+    assert np.allclose(r["out"], _torch_mlp(x, *one), rtol=1e-12, atol=1e-12)
+
+
+def pin_combine_identity_experts():
+    rng = np.random.default_rng(12)
+    T, d, E = 80, 8, 8
+    x = rng.standard_normal((T, d))
+    for k in (1, 2, 3):
+        z = rng.standard_normal((T, E)).astype(np.float32)
+        idx, w, _ = om.route(z, None, k=k, renorm=1)
+        p = om.permute(idx, E)
+        out = om.combine(om.gather_rows(x, p["src_of"], k), p["slot_of"], w)
+        if k == 1:
+            assert np.array_equal(out, x)
+        else:
+            assert np.allclose(out, x, rtol=1e-14, atol=1e-14)
+
+
+ROUTING_MODES = [
+    dict(E=8, k=2),
+    dict(E=8, k=2, bias="normal"),
+    dict(E=12, k=2, presel=8, renorm=0),
+    dict(E=16, k=3, n_group=4, topk_group=2),
+    dict(E=6, k=2, renorm=0),
+]
+
+
+def _small_problem(rng, E, T=24, d=12, f=20, bias=None):
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((E, d))
+    b = rng.standard_normal(E).astype(np.float32) if bias == "normal" else None
+    wg, wu, wd = (0.3 * rng.standard_normal(s) for s in ((E, f, d), (E, f, d), (E, d, f)))
+    return x, wr, b, wg, wu, wd
+
+
+def _mode_kw(m):
+    return {k: v for k, v in m.items() if k in ("k", "n_group", "topk_group", "presel", "renorm")}
+
+
+def pin_layer_matches_dense_bruteforce():
+    rng = np.random.default_rng(13)
+    for m in ROUTING_MODES:
+        prob = _small_problem(rng, m["E"], bias=m.get("bias"))
+        r = om.layer(*prob, **_mode_kw(m))
+        dense = om.dense_bruteforce(*prob, **_mode_kw(m))
+        assert np.allclose(r["out"], dense, rtol=1e-12, atol=1e-12), m
+
+
+def pin_token_permutation():
+    rng = np.random.default_rng(14)
+    for m in ROUTING_MODES:
+        x, wr, b, wg, wu, wd = _small_problem(rng, m["E"], bias=m.get("bias"))
+        perm = rng.permutation(x.shape[0])
+        r1 = om.layer(x, wr, b, wg, wu, wd, **_mode_kw(m))
+        r2 = om.layer(x[perm], wr, b, wg, wu, wd, **_mode_kw(m))
+        assert np.allclose(r2["out"], r1["out"][perm], rtol=1e-12, atol=1e-12), m
+
+
+def pin_expert_relabel():
+    rng = np.random.default_rng(15)
+    for m in ROUTING_MODES:
+        E = m["E"]
+        x, wr, b, wg, wu, wd = _small_problem(rng, E, bias=m.get("bias"))
+        ng = m.get("n_group", 1)
+        gs = E // ng
+        # permute whole groups, and experts inside each group
+        gperm = rng.permutation(ng)
+        relabel = np.concatenate([g * gs + rng.permutation(gs) for g in gperm])
+        bb = None if b is None else b[relabel]
+        r1 = om.layer(x, wr, b, wg, wu, wd, **_mode_kw(m))
+        r2 = om.layer(x, wr[relabel], bb, wg[relabel], wu[relabel], wd[relabel], **_mode_kw(m))
+        assert np.allclose(r2["out"], r1["out"], rtol=1e-12, atol=1e-12), m
+        assert np.array_equal(np.sort(relabel[r2["topk_idx"]], 1), np.sort(r1["topk_idx"], 1))
+
+
+def pin_margins():
+    s = np.array([[3.0, 1.0, 2.0, 1.5]])
+    assert om.margins(s, 2)[0] == pytest.approx(0.5)
+    g = np.array([[5.0, 0.0, 4.9, 4.8, 0.0, 0.0, 4.85, 4.0]])
+    # experts in kept groups: 5, 0, 4.9, 4.8 -> 3rd/4th gap 4.8 - 0 = 4.8; group gap 4.9 - 4.85
+    assert om.margins(g, 3, n_group=4, topk_group=2)[0] == pytest.approx(0.05)
+
+
+def pin_routing_statistics():
+    g = _golden("routing_statistics.json")
+    rng = np.random.default_rng(16)
+    z = rng.standard_normal((40000, 64)).astype(np.float32)
+    idx, _, _ = om.route(z, None, k=2)
+    share = np.bincount(idx.ravel(), minlength=64) / idx.size
+    assert abs(share.mean() - g["uniform_share_E64"]) < 1e-12
+    assert np.max(np.abs(share - g["uniform_share_E64"])) < 0.0025
+    z = rng.standard_normal((40000, 16)).astype(np.float32)
+    idx, _, _ = om.route(z, None, k=2)
+    p = np.bincount(idx.ravel(), minlength=16) / idx.size
+    ent = -(p * np.log2(p)).sum()
+    assert g["max_entropy_bits_E16"] - 0.01 < ent <= g["max_entropy_bits_E16"] + 1e-12
+
+
+def pin_widen_bf16():
+    bits = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x4049, 0x7F7F], np.uint16)
+    got = om.widen_bf16(bits)
+    want = [1.0, -1.0, 0.0, -0.0, 3.140625, float.fromhex("0x1.fep127")]
+    assert got.tolist() == want
+
+
+PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_")}
+
+
+@pytest.mark.parametrize("name", sorted(PINS))
+def test_pin(name):
+    PINS[name]()
+
+
+# ------------------------------------------------------------------ planted mistakes
+def _ties_to_highest(v):
+    n = v.shape[-1]
+    return (n - 1) - np.argsort(-v[..., ::-1], axis=-1, kind="stable")
+
+
+def _scores_without_bias(z32, bias=None):
+    return np.asarray(z32, dtype=np.float32) + np.float32(0.0)
+
+
+def _gates_presel_uses_k(s, sel, k, presel=0, renorm=1):
+    return _ORIG["gates"](s, sel, k, 0, 1)
+
+
+def _silu_wrong_branch(X, wg, wu, wd):
+    X = om._f64(X)
+    h = (X @ om._f64(wg).T) * om.silu(X @ om._f64(wu).T)
+    return h @ om._f64(wd).T, h
+
+
+def _permute_reversed_within_expert(topk_idx, E, ep_ranks=1):
+    p = _ORIG["permute"](topk_idx, E, ep_ranks)
+    src = p["src_of"].copy()
+    for e in range(E):
+        a, b = p["offsets"][e], p["offsets"][e + 1]
+        src[a:b] = src[a:b][::-1]
+    slot = np.empty_like(src)
+    slot[src] = np.arange(src.size)
+    p.update(src_of=src, slot_of=slot)
+    return p
+
+
+def _combine_swapped_gates(y_perm, slot_of, topk_w):
+    return _ORIG["combine"](y_perm, slot_of, np.asarray(topk_w)[:, ::-1])
+
+
+def _eligible_mean_group(s, n_group, topk_group):
+    T, E = s.shape
+    if n_group <= 1 or topk_group >= n_group:
+        return np.ones((T, E), dtype=bool)
+    gs = E // n_group
+    kept = om._order_desc(s.reshape(T, n_group, gs).mean(axis=2))[:, :topk_group]
+    gmask = np.zeros((T, n_group), dtype=bool)
+    np.put_along_axis(gmask, kept, True, axis=1)
+    return np.repeat(gmask, gs, axis=1)
+
+
+def _rank_offsets_by_rank_index(topk_idx, E, ep_ranks=1):
+    p = _ORIG["permute"](topk_idx, E, ep_ranks)
+    p["rank_offsets"] = p["offsets"][: ep_ranks + 1].copy()
+    return p
+
+
+def _gates_no_max_exp_sign(s, sel, k, presel=0, renorm=1):
+    w = _ORIG["gates"](s, sel, k, presel, renorm)
+    return w[:, ::-1].copy()
+
+
+_ORIG = {n: getattr(om, n) for n in ("gates", "permute", "combine")}
+
+MUTANTS = {
+    "ties-to-highest-index": ("_order_desc", _ties_to_highest),
+    "bias-dropped": ("scores", _scores_without_bias),
+    "presel-denominator-over-k": ("gates", _gates_presel_uses_k),
+    "silu-on-up-branch": ("expert_ffn", _silu_wrong_branch),
+    "permute-not-stable": ("permute", _permute_reversed_within_expert),
+    "combine-gates-swapped": ("combine", _combine_swapped_gates),
+    "group-score-mean": ("_eligible", _eligible_mean_group),
+    "rank-offsets-wrong": ("permute", _rank_offsets_by_rank_index),
+    "gates-reversed": ("gates", _gates_no_max_exp_sign),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_planted_mistake_is_caught(mutant, monkeypatch):
+    attr, fn = MUTANTS[mutant]
+    monkeypatch.setattr(om, attr, fn)
+    caught = []
+    for name, pin in PINS.items():
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(name)
+    assert caught, f"no pin catches the planted mistake {mutant!r}"
