@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""MoE-layer forward throughput on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic tokens:
+moe_route -> moe_permute -> moe_ffn_gate_up -> moe_ffn_down -> moe_combine,
+each a C-ABI call that enqueues the HIP kernels on the current stream.
+Inputs are resident in HBM before timing starts.  W warm-up steps, then K
+timed steps bracketed by device synchronisation; HIP events recorded on the
+same stream between the calls give each kernel's average duration inside the
+timed region.  Prints ONE JSON line (rank 0).
+
+Default workload: T=1024 tokens, d=4096, E=8 experts, top-2, SwiGLU f=11008,
+bf16 (the headline workload of the method's metric).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PHASES = ("route", "permute", "ffn_gate_up", "ffn_down", "combine")
+DOMINANT = "ffn_gate_up"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_gate_up_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "top_routing_expert_amd", "csrc", "ffn.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    from top_routing_expert_amd import configs as C
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="2",
+                    help="workload index 1..5 or name; default 2 (T1024-d4096-E8-top2-f11008)")
+    ap.add_argument("--cpu-tokens", type=int, default=256,
+                    help="tokens of the workload the CPU oracle baseline runs (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for counter calibration)")
+    a = ap.parse_args()
+    if a.config.isdigit():
+        a.shape = C.CONFIGS[int(a.config) - 1]
+    else:
+        a.shape = C.BY_NAME[a.config]
+    return a
+
+
+def algorithmic(shape, counts):
+    """Algorithmic HBM bytes and flops of one launch of every phase."""
+    s = 2 if shape.dtype == "bf16" else 4
+    T, d, E, k, f = shape.T, shape.d, shape.E, shape.k, shape.f
+    A = T * k
+    e_nz = int((counts > 0).sum())
+    return {
+        "route": dict(bytes=T * d * s + E * d * s + T * E * 4 + 8 * A, flops=2 * T * d * E),
+        "permute": dict(bytes=T * d * s + A * d * s + 4 * A + 8 * A + 8 * (E + 1), flops=0),
+        "ffn_gate_up": dict(bytes=2 * e_nz * f * d * s + A * d * s + A * f * s,
+                            flops=2 * A * d * 2 * f),
+        "ffn_down": dict(bytes=e_nz * d * f * s + A * f * s + A * d * s, flops=2 * A * f * d),
+        "combine": dict(bytes=A * d * s + T * d * s + 8 * A, flops=2 * A * d),
+    }
+
+
+def roofline_of(work, ms):
+    sec = ms * 1e-3
+    ai = work["flops"] / work["bytes"] if work["bytes"] else float("inf")
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    gbs = work["bytes"] / sec / 1e9
+    tfl = work["flops"] / sec / 1e12
+    if ai < ridge:
+        return dict(bound="hbm", achieved=gbs, peak=PEAK_HBM_GBS, unit="GB/s", frac=gbs / PEAK_HBM_GBS,
+                    tflops=tfl, mfma_frac=tfl / PEAK_BF16_TFLOPS, ai=ai)
+    return dict(bound="mfma", achieved=tfl, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                frac=tfl / PEAK_BF16_TFLOPS, gbs=gbs, hbm_frac=gbs / PEAK_HBM_GBS, ai=ai)
+
+
+def measured_traffic(launch_bytes):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if there is none or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+        with open(KERNEL_SRC, "rb") as fh:
+            h = hashlib.sha256(fh.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_src_sha256") != h or t.get("workload") is None:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(shape, inp, n_tok):
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    n_tok = min(n_tok, shape.T)
+    t0 = time.perf_counter()
+    oracle.layer(inp["x"][:n_tok], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
+                 inp["w_down"], k=shape.k, n_group=shape.n_group, topk_group=shape.topk_group,
+                 presel=shape.presel, renorm=shape.renorm, ep_ranks=shape.ep_ranks)
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": n_tok / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n_tok} of {shape.T} tokens, whole layer (route, permute, FFN, "
+                      f"combine) in float64 NumPy; {dt:.1f} s"}
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {a.gpus} requested): this path has no "
+              "multi-GPU mode; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from top_routing_expert_amd import binding as B
+    from top_routing_expert_amd import inputs as I
+
+    if a.copy_calibration:
+        copy_calibration()
+        return
+    shape = a.shape
+    log(f"workload {shape.name}: generating inputs")
+    from top_routing_expert_amd import configs as C
+    inp = I.make_inputs(shape, seed=C.CONFIGS.index(shape) + 1)
+    dev = {k: (None if v is None else B.to_device(v)) for k, v in inp.items()}
+    cfg = B.config(shape)
+    T, E, k, d, f, R = shape.T, shape.E, shape.k, shape.d, shape.f, shape.ep_ranks
+    A = T * k
+    dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    buf = dict(
+        logits=torch.empty((T, E), dtype=torch.float32, device="cuda"),
+        idx=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+        w=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+        offs=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+        roffs=torch.empty(R + 1, dtype=torch.int32, device="cuda"),
+        slot=torch.empty(A, dtype=torch.int32, device="cuda"),
+        src=torch.empty(A, dtype=torch.int32, device="cuda"),
+        xp=torch.empty((A, d), dtype=dt, device="cuda"),
+        h=torch.empty((A, f), dtype=dt, device="cuda"),
+        y=torch.empty((A, d), dtype=dt, device="cuda"),
+        out=torch.empty((T, d), dtype=dt, device="cuda"),
+    )
+    ws_r, ws_p = B.workspace(cfg, "route"), B.workspace(cfg, "permute")
+    stream = torch.cuda.current_stream()
+
+    calls = {
+        "route": lambda: B.moe_route(cfg, dev["x"], dev["w_router"], dev["bias"], buf["logits"],
+                                     buf["idx"], buf["w"], ws_r, stream),
+        "permute": lambda: B.moe_permute(cfg, dev["x"], buf["idx"], buf["offs"], buf["roffs"],
+                                         buf["slot"], buf["src"], buf["xp"], ws_p, stream),
+        "ffn_gate_up": lambda: B.moe_ffn_gate_up(cfg, buf["xp"], buf["offs"], dev["w_gate"],
+                                                 dev["w_up"], buf["h"], stream),
+        "ffn_down": lambda: B.moe_ffn_down(cfg, buf["h"], buf["offs"], dev["w_down"], buf["y"],
+                                           stream),
+        "combine": lambda: B.moe_combine(cfg, buf["y"], buf["slot"], buf["w"], buf["out"], stream),
+    }
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        for i, p in enumerate(PHASES):
+            calls[p]()
+            if ev is not None:
+                ev[i + 1].record(stream)
+
+    log(f"warmup {a.warmup}")
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    counts = np.diff(B.to_host_bits(buf["offs"]).astype(np.int64))
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(PHASES) + 1)]
+              for _ in range(a.steps)]
+    log(f"timing {a.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    phase_ms = {p: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
+                                  for s in range(a.steps)])) for i, p in enumerate(PHASES)}
+    ms_per_step = elapsed * 1e3 / a.steps
+    work = algorithmic(shape, counts)
+    phases = {p: dict(ms=phase_ms[p], **roofline_of(work[p], phase_ms[p])) for p in PHASES}
+    dom = phases[DOMINANT]
+    traffic = measured_traffic(work[DOMINANT]["bytes"])
+    roofline = {"bound": dom["bound"], "achieved": round(dom["achieved"], 3),
+                "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4),
+                "traffic": traffic, "kernel": "grouped_gemm_bf16_kernel<gated> (moe_ffn_gate_up)",
+                "algorithmic_bytes": work[DOMINANT]["bytes"],
+                "algorithmic_flops": work[DOMINANT]["flops"],
+                "avg_launch_ms": round(dom["ms"], 5)}
+    cpu = None
+    if a.cpu_tokens > 0:
+        log(f"cpu baseline: oracle on {a.cpu_tokens} tokens")
+        cpu = cpu_baseline(shape, inp, a.cpu_tokens)
+    res = {
+        "metric": "MoE-layer fwd tokens/s @1 GPU; % bf16 MFMA peak (FFN), % HBM BW (route/permute)",
+        "value": T * a.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic (seeded Gaussian inputs and random-init expert weights)",
+        "config": {"workload": shape.name, "T": T, "d": d, "E": E, "k": k, "f": f,
+                   "n_group": shape.n_group, "topk_group": shape.topk_group,
+                   "presel": shape.presel, "renorm": shape.renorm, "ep_ranks": R,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "phases": {p: {kk: (round(v, 5) if isinstance(v, float) else v) for kk, v in ph.items()}
+                   for p, ph in phases.items()},
+        "expert_rows": {"min": int(counts.min()), "max": int(counts.max()),
+                        "empty": int((counts == 0).sum())},
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

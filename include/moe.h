@@ -1,0 +1,248 @@
+/*
+ * moe.h -- C ABI of libmoe_mi355x.so: the forward token path of one
+ * Mixture-of-Experts layer on one MI355X (gfx950) GPU.
+ *
+ *   router (gate GEMM, scores, top-k, gates)  -> moe_route
+ *   histogram + stable permute (dispatch)     -> moe_permute
+ *   expert SwiGLU FFN, grouped over experts   -> moe_ffn_gate_up, moe_ffn_down
+ *                                                (both: moe_grouped_ffn)
+ *   weighted combine back to token order      -> moe_combine
+ *   all of the above in one call              -> moe_layer_fwd
+ *
+ * Pages cited by title and section:
+ *   [EP-V4]      "DeepSeek-V4的Expert Parallelism与计算通信遮掩实战解析" (tqpw.cn)
+ *   [ThunderEP]  ThunderEP article on MoE expert parallelism over PCIe
+ *                (discosf.com), section 2 "MoE专家并行的通信本质"
+ *   [V4-overlap] "DeepSeek-v4 Parallel comp-comm overlap" (recsys-frontier
+ *                blog), sections "先让 EP 在 IB 网络上跑起来" and
+ *                "V4 的 Waved-EP 通信计算遮掩"
+ *   [SyncTax]    "Deepseek-MoE同步税本质与四层实战优化指南" (qwbw.cn)
+ *
+ * The problem is stated as in the pages: T tokens of hidden size d, E experts,
+ * top-k experts per token, expert intermediate size f ([SyncTax] §2.1;
+ * [ThunderEP] §2; [EP-V4] §4.2 config fields num_experts / top_k /
+ * expert_parallel_size).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.  Every tensor pointer is a DEVICE pointer to a dense row-major array
+ *   owned by the caller; the library allocates nothing, frees nothing and
+ *   keeps no pointer after a call returns.  `ws` is caller-provided device
+ *   scratch of at least the size moe_workspace_bytes() reports for that entry
+ *   point (it may be NULL when that size is 0).  Calls that share a `ws`
+ *   buffer must not overlap in time.
+ * Element types.  cfg->dtype == MOE_BF16: x, w_*, x_perm, h, y_perm and out are
+ *   bfloat16 (raw 16-bit patterns); MOE_F32: all of them are float32.  Router
+ *   logits, bias and gate weights are always float32; indices and offsets are
+ *   int32.  Accumulation is always float32.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ *   stream).  Every call only enqueues work and returns: no host
+ *   synchronisation and no device-to-host copy.  Per-expert counts stay on the
+ *   device; the grouped FFN reads expert_offsets on the device.
+ * Errors.  All arguments are checked on the host before anything is launched;
+ *   a failed check returns a negative status and leaves every output
+ *   untouched.  A failed launch returns MOE_EHIP.  Errors raised inside a
+ *   kernel surface at the caller's next synchronisation.
+ * Values.  Non-finite inputs are unsupported (indices still stay in range).
+ *   topk_idx handed to moe_permute must hold distinct in-range experts per
+ *   token; otherwise the outputs are unspecified, but every access stays
+ *   inside the buffers described here.
+ * Determinism.  Every output is bitwise reproducible run to run (no
+ *   floating-point atomics; fixed reduction orders).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,       /* bad shape, flag, pointer or workspace size         */
+  MOE_EUNSUPPORTED = -2, /* valid problem outside what the kernels implement   */
+  MOE_EHIP = -3          /* a HIP launch failed                                */
+};
+
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+
+/* Which entry point a workspace size is asked for. */
+enum moe_entry {
+  MOE_ENTRY_ROUTE = 1,
+  MOE_ENTRY_PERMUTE = 2,
+  MOE_ENTRY_FFN = 3,
+  MOE_ENTRY_COMBINE = 4,
+  MOE_ENTRY_LAYER = 5
+};
+
+/*
+ * Problem description.
+ *   T, d, E, k, f  tokens, hidden size, experts, experts per token, expert
+ *                  intermediate size.  T may be 0 (an empty batch).
+ *   n_group, topk_group
+ *                  group-limited routing: experts form n_group contiguous
+ *                  groups of E/n_group; a group's score is the max of its
+ *                  experts' scores; only the topk_group best groups are
+ *                  eligible ([V4-overlap], EP-on-IB section: 8 experts chosen
+ *                  within the best 4 nodes).  n_group = topk_group = 1: off.
+ *   presel         0: off.  P > 0: the softmax is taken over the P best
+ *                  scores only, then the top-k of those are kept ([EP-V4]
+ *                  §3.2: partial sort to the top-8, exact softmax over those).
+ *   renorm         1: the k gates are renormalised to sum to 1 (softmax over
+ *                  the chosen set).  0: raw softmax probabilities over the
+ *                  pre-selected set (presel > 0) or over all E (presel = 0).
+ *   ep_ranks       R >= 1 expert-parallel ranks of the emitted send layout;
+ *                  rank r owns experts [r*E/R, (r+1)*E/R) ([EP-V4] §3.1:
+ *                  experts 0-7 on machine 0, 8-15 on machine 1, ...).
+ *   dtype          MOE_F32 or MOE_BF16.
+ * Limits: 1 <= k <= 16, k <= E <= 1024, presel = 0 or k <= presel <= min(E, 32),
+ *   n_group <= 64 divides E, topk_group*(E/n_group) >= max(k, presel),
+ *   R divides E.  MOE_BF16 needs d and f multiples of 64; MOE_F32 needs d
+ *   and f multiples of 4.  (T*k)*max(d, f) < 2^31.
+ */
+typedef struct moe_config {
+  int32_t T, d, E, k, f;
+  int32_t n_group, topk_group;
+  int32_t presel;
+  int32_t renorm;
+  int32_t ep_ranks;
+  int32_t dtype;
+} moe_config;
+
+/*
+ * Optional caller buffers for moe_layer_fwd's intermediates (device
+ * pointers).  A NULL field is carved from `ws` instead; a non-NULL field
+ * receives that intermediate exactly as the corresponding stage entry point
+ * would write it (routing indices kept for reuse: [SyncTax] §2.4).
+ */
+typedef struct moe_layer_bufs {
+  float* logits;           /* [T, E]            */
+  int32_t* topk_idx;       /* [T, k]            */
+  float* topk_w;           /* [T, k]            */
+  int32_t* expert_offsets; /* [E + 1]           */
+  int32_t* rank_offsets;   /* [ep_ranks + 1]    */
+  int32_t* slot_of;        /* [T * k]           */
+  int32_t* src_of;         /* [T * k]           */
+  void* x_perm;            /* [T * k, d]        */
+  void* h;                 /* [T * k, f]        */
+  void* y_perm;            /* [T * k, d]        */
+} moe_layer_bufs;
+
+/* Human-readable text of a moe_status value (static storage). */
+const char* moe_strerror(int status);
+
+/* Checks a configuration as moe_layer_fwd would; returns a moe_status. */
+int moe_validate(const moe_config* cfg);
+
+/*
+ * Bytes of `ws` that entry point `entry` (enum moe_entry) needs for `cfg`,
+ * written to *bytes.  For MOE_ENTRY_LAYER it assumes every moe_layer_bufs
+ * field is NULL (the worst case).  Returns a moe_status.
+ */
+int moe_workspace_bytes(const moe_config* cfg, int entry, size_t* bytes);
+
+/*
+ * Router: gate GEMM, scores, expert selection and gate weights.
+ *   z[t,e] = sum_i x[t,i] * w_router[e,i] in float32 ([EP-V4] §2.1: every
+ *   token's logits over all experts, then top-k and softmax gates locally);
+ *   s = z + bias[e] as one float32 add (-0 counts as +0); experts are ordered
+ *   by (s descending, index ascending) within the eligible groups; the first
+ *   k are written best first.  Gates: m = best score, e_j = exp(s_j - m)
+ *   ([EP-V4] §3.2 max subtraction), divided by the sum over the k chosen
+ *   (renorm = 1), the presel best (presel > 0) or all E experts.
+ *   x         [T, d] (dtype), or NULL: then `logits` is an INPUT [T, E] float32
+ *             and only selection and gates run.
+ *   w_router  [E, d] (dtype); ignored when x is NULL.
+ *   bias      [E] float32 or NULL (no bias).
+ *   logits    [T, E] float32: output when x != NULL, input otherwise.
+ *   topk_idx  [T, k] int32 out;  topk_w [T, k] float32 out.
+ */
+int moe_route(const moe_config* cfg, const void* x, const void* w_router, const float* bias,
+              float* logits, int32_t* topk_idx, float* topk_w,
+              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dispatch layout: per-expert histogram, exclusive scan and a stable
+ * permutation of the T*k (token, choice) pairs into expert-contiguous rows.
+ *   c_e = #pairs routed to e (sum = T*k: [ThunderEP] §2, 1024 tokens x top-2
+ *   are 2048 expert calls); expert_offsets = exclusive prefix sum of c (E+1
+ *   entries, last = T*k); the rows of expert e hold its tokens in ascending
+ *   token order: p(t,j) = expert_offsets[e] + #{t' < t routed to e}.
+ *   Rows are packed per destination, one chunk per expert in expert-ID order
+ *   ([EP-V4] §3.3), so the buffer is also the rank-major send layout:
+ *   rank r's chunk is rows [rank_offsets[r], rank_offsets[r+1]) with
+ *   rank_offsets[r] = expert_offsets[r*E/R].
+ *   x              [T, d] (dtype) in.   topk_idx [T, k] int32 in.
+ *   expert_offsets [E+1] int32 out.     rank_offsets [R+1] int32 out.
+ *   slot_of        [T*k] int32 out: slot_of[t*k+j] = p(t,j).
+ *   src_of         [T*k] int32 out: src_of[p] = t*k+j (inverse of slot_of).
+ *   x_perm         [T*k, d] (dtype) out: x_perm[p] = x[t], bit-exact copies.
+ */
+int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                int32_t* expert_offsets, int32_t* rank_offsets, int32_t* slot_of,
+                int32_t* src_of, void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Expert FFN, first half, grouped over experts: for every expert e and every
+ * row p in [expert_offsets[e], expert_offsets[e+1]):
+ *   h[p] = SiLU(x_perm[p] . w_gate[e]^T) * (x_perm[p] . w_up[e]^T),
+ *   SiLU(a) = a / (1 + exp(-a)); float32 accumulation, h stored in dtype
+ *   (bf16 rounds to nearest even).  The expert FFN is "L1 + Act + L2"
+ *   ([V4-overlap], Waved-EP section); expert weights are contiguous and in
+ *   expert-ID order ([EP-V4] §5.2).
+ *   x_perm         [rows, d] (dtype).
+ *   expert_offsets [E+1] int32 ABSOLUTE row offsets, non-decreasing, last
+ *                  <= T*k.  A sub-table (expert_offsets + e0 with cfg->E set
+ *                  to the number of experts of one rank and the weight
+ *                  pointers advanced by e0 experts) runs exactly one rank's
+ *                  share; rows outside the table are not touched.
+ *   w_gate, w_up   [E, f, d] (dtype).   h [T*k, f] (dtype) out.
+ * Only T, d, E, k, f and dtype of cfg are used.
+ */
+int moe_ffn_gate_up(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                    const void* w_gate, const void* w_up, void* h, void* stream);
+
+/*
+ * Expert FFN, second half: y_perm[p] = h[p] . w_down[e]^T for the rows of
+ * every expert e (same row-table rules as moe_ffn_gate_up).
+ *   h [T*k, f] (dtype).  w_down [E, d, f] (dtype).  y_perm [T*k, d] (dtype) out.
+ */
+int moe_ffn_down(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
+                 const void* w_down, void* y_perm, void* stream);
+
+/* moe_ffn_gate_up followed by moe_ffn_down on the same stream. */
+int moe_grouped_ffn(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                    const void* w_gate, const void* w_up, const void* w_down,
+                    void* h, void* y_perm, void* stream);
+
+/*
+ * Weighted combine back to token order ([SyncTax] §2.3: each token's k expert
+ * outputs summed with their gate weights on the token's home device):
+ *   out[t] = sum over j = 0..k-1, in that order, of topk_w[t,j] * y_perm[slot_of[t*k+j]],
+ *   float32 accumulation, stored in dtype.
+ *   y_perm [T*k, d] (dtype).  slot_of [T*k] int32, each in [0, T*k).
+ *   topk_w [T, k] float32.    out [T, d] (dtype) out.
+ */
+int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_of,
+                const float* topk_w, void* out, void* stream);
+
+/*
+ * The whole layer: moe_route -> moe_permute -> moe_ffn_gate_up ->
+ * moe_ffn_down -> moe_combine on one stream; dispatch, expert compute and
+ * combine run serially as the method states ([V4-overlap], EP-on-IB
+ * section).  `bufs` may be NULL (every intermediate lives in ws).
+ *   x [T, d], w_router [E, d], bias [E] float32 or NULL,
+ *   w_gate / w_up [E, f, d], w_down [E, d, f], out [T, d].
+ */
+int moe_layer_fwd(const moe_config* cfg, const void* x, const void* w_router, const float* bias,
+                  const void* w_gate, const void* w_up, const void* w_down, void* out,
+                  const moe_layer_bufs* bufs, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

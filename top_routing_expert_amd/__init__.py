@@ -2,16 +2,9 @@
 
 router -> permute (expert-contiguous, rank-major send layout) -> grouped SwiGLU
 FFN -> weighted combine, as hand-written HIP kernels behind a C ABI
-(`libmoe_mi355x.so`, declared in include/moe.h).  `binding` marshals torch
-tensors to that ABI; torch provides device memory and streams only.
+(`libmoe_mi355x.so`, declared in include/moe.h).  `top_routing_expert_amd.binding`
+marshals torch tensors to that ABI; torch provides device memory and streams only.
 """
 from . import configs, inputs  # noqa: F401
 
-__all__ = ["configs", "inputs", "binding"]
-
-
-def __getattr__(name):
-    if name == "binding":
-        from . import binding
-        return binding
-    raise AttributeError(name)
+__all__ = ["configs", "inputs"]

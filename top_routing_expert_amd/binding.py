@@ -1,0 +1,210 @@
+"""Thin Python binding of libmoe_mi355x.so (include/moe.h).
+
+Argument marshalling only: torch tensors are turned into device pointers and
+the current HIP stream, and the C functions of the same names are called.
+Every step of the MoE path runs in the library's HIP kernels; there is no
+Python or CPU fallback, and a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .configs import MoEShape
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3
+MOE_F32, MOE_BF16 = 0, 1
+ENTRY = {"route": 1, "permute": 2, "ffn": 3, "combine": 4, "layer": 5}
+
+CONFIG_FIELDS = ("T", "d", "E", "k", "f", "n_group", "topk_group", "presel", "renorm",
+                 "ep_ranks", "dtype")
+LAYER_BUF_FIELDS = ("logits", "topk_idx", "topk_w", "expert_offsets", "rank_offsets", "slot_of",
+                    "src_of", "x_perm", "h", "y_perm")
+
+# every function include/moe.h declares
+EXPORTS = ("moe_strerror", "moe_validate", "moe_workspace_bytes", "moe_route", "moe_permute",
+           "moe_ffn_gate_up", "moe_ffn_down", "moe_grouped_ffn", "moe_combine", "moe_layer_fwd")
+
+
+class MoEConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in CONFIG_FIELDS]
+
+
+class MoELayerBufs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_BUF_FIELDS]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({strerror(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads the in-tree library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        cfgp = ctypes.POINTER(MoEConfig)
+        L.moe_strerror.restype = ctypes.c_char_p
+        L.moe_strerror.argtypes = [i32]
+        L.moe_validate.argtypes = [cfgp]
+        L.moe_workspace_bytes.argtypes = [cfgp, i32, ctypes.POINTER(sz)]
+        L.moe_route.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_permute.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_ffn_gate_up.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
+        L.moe_ffn_down.argtypes = [cfgp, vp, vp, vp, vp, vp]
+        L.moe_grouped_ffn.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp]
+        L.moe_layer_fwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp,
+                                    ctypes.POINTER(MoELayerBufs), vp, sz, vp]
+        for name in EXPORTS[1:]:
+            if name != "moe_workspace_bytes":
+                getattr(L, name).restype = i32
+        L.moe_workspace_bytes.restype = i32
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().moe_strerror(int(status)).decode()
+
+
+def config(shape: MoEShape | None = None, **over) -> MoEConfig:
+    """MoEConfig from a workload shape (or keyword fields)."""
+    vals = {n: 0 for n in CONFIG_FIELDS}
+    vals.update(n_group=1, topk_group=1, renorm=1, ep_ranks=1, dtype=MOE_BF16)
+    if shape is not None:
+        for n in CONFIG_FIELDS[:-1]:
+            vals[n] = getattr(shape, n)
+        vals["dtype"] = MOE_BF16 if shape.dtype == "bf16" else MOE_F32
+    vals.update(over)
+    return MoEConfig(**vals)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensor arguments must live in device memory")
+    if not t.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous (dense row-major)")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoEError(fn, status)
+
+
+def validate(cfg: MoEConfig) -> int:
+    return lib().moe_validate(ctypes.byref(cfg))
+
+
+def workspace_bytes(cfg: MoEConfig, entry: str) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_workspace_bytes", lib().moe_workspace_bytes(ctypes.byref(cfg), ENTRY[entry],
+                                                            ctypes.byref(n)))
+    return n.value
+
+
+def workspace(cfg: MoEConfig, entry: str, device="cuda") -> torch.Tensor | None:
+    """A caller-owned device workspace of the size the library asks for."""
+    n = workspace_bytes(cfg, entry)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def moe_route(cfg, x, w_router, bias, logits, topk_idx, topk_w, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check("moe_route", lib().moe_route(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(bias),
+                                        _ptr(logits), _ptr(topk_idx), _ptr(topk_w), wp, wn,
+                                        _stream(stream)))
+
+
+def moe_permute(cfg, x, topk_idx, expert_offsets, rank_offsets, slot_of, src_of, x_perm,
+                ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check("moe_permute", lib().moe_permute(ctypes.byref(cfg), _ptr(x), _ptr(topk_idx),
+                                            _ptr(expert_offsets), _ptr(rank_offsets),
+                                            _ptr(slot_of), _ptr(src_of), _ptr(x_perm), wp, wn,
+                                            _stream(stream)))
+
+
+def moe_ffn_gate_up(cfg, x_perm, expert_offsets, w_gate, w_up, h, stream=None):
+    _check("moe_ffn_gate_up", lib().moe_ffn_gate_up(ctypes.byref(cfg), _ptr(x_perm),
+                                                    _ptr(expert_offsets), _ptr(w_gate), _ptr(w_up),
+                                                    _ptr(h), _stream(stream)))
+
+
+def moe_ffn_down(cfg, h, expert_offsets, w_down, y_perm, stream=None):
+    _check("moe_ffn_down", lib().moe_ffn_down(ctypes.byref(cfg), _ptr(h), _ptr(expert_offsets),
+                                              _ptr(w_down), _ptr(y_perm), _stream(stream)))
+
+
+def moe_grouped_ffn(cfg, x_perm, expert_offsets, w_gate, w_up, w_down, h, y_perm, stream=None):
+    _check("moe_grouped_ffn", lib().moe_grouped_ffn(ctypes.byref(cfg), _ptr(x_perm),
+                                                    _ptr(expert_offsets), _ptr(w_gate), _ptr(w_up),
+                                                    _ptr(w_down), _ptr(h), _ptr(y_perm),
+                                                    _stream(stream)))
+
+
+def moe_combine(cfg, y_perm, slot_of, topk_w, out, stream=None):
+    _check("moe_combine", lib().moe_combine(ctypes.byref(cfg), _ptr(y_perm), _ptr(slot_of),
+                                            _ptr(topk_w), _ptr(out), _stream(stream)))
+
+
+def moe_layer_fwd(cfg, x, w_router, bias, w_gate, w_up, w_down, out, bufs: dict | None = None,
+                  ws=None, stream=None):
+    b = None
+    if bufs:
+        b = MoELayerBufs(**{n: _ptr(bufs.get(n)) for n in LAYER_BUF_FIELDS})
+    wp, wn = _ws(ws)
+    _check("moe_layer_fwd", lib().moe_layer_fwd(ctypes.byref(cfg), _ptr(x), _ptr(w_router),
+                                                _ptr(bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                                _ptr(out), ctypes.byref(b) if b else None, wp, wn,
+                                                _stream(stream)))
+
+
+# ------------------------------------------------------------ device tensors
+def to_device(a, device="cuda") -> torch.Tensor:
+    """numpy array -> device tensor; uint16 arrays are bf16 bit patterns."""
+    import numpy as np
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def to_host_bits(t: torch.Tensor):
+    """device tensor -> numpy (bf16 as uint16 bit patterns)."""
+    import numpy as np
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()

@@ -1,0 +1,286 @@
+// C ABI of libmoe_mi355x.so (declared in include/moe.h): host-side argument
+// checks, workspace layout and the launch sequence of each entry point.
+// Nothing here allocates, frees or synchronises; every check runs before the
+// first launch, so a rejected call writes no output.
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr long kI32Max = 2147483647l;
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t elem_bytes(const moe_config& c) { return c.dtype == MOE_BF16 ? 2 : 4; }
+
+// Fields every entry point uses: sizes and element type.
+int check_core(const moe_config* c) {
+  if (!c) return MOE_EINVAL;
+  if (c->T < 0 || c->d <= 0 || c->E <= 0 || c->k <= 0 || c->f <= 0) return MOE_EINVAL;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_EINVAL;
+  if (c->k > c->E) return MOE_EINVAL;
+  if (c->k > 16 || c->E > 1024) return MOE_EUNSUPPORTED;
+  if (c->dtype == MOE_BF16 && (c->d % 64 || c->f % 64)) return MOE_EUNSUPPORTED;
+  if (c->dtype == MOE_F32 && (c->d % 4 || c->f % 4)) return MOE_EUNSUPPORTED;
+  const long rows = (long)c->T * c->k;
+  const long wide = c->d > c->f ? c->d : c->f;
+  if (rows * wide > kI32Max || (long)c->T * c->E > kI32Max) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+// Routing fields (router, permute, whole layer).
+int check_routing(const moe_config* c) {
+  int s = check_core(c);
+  if (s != MOE_OK) return s;
+  if (c->presel != 0 && (c->presel < c->k || c->presel > c->E)) return MOE_EINVAL;
+  if (c->presel > 32) return MOE_EUNSUPPORTED;
+  if (c->n_group < 1 || c->E % c->n_group != 0) return MOE_EINVAL;
+  if (c->topk_group < 1 || c->topk_group > c->n_group) return MOE_EINVAL;
+  if (c->n_group > 64) return MOE_EUNSUPPORTED;
+  const int nsel = c->presel > c->k ? c->presel : c->k;
+  if ((long)c->topk_group * (c->E / c->n_group) < nsel) return MOE_EINVAL;
+  if (c->renorm != 0 && c->renorm != 1) return MOE_EINVAL;
+  if (c->ep_ranks < 1 || c->E % c->ep_ranks != 0) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+size_t route_ws(const moe_config& c) {
+  const int s = router_splits(c);
+  return s > 1 ? align256((size_t)s * c.T * c.E * sizeof(float)) : 0;
+}
+
+// moe_layer_fwd workspace: the route/permute scratch (never live at the same
+// time, so they share one region) followed by every intermediate that `bufs`
+// does not provide.
+struct LayerLayout {
+  size_t scratch, logits, idx, w, offs, roffs, slot, src, xperm, h, y, total;
+};
+
+LayerLayout layer_layout(const moe_config& c, const moe_layer_bufs* b) {
+  LayerLayout L{};
+  const size_t A = (size_t)c.T * c.k, es = elem_bytes(c);
+  size_t off = 0;
+  auto take = [&](size_t bytes, bool provided) {
+    const size_t at = off;
+    if (!provided) off += align256(bytes);
+    return at;
+  };
+  const size_t rs = route_ws(c), ps = permute_ws_bytes(c);
+  L.scratch = take(rs > ps ? rs : ps, false);
+  L.logits = take((size_t)c.T * c.E * 4, b && b->logits);
+  L.idx = take(A * 4, b && b->topk_idx);
+  L.w = take(A * 4, b && b->topk_w);
+  L.offs = take(((size_t)c.E + 1) * 4, b && b->expert_offsets);
+  L.roffs = take(((size_t)c.ep_ranks + 1) * 4, b && b->rank_offsets);
+  L.slot = take(A * 4, b && b->slot_of);
+  L.src = take(A * 4, b && b->src_of);
+  L.xperm = take(A * c.d * es, b && b->x_perm);
+  L.h = take(A * c.f * es, b && b->h);
+  L.y = take(A * c.d * es, b && b->y_perm);
+  L.total = off;
+  return L;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+int check_ws(size_t need, const void* ws, size_t ws_bytes) {
+  if (need == 0) return MOE_OK;
+  if (!ws || ws_bytes < need) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+// Enqueue-only bodies, called after every check passed.
+int do_route(const moe_config& c, const void* x, const void* wr, const float* bias, float* logits,
+             int32_t* idx, float* w, void* ws, hipStream_t st) {
+  if (c.T == 0) return MOE_OK;
+  if (x) {
+    if (c.dtype == MOE_F32) {
+      hipError_t e = launch_router_gemm_f32(static_cast<const float*>(x),
+                                            static_cast<const float*>(wr), logits, c.T, c.d, c.E, st);
+      if (e != hipSuccess) return MOE_EHIP;
+      return status_of(launch_topk(c, logits, 1, bias, nullptr, idx, w, st));
+    }
+    const int s = router_splits(c);
+    float* dst = s > 1 ? static_cast<float*>(ws) : logits;
+    hipError_t e = launch_router_gemm_bf16(static_cast<const uint16_t*>(x),
+                                           static_cast<const uint16_t*>(wr), dst, c.T, c.d, c.E, s,
+                                           st);
+    if (e != hipSuccess) return MOE_EHIP;
+    return status_of(launch_topk(c, dst, s, bias, s > 1 ? logits : nullptr, idx, w, st));
+  }
+  return status_of(launch_topk(c, logits, 1, bias, nullptr, idx, w, st));
+}
+
+int do_permute(const moe_config& c, const void* x, const int32_t* idx, int32_t* offs,
+               int32_t* roffs, int32_t* slot, int32_t* src, void* xperm, void* ws, hipStream_t st) {
+  if (c.T == 0) {
+    hipError_t e = launch_fill_i32(offs, c.E + 1, 0, st);
+    if (e != hipSuccess) return MOE_EHIP;
+    return status_of(launch_fill_i32(roffs, c.ep_ranks + 1, 0, st));
+  }
+  return status_of(launch_permute(c, x, idx, offs, roffs, slot, src, xperm, ws, st));
+}
+
+int do_ffn(const moe_config& c, const void* xperm, const int32_t* offs, const void* wg,
+           const void* wu, const void* wd, void* h, void* y, hipStream_t st) {
+  if (c.T == 0) return MOE_OK;
+  if (wg) {
+    hipError_t e = launch_ffn_gate_up(c, xperm, offs, wg, wu, h, st);
+    if (e != hipSuccess) return MOE_EHIP;
+  }
+  if (wd) return status_of(launch_ffn_down(c, h, offs, wd, y, st));
+  return MOE_OK;
+}
+
+int do_combine(const moe_config& c, const void* y, const int32_t* slot, const float* w, void* out,
+               hipStream_t st) {
+  if (c.T == 0) return MOE_OK;
+  return status_of(launch_combine(c, y, slot, w, out, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (shape, flag, pointer or workspace)";
+    case MOE_EUNSUPPORTED: return "valid problem outside what the kernels implement";
+    case MOE_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_validate(const moe_config* cfg) { return check_routing(cfg); }
+
+int moe_workspace_bytes(const moe_config* cfg, int entry, size_t* bytes) {
+  if (!bytes) return MOE_EINVAL;
+  int s;
+  switch (entry) {
+    case MOE_ENTRY_ROUTE:
+      if ((s = check_routing(cfg)) != MOE_OK) return s;
+      *bytes = route_ws(*cfg);
+      return MOE_OK;
+    case MOE_ENTRY_PERMUTE:
+      if ((s = check_routing(cfg)) != MOE_OK) return s;
+      *bytes = cfg->T ? align256(permute_ws_bytes(*cfg)) : 0;
+      return MOE_OK;
+    case MOE_ENTRY_FFN:
+    case MOE_ENTRY_COMBINE:
+      if ((s = check_core(cfg)) != MOE_OK) return s;
+      *bytes = 0;
+      return MOE_OK;
+    case MOE_ENTRY_LAYER:
+      if ((s = check_routing(cfg)) != MOE_OK) return s;
+      *bytes = layer_layout(*cfg, nullptr).total;
+      return MOE_OK;
+    default:
+      return MOE_EINVAL;
+  }
+}
+
+int moe_route(const moe_config* cfg, const void* x, const void* w_router, const float* bias,
+              float* logits, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+              void* stream) {
+  int s = check_routing(cfg);
+  if (s != MOE_OK) return s;
+  const moe_config& c = *cfg;
+  if (c.T > 0) {
+    if (!logits || !topk_idx || !topk_w) return MOE_EINVAL;
+    if (x && !w_router) return MOE_EINVAL;
+    if (x && (s = check_ws(route_ws(c), ws, ws_bytes)) != MOE_OK) return s;
+  }
+  return do_route(c, x, w_router, bias, logits, topk_idx, topk_w, ws,
+                  static_cast<hipStream_t>(stream));
+}
+
+int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                int32_t* expert_offsets, int32_t* rank_offsets, int32_t* slot_of, int32_t* src_of,
+                void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_routing(cfg);
+  if (s != MOE_OK) return s;
+  const moe_config& c = *cfg;
+  if (!expert_offsets || !rank_offsets) return MOE_EINVAL;
+  if (c.T > 0) {
+    if (!x || !topk_idx || !slot_of || !src_of || !x_perm) return MOE_EINVAL;
+    if ((s = check_ws(permute_ws_bytes(c), ws, ws_bytes)) != MOE_OK) return s;
+  }
+  return do_permute(c, x, topk_idx, expert_offsets, rank_offsets, slot_of, src_of, x_perm, ws,
+                    static_cast<hipStream_t>(stream));
+}
+
+int moe_ffn_gate_up(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                    const void* w_gate, const void* w_up, void* h, void* stream) {
+  int s = check_core(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->T > 0 && (!x_perm || !expert_offsets || !w_gate || !w_up || !h)) return MOE_EINVAL;
+  return do_ffn(*cfg, x_perm, expert_offsets, w_gate, w_up, nullptr, h, nullptr,
+                static_cast<hipStream_t>(stream));
+}
+
+int moe_ffn_down(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
+                 const void* w_down, void* y_perm, void* stream) {
+  int s = check_core(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->T > 0 && (!h || !expert_offsets || !w_down || !y_perm)) return MOE_EINVAL;
+  return do_ffn(*cfg, nullptr, expert_offsets, nullptr, nullptr, w_down, const_cast<void*>(h),
+                y_perm, static_cast<hipStream_t>(stream));
+}
+
+int moe_grouped_ffn(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                    const void* w_gate, const void* w_up, const void* w_down, void* h, void* y_perm,
+                    void* stream) {
+  int s = check_core(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->T > 0 &&
+      (!x_perm || !expert_offsets || !w_gate || !w_up || !w_down || !h || !y_perm))
+    return MOE_EINVAL;
+  return do_ffn(*cfg, x_perm, expert_offsets, w_gate, w_up, w_down, h, y_perm,
+                static_cast<hipStream_t>(stream));
+}
+
+int moe_combine(const moe_config* cfg, const void* y_perm, const int32_t* slot_of,
+                const float* topk_w, void* out, void* stream) {
+  int s = check_core(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->T > 0 && (!y_perm || !slot_of || !topk_w || !out)) return MOE_EINVAL;
+  return do_combine(*cfg, y_perm, slot_of, topk_w, out, static_cast<hipStream_t>(stream));
+}
+
+int moe_layer_fwd(const moe_config* cfg, const void* x, const void* w_router, const float* bias,
+                  const void* w_gate, const void* w_up, const void* w_down, void* out,
+                  const moe_layer_bufs* bufs, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_routing(cfg);
+  if (s != MOE_OK) return s;
+  const moe_config& c = *cfg;
+  const LayerLayout L = layer_layout(c, bufs);
+  if (c.T > 0) {
+    if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return MOE_EINVAL;
+  }
+  if ((s = check_ws(L.total, ws, ws_bytes)) != MOE_OK) return s;
+  char* base = static_cast<char*>(ws);
+  auto pick = [&](void* given, size_t at) -> void* { return given ? given : base + at; };
+  const moe_layer_bufs none{};
+  const moe_layer_bufs& b = bufs ? *bufs : none;
+  void* scratch = base + L.scratch;
+  float* logits = static_cast<float*>(pick(b.logits, L.logits));
+  int32_t* idx = static_cast<int32_t*>(pick(b.topk_idx, L.idx));
+  float* w = static_cast<float*>(pick(b.topk_w, L.w));
+  int32_t* offs = static_cast<int32_t*>(pick(b.expert_offsets, L.offs));
+  int32_t* roffs = static_cast<int32_t*>(pick(b.rank_offsets, L.roffs));
+  int32_t* slot = static_cast<int32_t*>(pick(b.slot_of, L.slot));
+  int32_t* src = static_cast<int32_t*>(pick(b.src_of, L.src));
+  void* xperm = pick(b.x_perm, L.xperm);
+  void* h = pick(b.h, L.h);
+  void* y = pick(b.y_perm, L.y);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = do_route(c, x, w_router, bias, logits, idx, w, scratch, st)) != MOE_OK) return s;
+  if ((s = do_permute(c, x, idx, offs, roffs, slot, src, xperm, scratch, st)) != MOE_OK) return s;
+  if ((s = do_ffn(c, xperm, offs, w_gate, w_up, w_down, h, y, st)) != MOE_OK) return s;
+  return do_combine(c, y, slot, w, out, st);
+}
+
+}  // extern "C"

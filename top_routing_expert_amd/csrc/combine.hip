@@ -1,0 +1,126 @@
+// Weighted combine back to token order:
+//   out[t] = sum_{j=0..k-1} topk_w[t, j] * y_perm[slot_of[t*k + j]]   (fp32, j ascending)
+//
+// Pages: [SyncTax] §2.3 (each token's k expert outputs are summed with their
+// gate weights on the token's home device).
+//
+// gfx950 design: one wave per token, 16-byte vector gathers of the k expert
+// rows (each row contiguous), fp32 FMAs in a fixed j order, one 16-byte store
+// per lane.  HBM traffic is the algorithmic minimum: every y_perm row is read
+// once and every out row written once.
+#include "common.h"
+
+namespace moe {
+
+constexpr int kMaxKC = 16;
+
+__global__ __launch_bounds__(256) void combine_bf16_kernel(const u32x4* __restrict__ y,
+                                                           const int32_t* __restrict__ slot_of,
+                                                           const float* __restrict__ topk_w,
+                                                           u32x4* __restrict__ out, int T, int k,
+                                                           int row_vecs) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int p = 0;
+  float g = 0.f;
+  if (lane < k) {
+    p = slot_of[(size_t)t * k + lane];
+    p = p < 0 ? 0 : (p >= T * k ? T * k - 1 : p);  // keep every access in bounds
+    g = topk_w[(size_t)t * k + lane];
+  }
+  int pj[kMaxKC];
+  float gj[kMaxKC];
+#pragma unroll
+  for (int j = 0; j < kMaxKC; ++j) {
+    pj[j] = __shfl(p, j);
+    gj[j] = __shfl(g, j);
+  }
+  for (int v = lane; v < row_vecs; v += 64) {
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kMaxKC; ++j) {
+      if (j < k) {
+        const u32x4 w = y[(size_t)pj[j] * row_vecs + v];
+        a[0] = fmaf(gj[j], bf16_lo(w.x), a[0]);
+        a[1] = fmaf(gj[j], bf16_hi(w.x), a[1]);
+        a[2] = fmaf(gj[j], bf16_lo(w.y), a[2]);
+        a[3] = fmaf(gj[j], bf16_hi(w.y), a[3]);
+        a[4] = fmaf(gj[j], bf16_lo(w.z), a[4]);
+        a[5] = fmaf(gj[j], bf16_hi(w.z), a[5]);
+        a[6] = fmaf(gj[j], bf16_lo(w.w), a[6]);
+        a[7] = fmaf(gj[j], bf16_hi(w.w), a[7]);
+      }
+    }
+    u32x4 o;
+    o.x = pack_bf16x2(a[0], a[1]);
+    o.y = pack_bf16x2(a[2], a[3]);
+    o.z = pack_bf16x2(a[4], a[5]);
+    o.w = pack_bf16x2(a[6], a[7]);
+    out[(size_t)t * row_vecs + v] = o;
+  }
+}
+
+__global__ __launch_bounds__(256) void combine_f32_kernel(const float4* __restrict__ y,
+                                                          const int32_t* __restrict__ slot_of,
+                                                          const float* __restrict__ topk_w,
+                                                          float4* __restrict__ out, int T, int k,
+                                                          int row_vecs) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int p = 0;
+  float g = 0.f;
+  if (lane < k) {
+    p = slot_of[(size_t)t * k + lane];
+    p = p < 0 ? 0 : (p >= T * k ? T * k - 1 : p);  // keep every access in bounds
+    g = topk_w[(size_t)t * k + lane];
+  }
+  int pj[kMaxKC];
+  float gj[kMaxKC];
+#pragma unroll
+  for (int j = 0; j < kMaxKC; ++j) {
+    pj[j] = __shfl(p, j);
+    gj[j] = __shfl(g, j);
+  }
+  for (int v = lane; v < row_vecs; v += 64) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < kMaxKC; ++j) {
+      if (j < k) {
+        const float4 w = y[(size_t)pj[j] * row_vecs + v];
+        a.x = fmaf(gj[j], w.x, a.x);
+        a.y = fmaf(gj[j], w.y, a.y);
+        a.z = fmaf(gj[j], w.z, a.z);
+        a.w = fmaf(gj[j], w.w, a.w);
+      }
+    }
+    out[(size_t)t * row_vecs + v] = a;
+  }
+}
+
+hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_of,
+                          const float* topk_w, void* out, hipStream_t st) {
+  const dim3 grid(div_up(c.T, 4));
+  if (c.dtype == MOE_BF16) {
+    combine_bf16_kernel<<<grid, 256, 0, st>>>(static_cast<const u32x4*>(y_perm), slot_of, topk_w,
+                                              static_cast<u32x4*>(out), c.T, c.k, c.d / 8);
+  } else {
+    combine_f32_kernel<<<grid, 256, 0, st>>>(static_cast<const float4*>(y_perm), slot_of, topk_w,
+                                             static_cast<float4*>(out), c.T, c.k, c.d / 4);
+  }
+  return hipGetLastError();
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  fill_i32_kernel<<<div_up(n, 256), 256, 0, st>>>(p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace moe

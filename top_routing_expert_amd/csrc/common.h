@@ -1,0 +1,76 @@
+// Shared device helpers and the internal launch interface of libmoe_mi355x.
+// gfx950 (CDNA4) only: wave64, MFMA bf16 16x16x32, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Raw 16-byte vector.  A native vector type (not HIP's uint4 struct) so that
+// arrays of them are kept in registers by the compiler.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16 helpers
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 bits, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ------------------------------------------------------------ ordering keys
+// Maps a float to a uint32 whose unsigned order is the float order (finite
+// values; -0 must have been canonicalised to +0 before).
+__device__ __forceinline__ uint32_t ord_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ------------------------------------------------------------ launch helpers
+inline int div_up(long a, long b) { return (int)((a + b - 1) / b); }
+
+// Row-table grouped GEMM tile geometry (shared by the launcher and kernels).
+constexpr int kGemmBM = 128;   // token rows per tile
+constexpr int kGemmBNW = 256;  // weight rows per tile (gated: 128 gate + 128 up)
+constexpr int kGemmBK = 64;
+
+// ------------------------------------------------------------ internal launches
+// Every launcher returns hipSuccess or the launch error; shapes are validated
+// by the C-ABI layer before these are called.
+hipError_t launch_router_gemm_bf16(const uint16_t* x, const uint16_t* wr, float* dst, int T, int d,
+                                   int E, int splits, hipStream_t st);
+hipError_t launch_router_gemm_f32(const float* x, const float* wr, float* dst, int T, int d, int E,
+                                  hipStream_t st);
+hipError_t launch_topk(const moe_config& c, const float* partial, int splits, const float* bias,
+                       float* logits_out, int32_t* topk_idx, float* topk_w, hipStream_t st);
+int router_splits(const moe_config& c);
+
+hipError_t launch_permute(const moe_config& c, const void* x, const int32_t* topk_idx,
+                          int32_t* expert_offsets, int32_t* rank_offsets, int32_t* slot_of,
+                          int32_t* src_of, void* x_perm, void* ws, hipStream_t st);
+size_t permute_ws_bytes(const moe_config& c);
+
+hipError_t launch_ffn_gate_up(const moe_config& c, const void* x_perm, const int32_t* offs,
+                              const void* wg, const void* wu, void* h, hipStream_t st);
+hipError_t launch_ffn_down(const moe_config& c, const void* h, const int32_t* offs, const void* wd,
+                           void* y, hipStream_t st);
+
+hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_of,
+                          const float* topk_w, void* out, hipStream_t st);
+
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,344 @@
+// Router: gate GEMM z = x . Wr^T, then scores, (group-limited) top-k and gates.
+//
+// Pages: [EP-V4] §2.1 (each token's logits over all experts, then local top-2
+// and softmax gates), §3.2 (max subtraction before the exponential; partial
+// sort to the top-8 and an exact softmax over those); [V4-overlap] EP-on-IB
+// section (experts chosen only within the best groups/nodes).
+//
+// gfx950 design
+//  * Gate GEMM (bf16): MFMA 16x16x32, experts on the M side (A operand, staged
+//    through LDS per 64-wide K chunk), tokens on the N side (B operand, read
+//    straight from HBM into registers: every x row is used by exactly one
+//    wave, so it never needs LDS).  A block is 4 waves x 16 tokens and up to
+//    256 experts.  Short batches are split along d into `splits` partial
+//    products that the top-k kernel sums in a fixed order, so logits stay
+//    bitwise reproducible (no float atomics) while the grid still covers the
+//    256 CUs.
+//  * Top-k: a group of LPT = min(64, pow2 >= E) lanes per token; each lane
+//    holds E/LPT scores.  Every selection round is one argmax over 64-bit keys
+//    (order-preserving score bits, then inverted index), reduced with xor
+//    shuffles: highest score wins, ties go to the lowest expert index.
+#include "common.h"
+
+namespace moe {
+
+// ============================================================== gate GEMM bf16
+// One K chunk = 64 bf16 of every row.  Inside a chunk lane group g = lane/16
+// owns k in [16g, 16g+16) (two 16-byte pieces); the two MFMA k-slabs take the
+// first and second piece.  A and B use the same assignment, so the products
+// pair up correctly whatever the hardware's k order inside one MFMA is.
+template <int EC>
+__global__ __launch_bounds__(256) void router_gemm_bf16_kernel(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ wr,
+                                                               float* __restrict__ dst, int T, int d,
+                                                               int E, int splits) {
+  constexpr int NF = EC / 16;                         // expert fragments per wave
+  constexpr int WLOADS = (EC * 8 + 255) / 256;        // 16-byte pieces per thread per chunk
+  __shared__ u32x4 sW[2][EC * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e0 = blockIdx.z * EC;
+  const int nch = d >> 6;
+  const int c_beg = (int)((long)blockIdx.y * nch / splits);
+  const int c_end = (int)((long)(blockIdx.y + 1) * nch / splits);
+  const int g = lane >> 4;
+
+  const int tok = blockIdx.x * 64 + wave * 16 + (lane & 15);
+  const u32x4* xrow = reinterpret_cast<const u32x4*>(x + (size_t)min(tok, T - 1) * d);
+
+  // W chunk loader: piece i of this thread covers row (p >> 3), piece (p & 7).
+  const u32x4* wrow[WLOADS];
+  int wdst[WLOADS];
+  bool wact[WLOADS];
+#pragma unroll
+  for (int i = 0; i < WLOADS; ++i) {
+    const int p = tid + i * 256;
+    wact[i] = p < EC * 8;
+    const int r = p >> 3, q = p & 7;
+    const int er = min(e0 + r, E - 1);
+    wrow[i] = reinterpret_cast<const u32x4*>(wr + (size_t)er * d) + q;
+    wdst[i] = r * 8 + (q ^ (r & 7));
+  }
+
+  f32x4 acc[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 wreg[WLOADS];
+  u32x4 xv[2], xn[2];
+  if (c_beg < c_end) {
+#pragma unroll
+    for (int i = 0; i < WLOADS; ++i)
+      if (wact[i]) wreg[i] = wrow[i][c_beg * 8];
+    xv[0] = xrow[c_beg * 8 + 2 * g];
+    xv[1] = xrow[c_beg * 8 + 2 * g + 1];
+#pragma unroll
+    for (int i = 0; i < WLOADS; ++i)
+      if (wact[i]) sW[0][wdst[i]] = wreg[i];
+  }
+  __syncthreads();
+
+  for (int c = c_beg; c < c_end; ++c) {
+    const int st = (c - c_beg) & 1;
+    const bool more = c + 1 < c_end;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < WLOADS; ++i)
+        if (wact[i]) wreg[i] = wrow[i][(c + 1) * 8];
+      xn[0] = xrow[(c + 1) * 8 + 2 * g];
+      xn[1] = xrow[(c + 1) * 8 + 2 * g + 1];
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 b = as_bf16x8(xv[s]);
+      const int q = 2 * g + s;
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int r = f * 16 + (lane & 15);
+        const bf16x8 a = as_bf16x8(sW[st][r * 8 + (q ^ (r & 7))]);
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[f], 0, 0, 0);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < WLOADS; ++i)
+        if (wact[i]) sW[st ^ 1][wdst[i]] = wreg[i];
+      xv[0] = xn[0];
+      xv[1] = xn[1];
+    }
+    __syncthreads();
+  }
+
+  // acc[f][i] = z[token = lane&15][expert = e0 + 16f + 4(lane>>4) + i]
+  if (tok < T) {
+    float* drow = dst + ((size_t)blockIdx.y * T + tok) * E;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = e0 + f * 16 + 4 * g + i;
+        if (e < E) drow[e] = acc[f][i];
+      }
+    }
+  }
+}
+
+int router_splits(const moe_config& c) {
+  if (c.dtype != MOE_BF16 || c.T == 0) return 1;
+  const int nch = c.d / 64;
+  const int ec = c.E <= 16 ? 16 : c.E <= 32 ? 32 : c.E <= 64 ? 64 : c.E <= 128 ? 128 : 256;
+  const long tiles = (long)div_up(c.T, 64) * div_up(c.E, ec);
+  long s = (1024 + tiles - 1) / tiles;
+  if (s > 16) s = 16;
+  if (s > nch) s = nch;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+hipError_t launch_router_gemm_bf16(const uint16_t* x, const uint16_t* wr, float* dst, int T, int d,
+                                   int E, int splits, hipStream_t st) {
+  const int ec = E <= 16 ? 16 : E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256;
+  dim3 grid(div_up(T, 64), splits, div_up(E, ec));
+  switch (ec) {
+    case 16: router_gemm_bf16_kernel<16><<<grid, 256, 0, st>>>(x, wr, dst, T, d, E, splits); break;
+    case 32: router_gemm_bf16_kernel<32><<<grid, 256, 0, st>>>(x, wr, dst, T, d, E, splits); break;
+    case 64: router_gemm_bf16_kernel<64><<<grid, 256, 0, st>>>(x, wr, dst, T, d, E, splits); break;
+    case 128: router_gemm_bf16_kernel<128><<<grid, 256, 0, st>>>(x, wr, dst, T, d, E, splits); break;
+    default: router_gemm_bf16_kernel<256><<<grid, 256, 0, st>>>(x, wr, dst, T, d, E, splits); break;
+  }
+  return hipGetLastError();
+}
+
+// ============================================================== gate GEMM f32
+// Small fp32 problems: one thread per logit, sequential fp32 FMA over d.
+__global__ void router_gemm_f32_kernel(const float* __restrict__ x, const float* __restrict__ wr,
+                                       float* __restrict__ z, int T, int d, int E) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long)T * E) return;
+  const int t = (int)(i / E), e = (int)(i % E);
+  const float* xr = x + (size_t)t * d;
+  const float* wrow = wr + (size_t)e * d;
+  float acc = 0.f;
+  for (int j = 0; j < d; ++j) acc = fmaf(xr[j], wrow[j], acc);
+  z[i] = acc;
+}
+
+hipError_t launch_router_gemm_f32(const float* x, const float* wr, float* dst, int T, int d, int E,
+                                  hipStream_t st) {
+  const long n = (long)T * E;
+  router_gemm_f32_kernel<<<div_up(n, 256), 256, 0, st>>>(x, wr, dst, T, d, E);
+  return hipGetLastError();
+}
+
+// ============================================================== top-k + gates
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  const int lo = __shfl_xor((int)(uint32_t)v, m);
+  const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+template <int LPT>
+__device__ __forceinline__ unsigned long long seg_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = LPT / 2; o > 0; o >>= 1) {
+    const unsigned long long w = shfl_xor_u64(v, o);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+template <int LPT>
+__device__ __forceinline__ uint32_t seg_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = LPT / 2; o > 0; o >>= 1) {
+    const uint32_t w = (uint32_t)__shfl_xor((int)v, o);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+template <int LPT>
+__device__ __forceinline__ float seg_sum(float v) {
+#pragma unroll
+  for (int o = LPT / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ float ord_key_inv(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+constexpr int kMaxEPL = 16;  // E <= 1024 with 64 lanes per token
+
+template <int LPT>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ partial, int splits,
+                                                   const float* __restrict__ bias,
+                                                   float* __restrict__ logits_out,
+                                                   int32_t* __restrict__ topk_idx,
+                                                   float* __restrict__ topk_w, int T, int E, int k,
+                                                   int n_group, int topk_group, int presel,
+                                                   int renorm) {
+  constexpr int TPW = 64 / LPT;  // tokens per wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int q = lane % LPT;
+  const int t = (blockIdx.x * 4 + wave) * TPW + lane / LPT;
+  const bool live = t < T;
+  const int epl = (E + LPT - 1) / LPT;
+
+  // scores s = z + b (one fp32 add), -0 -> +0; key32 = order-preserving bits
+  uint32_t key[kMaxEPL];
+#pragma unroll
+  for (int i = 0; i < kMaxEPL; ++i) {
+    key[i] = 0u;
+    const int e = q + i * LPT;
+    if (i < epl && e < E && live) {
+      float z = partial[(size_t)t * E + e];
+      for (int s = 1; s < splits; ++s) z += partial[((size_t)s * T + t) * E + e];
+      if (logits_out) logits_out[(size_t)t * E + e] = z;
+      float sc = bias ? __fadd_rn(z, bias[e]) : z;
+      uint32_t u = __float_as_uint(sc);
+      if (u == 0x80000000u) u = 0u;
+      key[i] = ord_key(__uint_as_float(u));
+    }
+  }
+
+  // group-limited eligibility: keep the topk_group groups with the largest max
+  unsigned long long kept = ~0ull;
+  const bool grouped = n_group > 1 && topk_group < n_group;
+  int gsz = E / n_group;
+  if (grouped) {
+    uint32_t my_g = 0u;
+    for (int g = 0; g < n_group; ++g) {
+      uint32_t m = 0u;
+#pragma unroll
+      for (int i = 0; i < kMaxEPL; ++i) {
+        const int e = q + i * LPT;
+        if (i < epl && e < E && e / gsz == g) m = key[i] > m ? key[i] : m;
+      }
+      m = seg_max_u32<LPT>(m);
+      if (q == g) my_g = m;
+    }
+    kept = 0ull;
+    for (int r = 0; r < topk_group; ++r) {
+      unsigned long long cand = 0ull;
+      if (q < n_group && !((kept >> q) & 1ull))
+        cand = ((unsigned long long)my_g << 32) | (0xffffffffu - (uint32_t)q);
+      cand = seg_max_u64<LPT>(cand);
+      const int gw = (int)(0xffffffffu - (uint32_t)cand);
+      kept |= 1ull << gw;
+    }
+  }
+
+  // selection rounds: the r-th winner is kept by lane q == r
+  const int nsel = presel > k ? presel : k;
+  uint32_t taken = 0u;
+  int my_e = 0;
+  float my_s = 0.f, s_max = 0.f;
+  for (int r = 0; r < nsel; ++r) {
+    unsigned long long best = 0ull;
+#pragma unroll
+    for (int i = 0; i < kMaxEPL; ++i) {
+      const int e = q + i * LPT;
+      const bool ok = i < epl && e < E && !((taken >> i) & 1u) &&
+                      (!grouped || ((kept >> (e / gsz)) & 1ull));
+      const unsigned long long cand =
+          ok ? (((unsigned long long)key[i] << 32) | (0xffffffffu - (uint32_t)e)) : 0ull;
+      best = cand > best ? cand : best;
+    }
+    best = seg_max_u64<LPT>(best);
+    const int we = (int)(0xffffffffu - (uint32_t)best);
+    const float ws = ord_key_inv((uint32_t)(best >> 32));
+    if (we % LPT == q) taken |= 1u << (we / LPT);
+    if (r == 0) s_max = ws;
+    if (q == r) {
+      my_e = we;
+      my_s = ws;
+    }
+  }
+
+  // gates: e_j = exp(s_j - m) over the chosen / pre-selected / all experts
+  const float ej = q < nsel ? expf(my_s - s_max) : 0.f;
+  float denom;
+  if (renorm) {
+    denom = seg_sum<LPT>(q < k ? ej : 0.f);
+  } else if (presel) {
+    denom = seg_sum<LPT>(q < presel ? ej : 0.f);
+  } else {
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxEPL; ++i) {
+      const int e = q + i * LPT;
+      if (i < epl && e < E) part += expf(ord_key_inv(key[i]) - s_max);
+    }
+    denom = seg_sum<LPT>(part);
+  }
+  if (live && q < k) {
+    topk_idx[(size_t)t * k + q] = my_e;
+    topk_w[(size_t)t * k + q] = ej / denom;
+  }
+}
+
+hipError_t launch_topk(const moe_config& c, const float* partial, int splits, const float* bias,
+                       float* logits_out, int32_t* topk_idx, float* topk_w, hipStream_t st) {
+  int lpt = 1;
+  while (lpt < c.E && lpt < 64) lpt <<= 1;
+  if (lpt < 2) lpt = 2;
+  const int tpb = 4 * (64 / lpt);
+  const dim3 grid(div_up(c.T, tpb));
+#define MOE_TOPK(L)                                                                        \
+  topk_kernel<L><<<grid, 256, 0, st>>>(partial, splits, bias, logits_out, topk_idx, topk_w, \
+                                       c.T, c.E, c.k, c.n_group, c.topk_group, c.presel,    \
+                                       c.renorm)
+  switch (lpt) {
+    case 2: MOE_TOPK(2); break;
+    case 4: MOE_TOPK(4); break;
+    case 8: MOE_TOPK(8); break;
+    case 16: MOE_TOPK(16); break;
+    case 32: MOE_TOPK(32); break;
+    default: MOE_TOPK(64); break;
+  }
+#undef MOE_TOPK
+  return hipGetLastError();
+}
+
+}  // namespace moe
