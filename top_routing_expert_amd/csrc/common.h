@@ -12,6 +12,7 @@ namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 // Raw 16-byte vector.  A native vector type (not HIP's uint4 struct) so that
 // arrays of them are kept in registers by the compiler.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -41,11 +42,6 @@ __device__ __forceinline__ uint32_t ord_key(float s) {
 
 // ------------------------------------------------------------ launch helpers
 inline int div_up(long a, long b) { return (int)((a + b - 1) / b); }
-
-// Row-table grouped GEMM tile geometry (shared by the launcher and kernels).
-constexpr int kGemmBM = 128;   // token rows per tile
-constexpr int kGemmBNW = 256;  // weight rows per tile (gated: 128 gate + 128 up)
-constexpr int kGemmBK = 64;
 
 // ------------------------------------------------------------ internal launches
 // Every launcher returns hipSuccess or the launch error; shapes are validated

@@ -34,13 +34,11 @@
 //    the 8 XCDs (blocks are dispatched to XCDs round-robin) in equal
 //    contiguous ranges, so the empty slots of the worst-case grid never pile
 //    up on one XCD.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
-
-constexpr int BM = kGemmBM;    // 128 token rows
-constexpr int BNW = kGemmBNW;  // 256 weight rows
-constexpr int BK = kGemmBK;    // 64
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -52,14 +50,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // writes LDS bytes [lds + 16 L, lds + 16 L + 16); `lds` is wave-uniform.  Issued
 // as inline asm so that the wait for it stays under this kernel's explicit
 // vmcnt control (the compiler would otherwise drain every copy in flight
-// before each LDS read).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
+// before each LDS read).  The kernel issues no other vector-memory reads in
+// its main loop, so the counts below are exact.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
                : "memory", "m0");
 }
-#pragma clang diagnostic pop
 
 // Wait until at most N of this wave's vector-memory operations are in flight,
 // then barrier.  No memory fence: the LDS DMA traffic is ordered by vmcnt.
@@ -68,18 +64,29 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-constexpr int kStages = 3;
-constexpr int kChunksA = BNW * 128 / 1024;         // 1 KB LDS chunks per stage: 32 weights
-constexpr int kChunksB = BM * 128 / 1024;          // 16 tokens
-constexpr int kDmaPerWave = (kChunksA + kChunksB) / 4;  // 12
+// LDS image of one stage: rows of 64 bytes (32 k), weight-tile rows first,
+// then token-tile rows; the 16-byte piece q of row r sits at q ^ ((r >> 2) & 3).
+__device__ __forceinline__ int lds_piece(int r, int q) { return r * 4 + (q ^ ((r >> 2) & 3)); }
 
-template <bool GATED>
+constexpr int kStages = 4;
+constexpr int kStageK = 32;
+
+// WA / WB: 32-row fragments per wave on the weight / token side.  Four waves
+// in a 2 (weights) x 2 (tokens) layout; the block tile is 64 WA weight rows
+// by 64 WB token rows.
+template <bool GATED, int WA, int WB>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offs,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, uint16_t* __restrict__ out,
     int E, int N, int K, int rows, int n_tiles, int band) {
-  // per stage: weights 256 rows x 128 B, then tokens 128 rows x 128 B
-  __shared__ u32x4 sbuf[kStages][(kChunksA + kChunksB) * 64];
+  constexpr int TW = 64 * WA;                   // weight rows per tile
+  constexpr int TM = 64 * WB;                   // token rows per tile
+  constexpr int TN = GATED ? TW / 2 : TW;       // output features per tile
+  constexpr int ROWS = TW + TM;                 // LDS rows per stage
+  constexpr int CHUNKS = ROWS * 64 / 1024;      // 1 KB DMA chunks per stage
+  constexpr int DPW = CHUNKS / 4;               // DMA instructions per wave per stage
+  static_assert(CHUNKS % 4 == 0, "stage must split evenly over 4 waves");
+  __shared__ u32x4 sbuf[kStages][ROWS * 4];
   __shared__ int s_tile[4];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -100,7 +107,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
       int nt = 0;
       if (e < E) {  // clamp a malformed table into [0, rows] so accesses stay in bounds
         const int o0 = min(max(offs[e], 0), rows), o1 = min(max(offs[e + 1], o0), rows);
-        nt = (o1 - o0 + BM - 1) / BM;
+        nt = (o1 - o0 + TM - 1) / TM;
       }
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) nt += __shfl_xor(nt, o);
@@ -118,7 +125,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
           o0 = min(max(offs[e], 0), rows);
           o1 = min(max(offs[e + 1], o0), rows);
         }
-        const int mt = (o1 - o0 + BM - 1) / BM;
+        const int mt = (o1 - o0 + TM - 1) / TM;
         int incl = mt * n_tiles;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
@@ -141,7 +148,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
             m = full * g + rr % gl;
           }
           s_tile[0] = e;
-          s_tile[1] = o0 + m * BM;
+          s_tile[1] = o0 + m * TM;
           s_tile[2] = o1;
           s_tile[3] = n;
         }
@@ -153,29 +160,24 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   const int e = s_tile[0];
   if (e < 0) return;  // block-uniform
   const int row0 = s_tile[1], row_end = s_tile[2], n_tile = s_tile[3];
-  const int n0 = n_tile * (GATED ? BNW / 2 : BNW);
+  const int n0 = n_tile * TN;
 
-  // ---- DMA assignment.  Wave w copies LDS chunks c = w + 4 i (i < 12) of every
-  // stage; chunk c < 32 holds weight-tile rows 8c..8c+7, the others token-tile
-  // rows.  Lane l lands at row 8c' + l/8, physical 16-byte piece l%8, so it
-  // fetches the logical piece (l%8) ^ (row & 7) = (l & 7) ^ (l >> 3): the LDS
-  // image is XOR-swizzled exactly as the fragment reads below expect.
-  const int lr = lane >> 3;
-  const int lq = (lane & 7) ^ lr;
-  const uint16_t* gsrc[kDmaPerWave];
-  int ldst[kDmaPerWave];  // u32x4 index of the chunk inside a stage
+  // ---- DMA assignment.  Wave w copies chunks c = w + 4 i (i < DPW) of every
+  // stage; chunk c holds LDS rows 16c..16c+15 (weight rows first).  Lane l
+  // lands at row 16c + l/4, physical piece l%4, so it fetches the logical
+  // piece (l & 3) ^ ((row >> 2) & 3) = (l & 3) ^ ((l >> 4) & 3).
+  const int lq = (lane & 3) ^ ((lane >> 4) & 3);
+  const uint16_t* gsrc[DPW];
   const size_t wstride = (size_t)N * K;
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
-    const int c = wave + 4 * i;
-    ldst[i] = c * 64;
-    if (c < kChunksA) {
-      const int r = 8 * c + lr;  // weight tile row 0..255
+  for (int i = 0; i < DPW; ++i) {
+    const int r = 16 * (wave + 4 * i) + (lane >> 2);  // LDS row 0..ROWS-1
+    if (r < TW) {
       const uint16_t* base;
       int n;
       if (GATED) {
-        n = n0 + (r & 127);
-        base = (r < 128 ? w0 : w1) + (size_t)e * wstride;
+        n = n0 + (r % (TW / 2));
+        base = (r < TW / 2 ? w0 : w1) + (size_t)e * wstride;
       } else {
         n = n0 + r;
         base = w0 + (size_t)e * wstride;
@@ -183,103 +185,136 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
       n = min(n, N - 1);
       gsrc[i] = base + (size_t)n * K + lq * 8;
     } else {
-      const int r = min(row0 + 8 * (c - kChunksA) + lr, row_end - 1);
-      gsrc[i] = act + (size_t)r * K + lq * 8;
+      const int t = min(row0 + (r - TW), row_end - 1);
+      gsrc[i] = act + (size_t)t * K + lq * 8;
     }
   }
 
-  // ---- fragment addressing (constant per lane)
+  // ---- fragments.  MFMA 32x32x16: lane l holds row (l & 31) of a 32-row
+  // fragment and k in [8 (l >> 5), 8 (l >> 5) + 8) of a 16-wide slab, for
+  // weights (A) and tokens (B) alike.  Wave (wn, wm) owns WA weight fragments
+  // (GATED: WA/2 gate fragments and the matching up fragments, i.e. 32 WA/2
+  // output features) and WB token fragments.
   const int wn = wave >> 1, wm = wave & 1;
-  int arow[8];
+  const int lk = lane >> 5;
+  int arow[WA];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < WA; ++i) {
     if (GATED)
-      arow[i] = (i < 4 ? 0 : 128) + wn * 64 + (i & 3) * 16 + (lane & 15);
+      arow[i] = (i < WA / 2 ? 0 : TW / 2) + wn * 16 * WA + (i % (WA / 2)) * 32 + (lane & 31);
     else
-      arow[i] = wn * 128 + i * 16 + (lane & 15);
+      arow[i] = wn * 32 * WA + i * 32 + (lane & 31);
   }
-  int brow[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) brow[j] = BNW + wm * 64 + j * 16 + (lane & 15);  // token rows follow
-  const int lsw = lane & 7;  // (row & 7) of every fragment row this lane reads
+  // token fragments of this wave that hold any row; the others are skipped
+  const int tok0 = wm * 32 * WB;
+  const int jn = __builtin_amdgcn_readfirstlane(min(WB, max(0, (row_end - row0 - tok0 + 31) >> 5)));
+  const int brow0 = TW + tok0 + (lane & 31);
 
-  f32x4 acc[8][4];
+  f32x16 acc[WA][WB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < WA; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < WB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = K / BK;
+  const int nk = K / kStageK;
   const uint32_t lds0 = lds_addr(&sbuf[0][0]);
-  auto issue = [&](int kt, int st) {
-    const uint32_t sbase = lds0 + (uint32_t)st * (kChunksA + kChunksB) * 1024u;
+  auto issue = [&](int kt) {
+    const uint32_t sbase = lds0 + (uint32_t)(kt % kStages) * (ROWS * 64u);
 #pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i)
-      dma16(gsrc[i] + (size_t)kt * BK, sbase + (uint32_t)ldst[i] * 16u);
+    for (int i = 0; i < DPW; ++i)
+      dma16(gsrc[i] + (size_t)kt * kStageK, sbase + (uint32_t)(wave + 4 * i) * 1024u);
   };
-  issue(0, 0);
-  if (nk > 1) issue(1, 1);
-
-  int st = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    // this wave's copies of stage kt are done once only stage kt+1's (if any)
-    // remain in flight; the barrier then publishes every wave's copies and
-    // guarantees that nobody still reads the buffer refilled below
-    if (kt + 1 < nk)
-      wait_vm_barrier<kDmaPerWave>();
-    else
-      wait_vm_barrier<0>();
-    if (kt + 2 < nk) issue(kt + 2, st == 0 ? 2 : st - 1);
-    const u32x4* sb = sbuf[st];
+  // Main loop, specialised on JN = token fragments of this wave that hold any
+  // row (wave-uniform; the other fragments' reads and MFMAs are skipped).
+  auto main_loop = [&](auto jn_c) {
+    constexpr int JN = decltype(jn_c)::value;
+    auto load_frags = [&](const u32x4* sb, int slab, bf16x8 (&a)[WA], bf16x8 (&b)[WB]) {
+      const int q = 2 * slab + lk;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int q = (4 * s + (lane >> 4)) ^ lsw;
-      bf16x8 a[8], b[4];
+      for (int i = 0; i < WA; ++i) a[i] = as_bf16x8(sb[lds_piece(arow[i], q)]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a[i] = as_bf16x8(sb[arow[i] * 8 + q]);
+      for (int j = 0; j < JN; ++j) b[j] = as_bf16x8(sb[lds_piece(brow0 + 32 * j, q)]);
+    };
+    auto mfma_slab = [&](const bf16x8 (&a)[WA], const bf16x8 (&b)[WB]) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = as_bf16x8(sb[brow[j] * 8 + q]);
+      for (int j = 0; j < JN; ++j)
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < WA; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    };
+    // Pipeline.  Stage j (32-wide k-step j) goes to LDS buffer j % 4 and is
+    // issued three steps ahead.  At the top of step kt this wave waits for
+    // its own copies of stage kt (later stages may stay in flight); the
+    // barrier publishes every wave's copies and guarantees that nobody still
+    // reads buffer (kt + 3) % 4, which is refilled right after.
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < kStages - 1; ++i)
+      if (i < nk) issue(i);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int ahead = min(nk - 1 - kt, kStages - 2);  // stages after kt already issued
+      if (ahead >= 2)
+        wait_vm_barrier<2 * DPW>();
+      else if (ahead == 1)
+        wait_vm_barrier<DPW>();
+      else
+        wait_vm_barrier<0>();
+      if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
+      if (JN > 0) {
+        const u32x4* sb = sbuf[kt % kStages];
+        bf16x8 fa0[WA], fb0[WB], fa1[WA], fb1[WB];
+        load_frags(sb, 0, fa0, fb0);
+        load_frags(sb, 1, fa1, fb1);
+        mfma_slab(fa0, fb0);
+        mfma_slab(fa1, fb1);
+      }
     }
-    st = st == 2 ? 0 : st + 1;
+  };
+  switch (jn) {
+    case 0: main_loop(std::integral_constant<int, 0>()); break;
+    case 1: main_loop(std::integral_constant<int, 1>()); break;
+    case 2: main_loop(std::integral_constant<int, (WB >= 2 ? 2 : 1)>()); break;
+    case 3: main_loop(std::integral_constant<int, (WB >= 3 ? 3 : 1)>()); break;
+    default: main_loop(std::integral_constant<int, WB>()); break;
   }
 
-  // ---- epilogue: acc[i][j][r] = C[weight row arow_base(i) + 4(lane>>4) + r][token brow[j]]
-  const int g4 = 4 * (lane >> 4);
+  // ---- epilogue: acc[i][j][4 g + r] = C[fragment-i row 8 g + 4 (lane >> 5) + r]
+  // [token fragment j, token lane & 31]: four consecutive output features per
+  // group g, stored as one 8-byte vector.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = row0 + brow[j] - BNW;
-    if (row >= row_end) continue;
+  for (int j = 0; j < WB; ++j) {
+    const int row = row0 + tok0 + 32 * j + (lane & 31);
+    if (j >= jn || row >= row_end) continue;
     uint16_t* orow = out + (size_t)row * N;
-    if (GATED) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = n0 + wn * 64 + i * 16 + g4;
-        if (n >= N) continue;
-        float hv[4];
+    for (int g = 0; g < 4; ++g) {
+      if (GATED) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float gt = acc[i][j][r], up = acc[i + 4][j][r];
-          hv[r] = gt / (1.0f + __expf(-gt)) * up;
+        for (int i = 0; i < WA / 2; ++i) {
+          const int n = n0 + wn * 16 * WA + 32 * i + 8 * g + 4 * lk;
+          if (n >= N) continue;
+          float hv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gt = acc[i][j][4 * g + r], up = acc[i + WA / 2][j][4 * g + r];
+            hv[r] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+          }
+          u32x2 pk;
+          pk.x = pack_bf16x2(hv[0], hv[1]);
+          pk.y = pack_bf16x2(hv[2], hv[3]);
+          *reinterpret_cast<u32x2*>(orow + n) = pk;
         }
-        u32x2 pk;
-        pk.x = pack_bf16x2(hv[0], hv[1]);
-        pk.y = pack_bf16x2(hv[2], hv[3]);
-        *reinterpret_cast<u32x2*>(orow + n) = pk;
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int n = n0 + wn * 128 + i * 16 + g4;
-        if (n >= N) continue;
-        u32x2 pk;
-        pk.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-        pk.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-        *reinterpret_cast<u32x2*>(orow + n) = pk;
+        for (int i = 0; i < WA; ++i) {
+          const int n = n0 + wn * 32 * WA + 32 * i + 8 * g + 4 * lk;
+          if (n >= N) continue;
+          u32x2 pk;
+          pk.x = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+          pk.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          *reinterpret_cast<u32x2*>(orow + n) = pk;
+        }
       }
     }
   }
@@ -333,15 +368,42 @@ __global__ void ffn_down_f32_kernel(const float* __restrict__ h, const int32_t* 
 }
 
 // ------------------------------------------------------------------ launchers
-static void gemm_grid(int rows, int E, int N_out_per_tile, int N, int* n_tiles, int* band,
-                      int* blocks) {
-  *n_tiles = div_up(N, N_out_per_tile);
-  // upper bound of sum_e ceil(c_e / BM) over any row table with `rows` rows
-  long m_slots = ((long)rows + (long)E * (BM - 1)) / BM;
+// Tile choice.  256x256 tiles (128x128 per wave) halve LDS fragment traffic
+// per flop; they are used unless they would leave fewer than ~2 blocks per CU,
+// in which case 256 weight rows x 128 tokens keep the grid full.
+struct GemmPlan {
+  int wb;       // token fragments per wave (4: 256-token tiles, 2: 128)
+  int n_tiles;  // weight tiles over N
+  int blocks;   // grid size (multiple of 8, worst case over any row table)
+};
+
+static GemmPlan plan_gemm(long rows, int E, int N, bool gated) {
+  const int tn = gated ? 128 : 256;
+  GemmPlan p;
+  p.n_tiles = div_up(N, tn);
+  const int cus = 256;
+  const long avg = (rows + E - 1) / E;  // typical rows per expert
+  const long est256 = (long)p.n_tiles * E * ((avg + 255) / 256);
+  p.wb = est256 >= 2 * cus ? 4 : 2;
+  const int tm = 64 * p.wb;
+  long m_slots = (rows + (long)E * (tm - 1)) / tm;  // upper bound of sum_e ceil(c_e / tm)
   if (m_slots < 1) m_slots = 1;
-  *band = 8;
-  const long total = (long)(*n_tiles) * m_slots;
-  *blocks = (int)((total + 7) / 8 * 8);
+  const long total = (long)p.n_tiles * m_slots;
+  p.blocks = (int)((total + 7) / 8 * 8);
+  return p;
+}
+
+template <bool GATED>
+static void launch_gemm(const GemmPlan& p, const uint16_t* act, const int32_t* offs,
+                        const uint16_t* w0, const uint16_t* w1, uint16_t* out, int E, int N, int K,
+                        int rows, hipStream_t st) {
+  const int band = 8;
+  if (p.wb == 4)
+    grouped_gemm_bf16_kernel<GATED, 4, 4><<<p.blocks, 256, 0, st>>>(act, offs, w0, w1, out, E, N,
+                                                                    K, rows, p.n_tiles, band);
+  else
+    grouped_gemm_bf16_kernel<GATED, 4, 2><<<p.blocks, 256, 0, st>>>(act, offs, w0, w1, out, E, N,
+                                                                    K, rows, p.n_tiles, band);
 }
 
 hipError_t launch_ffn_gate_up(const moe_config& c, const void* x_perm, const int32_t* offs,
@@ -354,12 +416,10 @@ hipError_t launch_ffn_gate_up(const moe_config& c, const void* x_perm, const int
         static_cast<const float*>(wu), static_cast<float*>(h), c.E, c.f, c.d, rows);
     return hipGetLastError();
   }
-  int n_tiles, band, blocks;
-  gemm_grid((int)rows, c.E, BNW / 2, c.f, &n_tiles, &band, &blocks);
-  grouped_gemm_bf16_kernel<true><<<blocks, 256, 0, st>>>(
-      static_cast<const uint16_t*>(x_perm), offs, static_cast<const uint16_t*>(wg),
-      static_cast<const uint16_t*>(wu), static_cast<uint16_t*>(h), c.E, c.f, c.d, (int)rows,
-      n_tiles, band);
+  const GemmPlan p = plan_gemm(rows, c.E, c.f, true);
+  launch_gemm<true>(p, static_cast<const uint16_t*>(x_perm), offs,
+                    static_cast<const uint16_t*>(wg), static_cast<const uint16_t*>(wu),
+                    static_cast<uint16_t*>(h), c.E, c.f, c.d, (int)rows, st);
   return hipGetLastError();
 }
 
@@ -373,11 +433,9 @@ hipError_t launch_ffn_down(const moe_config& c, const void* h, const int32_t* of
         c.E, c.d, c.f, rows);
     return hipGetLastError();
   }
-  int n_tiles, band, blocks;
-  gemm_grid((int)rows, c.E, BNW, c.d, &n_tiles, &band, &blocks);
-  grouped_gemm_bf16_kernel<false><<<blocks, 256, 0, st>>>(
-      static_cast<const uint16_t*>(h), offs, static_cast<const uint16_t*>(wd), nullptr,
-      static_cast<uint16_t*>(y), c.E, c.d, c.f, (int)rows, n_tiles, band);
+  const GemmPlan p = plan_gemm(rows, c.E, c.d, false);
+  launch_gemm<false>(p, static_cast<const uint16_t*>(h), offs, static_cast<const uint16_t*>(wd),
+                     nullptr, static_cast<uint16_t*>(y), c.E, c.d, c.f, (int)rows, st);
   return hipGetLastError();
 }
 
