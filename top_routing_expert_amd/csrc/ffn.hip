@@ -7,24 +7,35 @@
 // what lets neighbouring tiles share weight lines in cache); [SyncTax] §2.2
 // (skewed expert load: hot experts must not stall the rest).
 //
-// gfx950 design (one kernel template, two instantiations)
-//  * Tile = 256 weight rows x 128 token rows x 64 k.  The weights are the MFMA
-//    A operand (M side) and the tokens the B operand (N side), so each lane's
-//    four accumulator values are four consecutive OUTPUT FEATURES of one token
-//    and the epilogue stores 8 contiguous bytes per lane.
-//    gate_up: the 256 weight rows are 128 rows of W_gate and the same 128 rows
-//    of W_up, so each wave holds matching gate/up accumulators and applies
-//    SiLU(g)*u in registers (no extra pass over h).  down: 256 rows of W_down.
-//  * 4 waves in a 2 (weights) x 2 (tokens) layout, 128 fp32 accumulators per
-//    lane; MFMA f32_16x16x32_bf16, 64 MFMAs per wave per k step.
-//  * Global -> register prefetch of the next k step while the current one is
-//    multiplied out of LDS; two LDS stages (96 KB), one barrier per k step.
-//    LDS rows are 128 B; 16-byte pieces are XOR-swizzled with (row & 7) so the
-//    fragment reads of 8 consecutive rows hit distinct banks.
+// gfx950 design
+//  * Weights are the MFMA A operand (M side), tokens the B operand (N side),
+//    so each lane's accumulator groups hold four consecutive OUTPUT FEATURES
+//    of one token and the epilogue stores 8 contiguous bytes per lane.
+//    gate_up: a tile's weight rows are rows n0.. of W_gate followed by the
+//    same rows of W_up, so every wave holds matching gate/up accumulators and
+//    applies SiLU(g)*u in registers (no extra pass over h).
+//  * MFMA f32_32x32x16_bf16 (a single wave per SIMD keeps this instruction at
+//    full rate; the 16x16x32 form needs two).  Four waves in a 2 (weights) x
+//    2 (tokens) layout.  Two tile shapes: 256 weight rows x 256 tokens (128 x
+//    128 per wave, 256 accumulators, one block per CU) for many rows per
+//    expert, and 256 x 128 (128 accumulators, two blocks per CU so one block's
+//    MFMAs overlap the other's memory phases) otherwise.
+//  * Operands reach LDS through the gfx950 LDS-DMA load
+//    (global_load_lds_dwordx4): no staging registers, 16 bytes per lane, each
+//    wave instruction fills eight full 128-byte lines.  32-wide k stages in a
+//    ring of 4 (or 3) buffers, several stages in flight, explicit vmcnt waits
+//    and one barrier per stage.  LDS rows are 64 bytes; 16-byte pieces are
+//    XOR-swizzled with (row >> 2) & 3, the pattern that measured fastest for
+//    the 32-row fragment reads.
+//  * The next stage's fragments are read from LDS while the current stage's
+//    MFMAs run (two register sets, 2x unrolled k loop), so LDS reads overlap
+//    matrix work instead of bunching after each barrier.
+//  * Token fragments past the expert's last row skip their LDS reads and
+//    MFMAs (the main loop is specialised on the live fragment count).
 //  * No host sync: the row table is read on the device.  Each block rebuilds
 //    the per-expert tile prefix sum from expert_offsets with one wave, finds
 //    its (expert, row tile) and exits if it has none; the grid is sized for
-//    the worst case  sum_e ceil(c_e/128) <= (rows + E*127)/128.  Skewed
+//    the worst case  sum_e ceil(c_e/TM) <= (rows + E*(TM-1))/TM.  Skewed
 //    experts therefore just own more tiles.
 //  * Rasterisation: tiles are ordered expert by expert; inside an expert in
 //    bands of up to 8 row tiles, and inside a band by weight tile with the row
@@ -75,7 +86,7 @@ constexpr int kStageK = 32;
 // in a 2 (weights) x 2 (tokens) layout; the block tile is 64 WA weight rows
 // by 64 WB token rows.
 template <bool GATED, int WA, int WB>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
+__global__ __launch_bounds__(256, (WB == 2 ? 2 : 1)) void grouped_gemm_bf16_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offs,
     const uint16_t* __restrict__ w0, const uint16_t* __restrict__ w1, uint16_t* __restrict__ out,
     int E, int N, int K, int rows, int n_tiles, int band) {
@@ -85,8 +96,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   constexpr int ROWS = TW + TM;                 // LDS rows per stage
   constexpr int CHUNKS = ROWS * 64 / 1024;      // 1 KB DMA chunks per stage
   constexpr int DPW = CHUNKS / 4;               // DMA instructions per wave per stage
+  constexpr int STAGES = WB == 2 ? 3 : kStages;  // LDS ring depth (two 128-token blocks per CU)
   static_assert(CHUNKS % 4 == 0, "stage must split evenly over 4 waves");
-  __shared__ u32x4 sbuf[kStages][ROWS * 4];
+  static_assert(STAGES * ROWS * 64 <= 150 * 1024, "LDS ring too large");
+  __shared__ u32x4 sbuf[STAGES][ROWS * 4];
   __shared__ int s_tile[4];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -161,6 +174,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   if (e < 0) return;  // block-uniform
   const int row0 = s_tile[1], row_end = s_tile[2], n_tile = s_tile[3];
   const int n0 = n_tile * TN;
+  const int nk = K / kStageK;
+  const size_t wstride = (size_t)N * K;
 
   // ---- DMA assignment.  Wave w copies chunks c = w + 4 i (i < DPW) of every
   // stage; chunk c holds LDS rows 16c..16c+15 (weight rows first).  Lane l
@@ -168,7 +183,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   // piece (l & 3) ^ ((row >> 2) & 3) = (l & 3) ^ ((l >> 4) & 3).
   const int lq = (lane & 3) ^ ((lane >> 4) & 3);
   const uint16_t* gsrc[DPW];
-  const size_t wstride = (size_t)N * K;
 #pragma unroll
   for (int i = 0; i < DPW; ++i) {
     const int r = 16 * (wave + 4 * i) + (lane >> 2);  // LDS row 0..ROWS-1
@@ -218,10 +232,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = K / kStageK;
   const uint32_t lds0 = lds_addr(&sbuf[0][0]);
   auto issue = [&](int kt) {
-    const uint32_t sbase = lds0 + (uint32_t)(kt % kStages) * (ROWS * 64u);
+    const uint32_t sbase = lds0 + (uint32_t)(kt % STAGES) * (ROWS * 64u);
 #pragma unroll
     for (int i = 0; i < DPW; ++i)
       dma16(gsrc[i] + (size_t)kt * kStageK, sbase + (uint32_t)(wave + 4 * i) * 1024u);
@@ -230,45 +243,77 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_kernel(
   // row (wave-uniform; the other fragments' reads and MFMAs are skipped).
   auto main_loop = [&](auto jn_c) {
     constexpr int JN = decltype(jn_c)::value;
-    auto load_frags = [&](const u32x4* sb, int slab, bf16x8 (&a)[WA], bf16x8 (&b)[WB]) {
-      const int q = 2 * slab + lk;
-#pragma unroll
-      for (int i = 0; i < WA; ++i) a[i] = as_bf16x8(sb[lds_piece(arow[i], q)]);
-#pragma unroll
-      for (int j = 0; j < JN; ++j) b[j] = as_bf16x8(sb[lds_piece(brow0 + 32 * j, q)]);
+    // fragments of one 32-wide stage: two 16-wide slabs
+    struct Frags {
+      bf16x8 a[2][WA];
+      bf16x8 b[2][WB];
     };
-    auto mfma_slab = [&](const bf16x8 (&a)[WA], const bf16x8 (&b)[WB]) {
+    auto load_frags = [&](int kt, Frags& F) {
+      const u32x4* sb = sbuf[kt % STAGES];
 #pragma unroll
-      for (int j = 0; j < JN; ++j)
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int q = 2 * s2 + lk;
 #pragma unroll
-        for (int i = 0; i < WA; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < WA; ++i) F.a[s2][i] = as_bf16x8(sb[lds_piece(arow[i], q)]);
+#pragma unroll
+        for (int j = 0; j < JN; ++j) F.b[s2][j] = as_bf16x8(sb[lds_piece(brow0 + 32 * j, q)]);
+      }
     };
-    // Pipeline.  Stage j (32-wide k-step j) goes to LDS buffer j % 4 and is
-    // issued three steps ahead.  At the top of step kt this wave waits for
-    // its own copies of stage kt (later stages may stay in flight); the
-    // barrier publishes every wave's copies and guarantees that nobody still
-    // reads buffer (kt + 3) % 4, which is refilled right after.
+    auto mfma_stage = [&](const Frags& F) {
 #pragma unroll
-    for (int i = 0; i < kStages - 1; ++i)
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int j = 0; j < JN; ++j)
+#pragma unroll
+          for (int i = 0; i < WA; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[s2][i], F.b[s2][j], acc[i][j],
+                                                                0, 0, 0);
+    };
+    // Pipeline.  Stage j (32-wide k-step j) goes to LDS buffer j % STAGES.
+    // Stage kt's fragments are read during step kt-1, while its MFMAs run, so
+    // LDS reads overlap the matrix work instead of bunching after a barrier.
+    // End of step kt: wait for this wave's copies of stage kt+2, barrier (all
+    // copies of kt+2 visible; nobody reads stages kt, kt+1 any more), then
+    // refill buffer kt % STAGES with stage kt + STAGES.
+    auto wait_for = [&](int j) {  // own copies of stage j complete; later ones may fly
+      const int later = min(nk - 1, j + STAGES - 3) - j;
+      switch (later) {  // vmcnt needs an immediate
+        case 0: wait_vm_barrier<0>(); break;
+        case 1: wait_vm_barrier<DPW>(); break;
+        case 2: wait_vm_barrier<2 * DPW>(); break;
+        case 3: wait_vm_barrier<3 * DPW>(); break;
+        default: wait_vm_barrier<4 * DPW>(); break;
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < STAGES; ++i)
       if (i < nk) issue(i);
-    for (int kt = 0; kt < nk; ++kt) {
-      const int ahead = min(nk - 1 - kt, kStages - 2);  // stages after kt already issued
-      if (ahead >= 2)
-        wait_vm_barrier<2 * DPW>();
-      else if (ahead == 1)
-        wait_vm_barrier<DPW>();
+    // stages 0 and 1 visible
+    {
+      const int later = min(nk - 1, STAGES - 1) - 1;  // issued after stage 1
+      if (later <= 0) wait_vm_barrier<0>();
+      else if (later == 1) wait_vm_barrier<DPW>();
+      else if (later == 2) wait_vm_barrier<2 * DPW>();
+      else wait_vm_barrier<3 * DPW>();
+    }
+    Frags F0, F1;
+    if (JN > 0) load_frags(0, F0);
+    auto step = [&](int kt, Frags& cur, Frags& nxt) {
+      if (JN > 0) {
+        // the last step re-reads the final stage (valid, no longer refilled)
+        load_frags(min(kt + 1, nk - 1), nxt);
+        mfma_stage(cur);
+      }
+      if (kt + 2 < nk)
+        wait_for(kt + 2);
       else
         wait_vm_barrier<0>();
-      if (kt + kStages - 1 < nk) issue(kt + kStages - 1);
-      if (JN > 0) {
-        const u32x4* sb = sbuf[kt % kStages];
-        bf16x8 fa0[WA], fb0[WB], fa1[WA], fb1[WB];
-        load_frags(sb, 0, fa0, fb0);
-        load_frags(sb, 1, fa1, fb1);
-        mfma_slab(fa0, fb0);
-        mfma_slab(fa1, fb1);
-      }
+      if (kt + STAGES < nk) issue(kt + STAGES);
+    };
+    // nk is even (K is a multiple of 64), so the two-step body needs no guard
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(kt, F0, F1);
+      step(kt + 1, F1, F0);
     }
   };
   switch (jn) {
@@ -372,7 +417,7 @@ __global__ void ffn_down_f32_kernel(const float* __restrict__ h, const int32_t* 
 // per flop; they are used unless they would leave fewer than ~2 blocks per CU,
 // in which case 256 weight rows x 128 tokens keep the grid full.
 struct GemmPlan {
-  int wb;       // token fragments per wave (4: 256-token tiles, 2: 128)
+  int wb;       // token fragments per wave (4: 256-token tiles, 2: 128-token tiles)
   int n_tiles;  // weight tiles over N
   int blocks;   // grid size (multiple of 8, worst case over any row table)
 };
@@ -384,7 +429,9 @@ static GemmPlan plan_gemm(long rows, int E, int N, bool gated) {
   const int cus = 256;
   const long avg = (rows + E - 1) / E;  // typical rows per expert
   const long est256 = (long)p.n_tiles * E * ((avg + 255) / 256);
-  p.wb = est256 >= 2 * cus ? 4 : 2;
+  // many rows per expert: MFMA-bound, big tiles; otherwise weight streaming
+  p.wb = (avg >= 512 && est256 >= 2 * cus) ? 4 : 2;
+  (void)cus;
   const int tm = 64 * p.wb;
   long m_slots = (rows + (long)E * (tm - 1)) / tm;  // upper bound of sum_e ceil(c_e / tm)
   if (m_slots < 1) m_slots = 1;
@@ -399,11 +446,11 @@ static void launch_gemm(const GemmPlan& p, const uint16_t* act, const int32_t* o
                         int rows, hipStream_t st) {
   const int band = 8;
   if (p.wb == 4)
-    grouped_gemm_bf16_kernel<GATED, 4, 4><<<p.blocks, 256, 0, st>>>(act, offs, w0, w1, out, E, N,
-                                                                    K, rows, p.n_tiles, band);
+    grouped_gemm_bf16_kernel<GATED, 4, 4><<<p.blocks, 256, 0, st>>>(
+        act, offs, w0, w1, out, E, N, K, rows, p.n_tiles, band);
   else
-    grouped_gemm_bf16_kernel<GATED, 4, 2><<<p.blocks, 256, 0, st>>>(act, offs, w0, w1, out, E, N,
-                                                                    K, rows, p.n_tiles, band);
+    grouped_gemm_bf16_kernel<GATED, 4, 2><<<p.blocks, 256, 0, st>>>(
+        act, offs, w0, w1, out, E, N, K, rows, p.n_tiles, band);
 }
 
 hipError_t launch_ffn_gate_up(const moe_config& c, const void* x_perm, const int32_t* offs,
