@@ -28,8 +28,16 @@ PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PHASES = ("route", "permute", "ffn_gate_up", "ffn_down", "combine")
 DOMINANT = "ffn_gate_up"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_gate_up_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "top_routing_expert_amd", "csrc", "ffn.hip")
+CSRC = os.path.join(ROOT, "top_routing_expert_amd", "csrc")
+# per FFN weight layout: (counter summary, kernel source it was taken on, kernel name)
+FFN_KERNELS = {
+    "rowmajor": (os.path.join(ROOT, "profiles", "ffn_gate_up_traffic.json"),
+                 os.path.join(CSRC, "ffn.hip"),
+                 "grouped_gemm_bf16_kernel<gated> (moe_ffn_gate_up)"),
+    "packed": (os.path.join(ROOT, "profiles", "ffn_gate_up_packed_traffic.json"),
+               os.path.join(CSRC, "ffn_packed.hip"),
+               "grouped_gemm_packed_kernel<gated> (moe_ffn_gate_up_packed)"),
+}
 
 
 def log(msg):
@@ -46,6 +54,9 @@ def parse():
                     help="workload index 1..5 or name; default 2 (T1024-d4096-E8-top2-f11008)")
     ap.add_argument("--cpu-tokens", type=int, default=256,
                     help="tokens of the workload the CPU oracle baseline runs (0 = skip)")
+    ap.add_argument("--ffn", choices=sorted(FFN_KERNELS), default="packed",
+                    help="expert-weight layout of the grouped FFN: packed once at load time "
+                         "(moe_pack_weights) or the plain [E,f,d] / [E,d,f] arrays")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     a = ap.parse_args()
@@ -85,17 +96,19 @@ def roofline_of(work, ms):
                 frac=tfl / PEAK_BF16_TFLOPS, gbs=gbs, hbm_frac=gbs / PEAK_HBM_GBS, ai=ai)
 
 
-def measured_traffic(launch_bytes):
+def measured_traffic(ffn, workload):
     """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None if there is none or the kernel source changed since."""
+    summary, or None if there is none, it is for another workload, or the
+    kernel source changed since."""
+    traffic_file, kernel_src, _ = FFN_KERNELS[ffn]
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(traffic_file) as fh:
             t = json.load(fh)
-        with open(KERNEL_SRC, "rb") as fh:
+        with open(kernel_src, "rb") as fh:
             h = hashlib.sha256(fh.read()).hexdigest()
     except (OSError, ValueError):
         return None
-    if t.get("kernel_src_sha256") != h or t.get("workload") is None:
+    if t.get("kernel_src_sha256") != h or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
 
@@ -146,6 +159,8 @@ def main():
         copy_calibration()
         return
     shape = a.shape
+    if shape.dtype != "bf16":
+        a.ffn = "rowmajor"  # packed images are bf16 only
     log(f"workload {shape.name}: generating inputs")
     from top_routing_expert_amd import configs as C
     inp = I.make_inputs(shape, seed=C.CONFIGS.index(shape) + 1)
@@ -169,16 +184,32 @@ def main():
     )
     ws_r, ws_p = B.workspace(cfg, "route"), B.workspace(cfg, "permute")
     stream = torch.cuda.current_stream()
+    if a.ffn == "packed":
+        # load-time weight layout: packed once, the plain arrays are then dropped
+        log("packing expert weights")
+        pgu, pd = B.pack_weights(cfg, dev["w_gate"], dev["w_up"], dev["w_down"], stream=stream)
+        torch.cuda.synchronize()
+        dev["w_gate"] = dev["w_up"] = dev["w_down"] = None
+        ffn_calls = {
+            "ffn_gate_up": lambda: B.moe_ffn_gate_up_packed(cfg, buf["xp"], buf["offs"], pgu,
+                                                            buf["h"], stream),
+            "ffn_down": lambda: B.moe_ffn_down_packed(cfg, buf["h"], buf["offs"], pd, buf["y"],
+                                                      stream),
+        }
+    else:
+        ffn_calls = {
+            "ffn_gate_up": lambda: B.moe_ffn_gate_up(cfg, buf["xp"], buf["offs"], dev["w_gate"],
+                                                     dev["w_up"], buf["h"], stream),
+            "ffn_down": lambda: B.moe_ffn_down(cfg, buf["h"], buf["offs"], dev["w_down"],
+                                               buf["y"], stream),
+        }
 
     calls = {
         "route": lambda: B.moe_route(cfg, dev["x"], dev["w_router"], dev["bias"], buf["logits"],
                                      buf["idx"], buf["w"], ws_r, stream),
         "permute": lambda: B.moe_permute(cfg, dev["x"], buf["idx"], buf["offs"], buf["roffs"],
                                          buf["slot"], buf["src"], buf["xp"], ws_p, stream),
-        "ffn_gate_up": lambda: B.moe_ffn_gate_up(cfg, buf["xp"], buf["offs"], dev["w_gate"],
-                                                 dev["w_up"], buf["h"], stream),
-        "ffn_down": lambda: B.moe_ffn_down(cfg, buf["h"], buf["offs"], dev["w_down"], buf["y"],
-                                           stream),
+        **ffn_calls,
         "combine": lambda: B.moe_combine(cfg, buf["y"], buf["slot"], buf["w"], buf["out"], stream),
     }
 
@@ -210,10 +241,10 @@ def main():
     work = algorithmic(shape, counts)
     phases = {p: dict(ms=phase_ms[p], **roofline_of(work[p], phase_ms[p])) for p in PHASES}
     dom = phases[DOMINANT]
-    traffic = measured_traffic(work[DOMINANT]["bytes"])
+    traffic = measured_traffic(a.ffn, shape.name)
     roofline = {"bound": dom["bound"], "achieved": round(dom["achieved"], 3),
                 "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4),
-                "traffic": traffic, "kernel": "grouped_gemm_bf16_kernel<gated> (moe_ffn_gate_up)",
+                "traffic": traffic, "kernel": FFN_KERNELS[a.ffn][2],
                 "algorithmic_bytes": work[DOMINANT]["bytes"],
                 "algorithmic_flops": work[DOMINANT]["flops"],
                 "avg_launch_ms": round(dom["ms"], 5)}
@@ -237,7 +268,7 @@ def main():
         "config": {"workload": shape.name, "T": T, "d": d, "E": E, "k": k, "f": f,
                    "n_group": shape.n_group, "topk_group": shape.topk_group,
                    "presel": shape.presel, "renorm": shape.renorm, "ep_ranks": R,
-                   "parallelism": "single GPU"},
+                   "ffn_weights": a.ffn, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "phases": {p: {kk: (round(v, 5) if isinstance(v, float) else v) for kk, v in ph.items()}

@@ -241,6 +241,48 @@ int moe_layer_fwd(const moe_config* cfg, const void* x, const void* w_router, co
                   const void* w_gate, const void* w_up, const void* w_down, void* out,
                   const moe_layer_bufs* bufs, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Packed expert weights (MOE_BF16 only).
+ *
+ * The expert weights are static across forward passes, so they can be laid
+ * out once, at load time, in the order the grouped-GEMM kernels consume them:
+ * each expert's image is a sequence of 1 KB blocks, one per wave load, in the
+ * matrix cores' operand order, zero padded to whole tiles.  The packed FFN
+ * computes exactly what moe_ffn_gate_up / moe_ffn_down compute ([V4-overlap]
+ * Waved-EP section, expert compute = L1 + Act + L2), with the weights read
+ * straight from HBM into registers instead of through LDS.  Each expert's
+ * image is contiguous and in expert-ID order ([EP-V4] §5.2), so one rank's
+ * share is still a plain offset: expert e0's image starts at byte
+ * e0 * (gate_up_bytes / E) (resp. down_bytes / E).
+ *
+ * moe_packed_weight_bytes: bytes of the two packed images for cfg (T, k and
+ *   the routing fields are ignored).  Fails with MOE_EUNSUPPORTED unless
+ *   dtype is MOE_BF16.
+ * moe_pack_weights: writes packed_gate_up from w_gate and w_up ([E, f, d]),
+ *   and/or packed_down from w_down ([E, d, f]); either output may be NULL (its
+ *   inputs are then ignored).  All pointers 16-byte aligned.  Enqueue-only,
+ *   like every other call.
+ */
+int moe_packed_weight_bytes(const moe_config* cfg, size_t* gate_up_bytes, size_t* down_bytes);
+int moe_pack_weights(const moe_config* cfg, const void* w_gate, const void* w_up,
+                     const void* w_down, void* packed_gate_up, void* packed_down, void* stream);
+
+/*
+ * moe_ffn_gate_up / moe_ffn_down / moe_layer_fwd on packed weights: same
+ * arguments, same outputs (h, y_perm, out within the same float32
+ * accumulation; the sums run over k in the same order), same row-table and
+ * sub-table rules.  x_perm, h and y_perm must be 16-byte aligned.
+ */
+int moe_ffn_gate_up_packed(const moe_config* cfg, const void* x_perm,
+                           const int32_t* expert_offsets, const void* packed_gate_up, void* h,
+                           void* stream);
+int moe_ffn_down_packed(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
+                        const void* packed_down, void* y_perm, void* stream);
+int moe_layer_fwd_packed(const moe_config* cfg, const void* x, const void* w_router,
+                         const float* bias, const void* packed_gate_up, const void* packed_down,
+                         void* out, const moe_layer_bufs* bufs, void* ws, size_t ws_bytes,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

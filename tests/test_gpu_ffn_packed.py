@@ -1,0 +1,155 @@
+"""Grouped SwiGLU FFN on packed expert weights: parity against the oracle on
+the same bf16 inputs, on row tables that reach every number of live 32-row
+token fragments of a tile (1..8), ragged tails, empty experts, K that is not a
+multiple of the 128-wide k iteration, one rank's sub-table, and the whole
+layer through moe_layer_fwd_packed."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _gpu import TOL_LAYER, alloc, host, log, rel_err, upload
+from test_gpu_ffn import _check, _weights
+from top_routing_expert_amd import binding as B
+from top_routing_expert_amd import configs as C
+from top_routing_expert_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_packed(shape, x_perm, offs, wg, wu, wd):
+    cfg = B.config(shape)
+    A = x_perm.shape[0]
+    pgu, pd = B.pack_weights(cfg, wg, wu, wd)
+    h = torch.empty((A, shape.f), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((A, shape.d), dtype=torch.bfloat16, device="cuda")
+    B.moe_ffn_gate_up_packed(cfg, x_perm, offs, pgu, h)
+    B.moe_ffn_down_packed(cfg, h, offs, pd, y)
+    torch.cuda.synchronize()
+    return h, y
+
+
+CASES = [
+    # (E, d, f, counts)
+    (8, 256, 448, [1, 33, 65, 97, 129, 161, 193, 225]),      # jn = 1..8
+    (8, 320, 192, [129, 127, 1, 0, 300, 128, 256, 2]),      # K % 128 == 64 both ways
+    (4, 128, 384, [256, 257, 512, 600]),                     # full tiles + tails
+    (16, 128, 128, [0] * 7 + [517] + [0] * 8),               # one hot expert
+    (4, 64, 64, [0, 0, 0, 1]),                               # one row
+    (64, 128, 192, None),                                    # many small experts
+    (8, 1024, 256, [40, 300, 0, 77, 256, 31, 5, 190]),      # long k loop (8 iterations)
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"E{c[0]}-d{c[1]}-f{c[2]}" for c in CASES])
+def test_packed_ffn_matches_oracle(case):
+    E, d, f, counts = case
+    log(f"[ffn-packed] {case[:3]}")
+    rng = np.random.default_rng(E * d + f + 1)
+    counts = rng.integers(0, 300, size=E) if counts is None else np.array(counts)
+    A = int(counts.sum())
+    shape = C.E8_D4096.replace(name="ffn-packed", T=A, k=1, E=E, d=d, f=f, ep_ranks=1)
+    offs_np = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    xp_np = I.make_x(shape, seed=21)
+    wg, wu, wd = _weights(shape, 22)
+    dev = [B.to_device(a) for a in (xp_np, wg, wu, wd)]
+    offs = torch.from_numpy(offs_np).cuda()
+    h, y = _run_packed(shape, dev[0], offs, *dev[1:])
+    _check(shape, xp_np, offs_np, wg, wu, wd, h, y)
+
+
+def test_packed_matches_row_major_path():
+    """Same sums in the same k order: the packed and row-major paths agree to
+    within one bf16 rounding of h (identical in almost every element)."""
+    log("[ffn-packed] vs row-major path")
+    E, d, f = 8, 512, 320
+    rng = np.random.default_rng(31)
+    counts = rng.integers(0, 400, size=E)
+    A = int(counts.sum())
+    shape = C.E8_D4096.replace(name="ffn-packed-rm", T=A, k=1, E=E, d=d, f=f, ep_ranks=1)
+    offs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+    xp = B.to_device(I.make_x(shape, seed=32))
+    w = [B.to_device(a) for a in _weights(shape, 33)]
+    h1, y1 = _run_packed(shape, xp, offs, *w)
+    cfg = B.config(shape)
+    h2 = torch.empty_like(h1)
+    y2 = torch.empty_like(y1)
+    B.moe_grouped_ffn(cfg, xp, offs, *w, h2, y2)
+    torch.cuda.synchronize()
+    hd = (h1.float() - h2.float()).abs()
+    assert float(hd.max()) <= float(h2.float().abs().max()) * 2 ** -7
+    assert float((hd > 0).float().mean()) < 0.01
+
+
+def test_packed_subtable_runs_only_that_share():
+    log("[ffn-packed] one rank's sub-table")
+    E, R, d, f = 16, 4, 128, 192
+    rng = np.random.default_rng(41)
+    counts = rng.integers(1, 300, size=E)
+    A = int(counts.sum())
+    shape = C.E8_D4096.replace(name="ffn-packed-sub", T=A, k=1, E=E, d=d, f=f, ep_ranks=R)
+    offs_np = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    xp_np = I.make_x(shape, seed=42)
+    wg, wu, wd = _weights(shape, 43)
+    xp, dg, du, dd = (B.to_device(a) for a in (xp_np, wg, wu, wd))
+    offs = torch.from_numpy(offs_np).cuda()
+    cfg = B.config(shape)
+    pgu, pd = B.pack_weights(cfg, dg, du, dd)
+    gu_bytes, d_bytes = B.packed_weight_bytes(cfg)
+    per = E // R
+    r = 1
+    e0 = r * per
+    sub = B.config(shape, E=per)
+    hs = torch.full((A, f), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    ys = torch.full((A, d), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    pgu_r = pgu[e0 * (gu_bytes // E):]
+    pd_r = pd[e0 * (d_bytes // E):]
+    B.moe_ffn_gate_up_packed(sub, xp, offs[e0:], pgu_r, hs)
+    B.moe_ffn_down_packed(sub, hs, offs[e0:], pd_r, ys)
+    torch.cuda.synchronize()
+    r0, r1 = int(offs_np[e0]), int(offs_np[e0 + per])
+    y_np, h_np = host(ys), host(hs)
+    assert np.all(y_np[:r0] == 7) and np.all(y_np[r1:] == 7)
+    assert np.all(h_np[:r0] == 7) and np.all(h_np[r1:] == 7)
+    _check(shape, xp_np, offs_np, wg, wu, wd, hs, ys, rows=np.arange(r0, r1))
+
+
+def test_packed_deterministic():
+    log("[ffn-packed] determinism")
+    E, d, f = 8, 256, 320
+    rng = np.random.default_rng(51)
+    counts = rng.integers(50, 300, size=E)
+    A = int(counts.sum())
+    shape = C.E8_D4096.replace(name="ffn-packed-det", T=A, k=1, E=E, d=d, f=f, ep_ranks=1)
+    offs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+    xp = B.to_device(I.make_x(shape, seed=52))
+    w = [B.to_device(a) for a in _weights(shape, 53)]
+    h1, y1 = _run_packed(shape, xp, offs, *w)
+    h2, y2 = _run_packed(shape, xp, offs, *w)
+    assert torch.equal(h1.view(torch.int16), h2.view(torch.int16))
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["e8", "e64", "e16", "e256"])
+def test_packed_layer_matches_oracle(name):
+    """moe_layer_fwd_packed on the reduced workloads, against the oracle run on
+    the GPU's own fp32 logits (so no routing flip can occur)."""
+    shape = C.SMALL[name]
+    log(f"[layer-packed] {shape.name}")
+    inp = I.make_inputs(shape, seed=61)
+    dev = upload(inp)
+    buf = alloc(shape)
+    cfg = B.config(shape)
+    pgu, pd = B.pack_weights(cfg, dev["w_gate"], dev["w_up"], dev["w_down"])
+    bufs = {k: buf[k] for k in ("logits", "topk_idx", "topk_w", "expert_offsets")}
+    B.moe_layer_fwd_packed(cfg, dev["x"], dev["w_router"], dev["bias"], pgu, pd, buf["out"], bufs,
+                           B.workspace(cfg, "layer"))
+    torch.cuda.synchronize()
+    ref = oracle.layer(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
+                       inp["w_down"], k=shape.k, n_group=shape.n_group,
+                       topk_group=shape.topk_group, presel=shape.presel, renorm=shape.renorm,
+                       ep_ranks=shape.ep_ranks, logits32=host(buf["logits"]))
+    assert np.array_equal(host(buf["topk_idx"]), ref["topk_idx"])
+    assert np.array_equal(host(buf["expert_offsets"]), ref["offsets"])
+    err = rel_err(host(buf["out"]), ref["out"])
+    assert err <= TOL_LAYER["bf16"], err

@@ -27,7 +27,9 @@ LAYER_BUF_FIELDS = ("logits", "topk_idx", "topk_w", "expert_offsets", "rank_offs
 
 # every function include/moe.h declares
 EXPORTS = ("moe_strerror", "moe_validate", "moe_workspace_bytes", "moe_route", "moe_permute",
-           "moe_ffn_gate_up", "moe_ffn_down", "moe_grouped_ffn", "moe_combine", "moe_layer_fwd")
+           "moe_ffn_gate_up", "moe_ffn_down", "moe_grouped_ffn", "moe_combine", "moe_layer_fwd",
+           "moe_packed_weight_bytes", "moe_pack_weights", "moe_ffn_gate_up_packed",
+           "moe_ffn_down_packed", "moe_layer_fwd_packed")
 
 
 class MoEConfig(ctypes.Structure):
@@ -68,10 +70,14 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [cfgp, vp, vp, vp, vp, vp]
         L.moe_layer_fwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.POINTER(MoELayerBufs), vp, sz, vp]
+        L.moe_packed_weight_bytes.argtypes = [cfgp, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        L.moe_pack_weights.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
+        L.moe_ffn_gate_up_packed.argtypes = [cfgp, vp, vp, vp, vp, vp]
+        L.moe_ffn_down_packed.argtypes = [cfgp, vp, vp, vp, vp, vp]
+        L.moe_layer_fwd_packed.argtypes = [cfgp, vp, vp, vp, vp, vp, vp,
+                                           ctypes.POINTER(MoELayerBufs), vp, sz, vp]
         for name in EXPORTS[1:]:
-            if name != "moe_workspace_bytes":
-                getattr(L, name).restype = i32
-        L.moe_workspace_bytes.restype = i32
+            getattr(L, name).restype = i32
         _lib = L
     return _lib
 
@@ -189,6 +195,53 @@ def moe_layer_fwd(cfg, x, w_router, bias, w_gate, w_up, w_down, out, bufs: dict 
                                                 _ptr(bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                                                 _ptr(out), ctypes.byref(b) if b else None, wp, wn,
                                                 _stream(stream)))
+
+
+def packed_weight_bytes(cfg) -> tuple[int, int]:
+    gu, dn = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("moe_packed_weight_bytes", lib().moe_packed_weight_bytes(ctypes.byref(cfg),
+                                                                    ctypes.byref(gu),
+                                                                    ctypes.byref(dn)))
+    return gu.value, dn.value
+
+
+def moe_pack_weights(cfg, w_gate, w_up, w_down, packed_gate_up, packed_down, stream=None):
+    _check("moe_pack_weights", lib().moe_pack_weights(ctypes.byref(cfg), _ptr(w_gate), _ptr(w_up),
+                                                      _ptr(w_down), _ptr(packed_gate_up),
+                                                      _ptr(packed_down), _stream(stream)))
+
+
+def pack_weights(cfg, w_gate, w_up, w_down, device="cuda", stream=None):
+    """Allocates the two packed images (uint8 device tensors) and fills them."""
+    gu, dn = packed_weight_bytes(cfg)
+    pgu = torch.empty(gu, dtype=torch.uint8, device=device)
+    pd = torch.empty(dn, dtype=torch.uint8, device=device)
+    moe_pack_weights(cfg, w_gate, w_up, w_down, pgu, pd, stream)
+    return pgu, pd
+
+
+def moe_ffn_gate_up_packed(cfg, x_perm, expert_offsets, packed_gate_up, h, stream=None):
+    _check("moe_ffn_gate_up_packed",
+           lib().moe_ffn_gate_up_packed(ctypes.byref(cfg), _ptr(x_perm), _ptr(expert_offsets),
+                                        _ptr(packed_gate_up), _ptr(h), _stream(stream)))
+
+
+def moe_ffn_down_packed(cfg, h, expert_offsets, packed_down, y_perm, stream=None):
+    _check("moe_ffn_down_packed",
+           lib().moe_ffn_down_packed(ctypes.byref(cfg), _ptr(h), _ptr(expert_offsets),
+                                     _ptr(packed_down), _ptr(y_perm), _stream(stream)))
+
+
+def moe_layer_fwd_packed(cfg, x, w_router, bias, packed_gate_up, packed_down, out,
+                         bufs: dict | None = None, ws=None, stream=None):
+    b = None
+    if bufs:
+        b = MoELayerBufs(**{n: _ptr(bufs.get(n)) for n in LAYER_BUF_FIELDS})
+    wp, wn = _ws(ws)
+    _check("moe_layer_fwd_packed",
+           lib().moe_layer_fwd_packed(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(bias),
+                                      _ptr(packed_gate_up), _ptr(packed_down), _ptr(out),
+                                      ctypes.byref(b) if b else None, wp, wn, _stream(stream)))
 
 
 # ------------------------------------------------------------ device tensors

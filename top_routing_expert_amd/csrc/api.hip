@@ -134,10 +134,68 @@ int do_ffn(const moe_config& c, const void* xperm, const int32_t* offs, const vo
   return MOE_OK;
 }
 
+int do_ffn_packed(const moe_config& c, const void* xperm, const int32_t* offs, const void* pgu,
+                  const void* pd, void* h, void* y, hipStream_t st) {
+  if (c.T == 0) return MOE_OK;
+  if (pgu) {
+    hipError_t e = launch_ffn_gate_up_packed(c, xperm, offs, pgu, h, st);
+    if (e != hipSuccess) return MOE_EHIP;
+  }
+  if (pd) return status_of(launch_ffn_down_packed(c, h, offs, pd, y, st));
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+// Packed-weight entry points: bf16 only, 16-byte aligned operands.
+int check_packed(const moe_config* c) {
+  int s = check_core(c);
+  if (s != MOE_OK) return s;
+  if (c->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t packed_bytes(const moe_config& c, bool gate_up) {
+  const PackGeom g = gate_up ? pack_geom(c.f, c.d, true) : pack_geom(c.d, c.f, false);
+  return (size_t)c.E * g.expert_elems * 2;
+}
+
 int do_combine(const moe_config& c, const void* y, const int32_t* slot, const float* w, void* out,
                hipStream_t st) {
   if (c.T == 0) return MOE_OK;
   return status_of(launch_combine(c, y, slot, w, out, st));
+}
+
+// moe_layer_fwd body shared by the row-major and packed-weight variants;
+// `ffn(x_perm, offs, h, y, stream)` runs the grouped FFN.  Routing checks and
+// the FFN's own argument checks have passed.
+template <typename Ffn>
+int run_layer(const moe_config& c, const void* x, const void* w_router, const float* bias,
+              void* out, const moe_layer_bufs* bufs, void* ws, size_t ws_bytes, void* stream,
+              Ffn&& ffn) {
+  const LayerLayout L = layer_layout(c, bufs);
+  int s;
+  if ((s = check_ws(L.total, ws, ws_bytes)) != MOE_OK) return s;
+  char* base = static_cast<char*>(ws);
+  auto pick = [&](void* given, size_t at) -> void* { return given ? given : base + at; };
+  const moe_layer_bufs none{};
+  const moe_layer_bufs& b = bufs ? *bufs : none;
+  void* scratch = base + L.scratch;
+  float* logits = static_cast<float*>(pick(b.logits, L.logits));
+  int32_t* idx = static_cast<int32_t*>(pick(b.topk_idx, L.idx));
+  float* w = static_cast<float*>(pick(b.topk_w, L.w));
+  int32_t* offs = static_cast<int32_t*>(pick(b.expert_offsets, L.offs));
+  int32_t* roffs = static_cast<int32_t*>(pick(b.rank_offsets, L.roffs));
+  int32_t* slot = static_cast<int32_t*>(pick(b.slot_of, L.slot));
+  int32_t* src = static_cast<int32_t*>(pick(b.src_of, L.src));
+  void* xperm = pick(b.x_perm, L.xperm);
+  void* h = pick(b.h, L.h);
+  void* y = pick(b.y_perm, L.y);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = do_route(c, x, w_router, bias, logits, idx, w, scratch, st)) != MOE_OK) return s;
+  if ((s = do_permute(c, x, idx, offs, roffs, slot, src, xperm, scratch, st)) != MOE_OK) return s;
+  if ((s = ffn(xperm, offs, h, y, st)) != MOE_OK) return s;
+  return do_combine(c, y, slot, w, out, st);
 }
 
 }  // namespace
@@ -255,32 +313,75 @@ int moe_layer_fwd(const moe_config* cfg, const void* x, const void* w_router, co
                   const moe_layer_bufs* bufs, void* ws, size_t ws_bytes, void* stream) {
   int s = check_routing(cfg);
   if (s != MOE_OK) return s;
-  const moe_config& c = *cfg;
-  const LayerLayout L = layer_layout(c, bufs);
-  if (c.T > 0) {
-    if (!x || !w_router || !w_gate || !w_up || !w_down || !out) return MOE_EINVAL;
-  }
-  if ((s = check_ws(L.total, ws, ws_bytes)) != MOE_OK) return s;
-  char* base = static_cast<char*>(ws);
-  auto pick = [&](void* given, size_t at) -> void* { return given ? given : base + at; };
-  const moe_layer_bufs none{};
-  const moe_layer_bufs& b = bufs ? *bufs : none;
-  void* scratch = base + L.scratch;
-  float* logits = static_cast<float*>(pick(b.logits, L.logits));
-  int32_t* idx = static_cast<int32_t*>(pick(b.topk_idx, L.idx));
-  float* w = static_cast<float*>(pick(b.topk_w, L.w));
-  int32_t* offs = static_cast<int32_t*>(pick(b.expert_offsets, L.offs));
-  int32_t* roffs = static_cast<int32_t*>(pick(b.rank_offsets, L.roffs));
-  int32_t* slot = static_cast<int32_t*>(pick(b.slot_of, L.slot));
-  int32_t* src = static_cast<int32_t*>(pick(b.src_of, L.src));
-  void* xperm = pick(b.x_perm, L.xperm);
-  void* h = pick(b.h, L.h);
-  void* y = pick(b.y_perm, L.y);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((s = do_route(c, x, w_router, bias, logits, idx, w, scratch, st)) != MOE_OK) return s;
-  if ((s = do_permute(c, x, idx, offs, roffs, slot, src, xperm, scratch, st)) != MOE_OK) return s;
-  if ((s = do_ffn(c, xperm, offs, w_gate, w_up, w_down, h, y, st)) != MOE_OK) return s;
-  return do_combine(c, y, slot, w, out, st);
+  if (cfg->T > 0 && (!x || !w_router || !w_gate || !w_up || !w_down || !out)) return MOE_EINVAL;
+  return run_layer(*cfg, x, w_router, bias, out, bufs, ws, ws_bytes, stream,
+                   [&](const void* xp, const int32_t* offs, void* h, void* y, hipStream_t st) {
+                     return do_ffn(*cfg, xp, offs, w_gate, w_up, w_down, h, y, st);
+                   });
+}
+
+int moe_packed_weight_bytes(const moe_config* cfg, size_t* gate_up_bytes, size_t* down_bytes) {
+  int s = check_packed(cfg);
+  if (s != MOE_OK) return s;
+  if (!gate_up_bytes || !down_bytes) return MOE_EINVAL;
+  *gate_up_bytes = packed_bytes(*cfg, true);
+  *down_bytes = packed_bytes(*cfg, false);
+  return MOE_OK;
+}
+
+int moe_pack_weights(const moe_config* cfg, const void* w_gate, const void* w_up,
+                     const void* w_down, void* packed_gate_up, void* packed_down, void* stream) {
+  int s = check_packed(cfg);
+  if (s != MOE_OK) return s;
+  if (!packed_gate_up && !packed_down) return MOE_EINVAL;
+  if (packed_gate_up && (!w_gate || !w_up || !aligned16(w_gate) || !aligned16(w_up) ||
+                         !aligned16(packed_gate_up)))
+    return MOE_EINVAL;
+  if (packed_down && (!w_down || !aligned16(w_down) || !aligned16(packed_down))) return MOE_EINVAL;
+  return status_of(launch_pack_weights(*cfg, w_gate, w_up, w_down, packed_gate_up, packed_down,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int moe_ffn_gate_up_packed(const moe_config* cfg, const void* x_perm,
+                           const int32_t* expert_offsets, const void* packed_gate_up, void* h,
+                           void* stream) {
+  int s = check_packed(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->T > 0 && (!x_perm || !expert_offsets || !packed_gate_up || !h || !aligned16(x_perm) ||
+                     !aligned16(packed_gate_up) || !aligned16(h)))
+    return MOE_EINVAL;
+  return do_ffn_packed(*cfg, x_perm, expert_offsets, packed_gate_up, nullptr, h, nullptr,
+                       static_cast<hipStream_t>(stream));
+}
+
+int moe_ffn_down_packed(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
+                        const void* packed_down, void* y_perm, void* stream) {
+  int s = check_packed(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->T > 0 && (!h || !expert_offsets || !packed_down || !y_perm || !aligned16(h) ||
+                     !aligned16(packed_down) || !aligned16(y_perm)))
+    return MOE_EINVAL;
+  return do_ffn_packed(*cfg, nullptr, expert_offsets, nullptr, packed_down, const_cast<void*>(h),
+                       y_perm, static_cast<hipStream_t>(stream));
+}
+
+int moe_layer_fwd_packed(const moe_config* cfg, const void* x, const void* w_router,
+                         const float* bias, const void* packed_gate_up, const void* packed_down,
+                         void* out, const moe_layer_bufs* bufs, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int s = check_routing(cfg);
+  if (s != MOE_OK) return s;
+  if ((s = check_packed(cfg)) != MOE_OK) return s;
+  if (cfg->T > 0 && (!x || !w_router || !packed_gate_up || !packed_down || !out ||
+                     !aligned16(packed_gate_up) || !aligned16(packed_down)))
+    return MOE_EINVAL;
+  if (bufs && ((bufs->x_perm && !aligned16(bufs->x_perm)) || (bufs->h && !aligned16(bufs->h)) ||
+               (bufs->y_perm && !aligned16(bufs->y_perm))))
+    return MOE_EINVAL;
+  return run_layer(*cfg, x, w_router, bias, out, bufs, ws, ws_bytes, stream,
+                   [&](const void* xp, const int32_t* offs, void* h, void* y, hipStream_t st) {
+                     return do_ffn_packed(*cfg, xp, offs, packed_gate_up, packed_down, h, y, st);
+                   });
 }
 
 }  // extern "C"

@@ -1,5 +1,5 @@
 // Shared device helpers and the internal launch interface of libmoe_mi355x.
-// gfx950 (CDNA4) only: wave64, MFMA bf16 16x16x32, 160 KB LDS per CU.
+// gfx950 (CDNA4) only: wave64, MFMA bf16 32x32x16, 160 KB LDS per CU.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -63,6 +63,21 @@ hipError_t launch_ffn_gate_up(const moe_config& c, const void* x_perm, const int
                               const void* wg, const void* wu, void* h, hipStream_t st);
 hipError_t launch_ffn_down(const moe_config& c, const void* h, const int32_t* offs, const void* wd,
                            void* y, hipStream_t st);
+
+// Packed expert weights (MFMA fragment order, zero padded; see ffn_packed.hip).
+struct PackGeom {
+  int slab_features;    // output features per slab (128 gated, 256 plain)
+  int slabs;            // slabs per expert
+  int kp;               // K rounded up to the 128-wide k iteration
+  size_t expert_elems;  // bf16 elements per expert
+};
+PackGeom pack_geom(int features, int K, bool gated);
+hipError_t launch_pack_weights(const moe_config& c, const void* wg, const void* wu, const void* wd,
+                               void* packed_gate_up, void* packed_down, hipStream_t st);
+hipError_t launch_ffn_gate_up_packed(const moe_config& c, const void* x_perm, const int32_t* offs,
+                                     const void* packed_gate_up, void* h, hipStream_t st);
+hipError_t launch_ffn_down_packed(const moe_config& c, const void* h, const int32_t* offs,
+                                  const void* packed_down, void* y, hipStream_t st);
 
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_of,
                           const float* topk_w, void* out, hipStream_t st);

@@ -48,6 +48,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "tiles.h"
 
 namespace moe {
 
@@ -105,70 +106,8 @@ __global__ __launch_bounds__(256, (WB == 2 ? 2 : 1)) void grouped_gemm_bf16_kern
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // ---- which tile: one wave reads the row table and places this block.
-  // Tiles are ordered expert by expert; inside an expert, in bands of up to
-  // `band` row tiles, and inside a band by weight tile with the row tiles
-  // fastest.  The actual tile count (known only on the device) is dealt to
-  // the 8 XCDs in equal contiguous ranges (blocks go to XCDs round-robin), so
-  // the tiles running at once on one XCD share weight and token rows in L2
-  // and no XCD is left with only empty slots.
-  if (wave == 0) {
-    if (lane == 0) s_tile[0] = -1;
-    int total = 0;
-    for (int b0 = 0; b0 < E; b0 += 64) {
-      const int e = b0 + lane;
-      int nt = 0;
-      if (e < E) {  // clamp a malformed table into [0, rows] so accesses stay in bounds
-        const int o0 = min(max(offs[e], 0), rows), o1 = min(max(offs[e + 1], o0), rows);
-        nt = (o1 - o0 + TM - 1) / TM;
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) nt += __shfl_xor(nt, o);
-      total += nt;
-    }
-    const int n_total = total * n_tiles;
-    const int per_xcd = (n_total + 7) >> 3;
-    const int L = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-    if ((int)(blockIdx.x >> 3) < per_xcd && L < n_total) {
-      int carry = 0;  // tiles of the experts before this 64-expert chunk
-      for (int b0 = 0; b0 < E; b0 += 64) {
-        const int e = b0 + lane;
-        int o0 = 0, o1 = 0;
-        if (e < E) {
-          o0 = min(max(offs[e], 0), rows);
-          o1 = min(max(offs[e + 1], o0), rows);
-        }
-        const int mt = (o1 - o0 + TM - 1) / TM;
-        int incl = mt * n_tiles;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(incl, o);
-          if (lane >= o) incl += y;
-        }
-        const int excl = carry + incl - mt * n_tiles;
-        if (mt > 0 && L >= excl && L < excl + mt * n_tiles) {
-          const int r = L - excl;
-          const int g = min(band, mt);
-          const int full = mt / g;
-          int n, m;
-          if (r < full * g * n_tiles) {
-            const int bi = r / (g * n_tiles), rr = r - bi * g * n_tiles;
-            n = rr / g;
-            m = bi * g + rr % g;
-          } else {
-            const int gl = mt - full * g, rr = r - full * g * n_tiles;
-            n = rr / gl;
-            m = full * g + rr % gl;
-          }
-          s_tile[0] = e;
-          s_tile[1] = o0 + m * TM;
-          s_tile[2] = o1;
-          s_tile[3] = n;
-        }
-        carry += __shfl(incl, 63);
-      }
-    }
-  }
+  // ---- which tile (one wave reads the row table)
+  if (wave == 0) place_tile<TM>(offs, E, rows, n_tiles, band, lane, s_tile);
   __syncthreads();
   const int e = s_tile[0];
   if (e < 0) return;  // block-uniform
@@ -432,10 +371,7 @@ static GemmPlan plan_gemm(long rows, int E, int N, bool gated) {
   // many rows per expert: MFMA-bound, big tiles; otherwise weight streaming
   p.wb = (avg >= 512 && est256 >= 2 * cus) ? 4 : 2;
   (void)cus;
-  const int tm = 64 * p.wb;
-  long m_slots = (rows + (long)E * (tm - 1)) / tm;  // upper bound of sum_e ceil(c_e / tm)
-  if (m_slots < 1) m_slots = 1;
-  const long total = (long)p.n_tiles * m_slots;
+  const long total = (long)p.n_tiles * worst_row_tiles(rows, E, 64 * p.wb);
   p.blocks = (int)((total + 7) / 8 * 8);
   return p;
 }

@@ -1,0 +1,90 @@
+// Device-side placement of a grouped-GEMM block on its tile.
+//
+// The per-expert row counts live only on the device (expert_offsets), so the
+// grid is sized on the host for the worst case and every block finds its tile
+// here.  Pages: [SyncTax] §2.2 (skewed expert load must not stall the rest;
+// hot experts simply own more tiles) and [EP-V4] §5.2 (expert weights are
+// contiguous and in expert-ID order, so neighbouring tiles share weight rows).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// Called by ONE whole wave (64 lanes) of the block.  Tiles are ordered expert
+// by expert; inside an expert in bands of up to `band` row tiles of TM rows,
+// and inside a band by weight tile with the row tiles fastest, so the tiles
+// running at once on one XCD share one expert's weight rows (across row
+// tiles) and token rows (across weight tiles) in that XCD's L2.  The actual
+// tile count is dealt to the 8 XCDs (the hardware hands blocks to XCDs
+// round-robin) in equal contiguous ranges, so the surplus blocks of the
+// worst-case grid never pile up on one XCD.
+// Writes s_tile = {expert, first row, end row of the expert, weight tile};
+// s_tile[0] = -1 when the block has no tile.  A malformed table is clamped
+// into [0, rows] so that every access stays in bounds.
+template <int TM>
+__device__ __forceinline__ void place_tile(const int32_t* __restrict__ offs, int E, int rows,
+                                           int n_tiles, int band, int lane, int* s_tile) {
+  if (lane == 0) s_tile[0] = -1;
+  int total = 0;
+  for (int b0 = 0; b0 < E; b0 += 64) {
+    const int e = b0 + lane;
+    int nt = 0;
+    if (e < E) {
+      const int o0 = min(max(offs[e], 0), rows), o1 = min(max(offs[e + 1], o0), rows);
+      nt = (o1 - o0 + TM - 1) / TM;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) nt += __shfl_xor(nt, o);
+    total += nt;
+  }
+  const int n_total = total * n_tiles;
+  const int per_xcd = (n_total + 7) >> 3;
+  const int L = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= per_xcd || L >= n_total) return;
+  int carry = 0;  // tiles of the experts before this 64-expert chunk
+  for (int b0 = 0; b0 < E; b0 += 64) {
+    const int e = b0 + lane;
+    int o0 = 0, o1 = 0;
+    if (e < E) {
+      o0 = min(max(offs[e], 0), rows);
+      o1 = min(max(offs[e + 1], o0), rows);
+    }
+    const int mt = (o1 - o0 + TM - 1) / TM;
+    int incl = mt * n_tiles;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const int excl = carry + incl - mt * n_tiles;
+    if (mt > 0 && L >= excl && L < excl + mt * n_tiles) {
+      const int r = L - excl;
+      const int g = min(band, mt);
+      const int full = mt / g;
+      int n, m;
+      if (r < full * g * n_tiles) {
+        const int bi = r / (g * n_tiles), rr = r - bi * g * n_tiles;
+        n = rr / g;
+        m = bi * g + rr % g;
+      } else {
+        const int gl = mt - full * g, rr = r - full * g * n_tiles;
+        n = rr / gl;
+        m = full * g + rr % gl;
+      }
+      s_tile[0] = e;
+      s_tile[1] = o0 + m * TM;
+      s_tile[2] = o1;
+      s_tile[3] = n;
+    }
+    carry += __shfl(incl, 63);
+  }
+}
+
+// Upper bound of sum_e ceil(c_e / TM) over every row table with `rows` rows.
+inline long worst_row_tiles(long rows, int E, int tm) {
+  const long m = (rows + (long)E * (tm - 1)) / tm;
+  return m < 1 ? 1 : m;
+}
+
+}  // namespace moe
