@@ -32,18 +32,19 @@
 //     F..F+31 of W_down with F = 256 slab + 64 w + 32 i.
 //   Rows past the last feature are zero.
 //
-// Kernel (one block of 4 waves per CU, 256 accumulators per wave):
-//  * block tile = one slab x up to 256 tokens of one expert; wave w owns two
+// Kernel (persistent, one block of 4 waves per CU, 256 accumulators per wave):
+//  * tile = one slab x up to 256 token rows of one expert; wave w owns two
 //    32-row weight fragments (64 rows) against all token fragments, so every
 //    weight byte is used by exactly one wave.
 //  * k loop in iterations of 128 (8 MFMA k-steps).  Weight fragments for
-//    k-step s+8 are loaded into the register slot of k-step s right after its
-//    MFMAs.  The next 128-wide token stage is loaded into registers during
-//    k-steps 0..3 and written to the other LDS buffer during k-steps 4..7
-//    (LDS rows of 256 bytes, 16-byte pieces XOR-swizzled with row & 15); one
-//    barrier per iteration.
-//  * All loads are ordinary compiler-visible loads, so the compiler's own
-//    vmcnt waits are exact.
+//    k-step s+8 are loaded into the register slot of k-step s right after the
+//    MFMAs that use it.  Token rows pass through a ring of four 64-wide k
+//    half-stages in LDS (rows of 128 bytes, 16-byte pieces XOR-swizzled with
+//    (row >> 1) & 7 so the 16 lanes of a 16-byte read hit 16 bank groups):
+//    each half-stage is loaded into registers one half-stage ahead and written
+//    two ahead; one barrier per half-stage.
+//  * Operands are read through buffer resources (one address register per
+//    stream); all loads are compiler-visible, so its vmcnt waits are exact.
 //  * The main loop is specialised on the number of 32-token fragments that
 //    hold rows; padded token rows read a clamped (real) row and are not
 //    stored; padded k reads zeros.
@@ -58,6 +59,8 @@ namespace moe {
 
 constexpr int kPkIterK = 128;  // k per main-loop iteration
 constexpr int kPkSteps = 8;    // MFMA k-steps (16 wide) per iteration
+// Word 3 of a raw (untyped, unswizzled) buffer resource on gfx950.
+constexpr int kBufferFlags = 0x00020000;
 
 // Features per slab and packed geometry of one weight set.
 PackGeom pack_geom(int features, int K, bool gated) {
@@ -119,89 +122,118 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // JMAX: 32-token fragments per block tile (tile = 32 JMAX tokens).
-template <bool GATED, int JMAX>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
+//
+// Persistent: the grid holds one block per CU (a multiple of 8) and every
+// block walks its own list of tiles.  Tiles go out in rounds of one tile per
+// block; inside a round, consecutive tiles go to the blocks of one XCD (the
+// hardware hands blocks to XCDs round-robin, block b to XCD b % 8), so the
+// tiles running at once on an XCD are neighbours in the tile order and share
+// weight and token rows in its L2; every other round runs backwards, which
+// evens out the per-block totals when tiles differ in size.  A grid of one
+// block per tile would be dispatched in block order, and an XCD whose tiles
+// run long would hold back the dispatch of every other XCD.
+template <bool GATED, int JMAX, int OCC>
+__global__ __launch_bounds__(256, OCC) void grouped_gemm_packed_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offs,
     const u32x4* __restrict__ wp, uint16_t* __restrict__ out, int E, int N, int K, int rows,
     int slabs, int band) {
   constexpr int TM = 32 * JMAX;
+  // k-steps of weight fragments in flight per wave: 8 with one block per CU;
+  // 4 with two, whose other block's waves cover the rest of the latency
+  constexpr int WQ = (OCC == 1 && JMAX <= 8) ? kPkSteps : kPkSteps / 2;
   constexpr int TN = GATED ? 128 : 256;  // output features per slab
   constexpr int HALF = TM * 8;           // 16-byte pieces of one 64-wide k half-stage
-  static_assert(JMAX <= 8, "two staging chunks per k-step cover at most 8 fragments");
-  __shared__ u32x4 tok[4 * HALF];        // ring of four 64-wide k half-stages
+  // LDS ring of 64-wide k half-stages: four slots, three for 320-row tiles
+  constexpr int NSLOT = JMAX > 8 ? 3 : 4;
+  static_assert(JMAX <= 10, "at most 10 token fragments per tile");
+  __shared__ u32x4 tok[NSLOT * HALF];
   __shared__ int s_tile[4];
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int G = (int)gridDim.x;
+  const int qp = (G >> 3) * (int)(blockIdx.x & 7) + (int)(blockIdx.x >> 3);
+  __shared__ int s_total;
+  if (threadIdx.x < 64) {
+    const int n = count_row_tiles<TM>(offs, E, rows, (int)threadIdx.x) * slabs;
+    if (threadIdx.x == 0) s_total = n;
+  }
+  for (int round = 0;; ++round) {
+  // Per-tile state is recomputed every round: values live across the loop
+  // would push the main loop's register allocation past the register file.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));  // keep the compiler from hoisting lane state out of the loop
+  const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (wave == 0) place_tile<TM>(offs, E, rows, slabs, band, lane, s_tile);
+  if (wave == 0) {  // s_total and s_tile: written and read in order by this one wave
+    const int L = round * G + ((round & 1) ? G - 1 - qp : qp);
+    if (lane == 0) s_tile[0] = -1;
+    if (L < s_total) locate_tile<TM>(offs, E, rows, slabs, band, L, lane, s_tile);
+  }
   __syncthreads();
   const int e = __builtin_amdgcn_readfirstlane(s_tile[0]);
-  if (e < 0) return;  // block-uniform
+  if (e < 0) break;  // block-uniform; later rounds only hold larger tile numbers
+  const int kp = (K + kPkIterK - 1) / kPkIterK * kPkIterK;
+  const int nit = kp / kPkIterK;
+  const uint32_t wl = (uint32_t)lane * 16u;
+  // the activations as one buffer resource: rows * K * 2 < 2^32 bytes
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(act), (short)0, (int)((uint32_t)rows * (uint32_t)K * 2u), kBufferFlags);
+
+  // Token half-stage h = k range [64 h, 64 h + 64) of the tile's rows: LDS
+  // rows of 128 bytes, 16-byte piece q of row r at q ^ ((r >> 1) & 7), so the
+  // 16 lanes served together by a 16-byte LDS read (16 consecutive rows, one
+  // piece) hit 16 different bank groups.  Load chunk c covers tile rows
+  // 32c..32c+31; this lane takes row 32c + 8 wave + lane/8, piece lane & 7.
+  const int tq = lane & 7, trow = 8 * wave + (lane >> 3);
+  const int tpos = trow * 8 + (tq ^ ((trow >> 1) & 7));  // LDS piece in chunk 0
+  // fragment reads: token row 32 j + (lane & 31), piece (2 u' + lk) ^ (row >> 1 & 7)
+  const int lk = lane >> 5, bbase = (lane & 31) * 8, bsw = (lane >> 1) & 7;
   const int row0 = __builtin_amdgcn_readfirstlane(s_tile[1]);
   const int row_end = __builtin_amdgcn_readfirstlane(s_tile[2]);
   const int slab = __builtin_amdgcn_readfirstlane(s_tile[3]);
   const int nrow = min(row_end - row0, TM);
   const int jn = (nrow + 31) >> 5;  // live token fragments, 1..JMAX
-  const int kp = (K + kPkIterK - 1) / kPkIterK * kPkIterK;
-  const int nit = kp / kPkIterK;
-  // this wave's weight stream (wave-uniform base) and the lane's byte offset in it
-  const char* __restrict__ wbase = reinterpret_cast<const char*>(
-      wp + (((size_t)e * slabs + slab) * 4 + wave) * ((size_t)(kp / 16) * 128));
-  const uint32_t wl = (uint32_t)lane * 16u;
+  // This wave's weight stream as a buffer resource (wave-uniform base and
+  // size): a load is one VGPR offset (the lane's 16 bytes) plus a uniform
+  // offset (fragment i of k-step s), so the stream costs no address registers.
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4*>(wp + (((size_t)e * slabs + slab) * 4 + wave) * ((size_t)(kp / 16) * 128)),
+      (short)0, (kp / 16) * 2048, kBufferFlags);
   auto wload = [&](int s, int i) -> u32x4 {  // fragment i of k-step s
-    return *reinterpret_cast<const u32x4*>(wbase + (size_t)(s * 2 + i) * 1024 + wl);
+    return __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)wl, s * 2048 + i * 1024, 0);
   };
-  const char* __restrict__ abase = reinterpret_cast<const char*>(act);
-
-  // Token half-stage h = k range [64 h, 64 h + 64) of the tile's rows: LDS
-  // rows of 128 bytes, 16-byte piece q of row r at q ^ (r & 7).  Load chunk c
-  // covers tile rows 32c..32c+31; this lane takes row 32c + 8 wave + lane/8,
-  // piece lane & 7.
-  const int tq = lane & 7, trow = 8 * wave + (lane >> 3);
-  const int tpos = trow * 8 + (tq ^ (trow & 7));  // LDS piece in chunk 0
-  // fragment reads: token row 32 j + (lane & 31), piece (2 u' + lk) ^ (lane & 7)
-  const int lk = lane >> 5, bbase = (lane & 31) * 8, bsw = lane & 7;
 
   auto run = [&](auto jn_c) {
     constexpr int JN = decltype(jn_c)::value;
-    // byte offset of each load chunk's row (clamped to the tile's last row)
-    uint32_t toff[JN];
-#pragma unroll
-    for (int c = 0; c < JN; ++c)
-      toff[c] = ((uint32_t)(row0 + min(32 * c + trow, nrow - 1)) * (uint32_t)K + 8u * tq) * 2u;
+    // Load chunk c covers tile rows 32c..32c+31.  Only the last chunk can
+    // reach past the expert's rows; it reads a clamped (real) row instead.
+    // The other chunks are this lane's row plus a uniform stride.
+    const uint32_t toff0 = ((uint32_t)(row0 + trow) * (uint32_t)K + 8u * tq) * 2u;
+    const uint32_t tofl =
+        ((uint32_t)(row0 + min(32 * (JN - 1) + trow, nrow - 1)) * (uint32_t)K + 8u * tq) * 2u;
+    const int cstride = 64 * K;  // bytes of 32 rows
     // Half-stages past K (K % 128 == 64) re-read the last real one: their
     // weights are zero in the packed image, so they add exact zeros.
     const int hlast = K / 64 - 1;
     auto load_chunk = [&](int h, int c) -> u32x4 {
-      return *reinterpret_cast<const u32x4*>(abase + (size_t)min(h, hlast) * 128 + toff[c]);
+      const int hb = min(h, hlast) * 128;
+      if (c == JN - 1) return __builtin_amdgcn_raw_buffer_load_b128(arsrc, (int)tofl, hb, 0);
+      return __builtin_amdgcn_raw_buffer_load_b128(arsrc, (int)toff0, hb + c * cstride, 0);
     };
-    // B fragments of k-step u of iteration t (LDS slot of its half-stage)
-    auto read_b = [&](int t, int u, u32x4(&b)[JN]) {
-      const u32x4* cur = tok + ((2 * t + (u >> 2)) & 3) * HALF;
-      const int q = (2 * (u & 3) + lk) ^ bsw;
-#pragma unroll
-      for (int j = 0; j < JN; ++j) b[j] = cur[bbase + 256 * j + q];
-    };
-
-    f32x16 acc[2][JN];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < JN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    auto slot = [&](int h) -> u32x4* { return tok + (h % NSLOT) * HALF; };
 
     // Pipeline.  Half-stage h (k range [64 h, 64 h + 64)) lives in LDS slot
-    // h % 4.  While the MFMAs of half-stage h run, the staged registers sg
-    // (half-stage h+2, loaded during h-1) are written to slot h+2 and sg is
-    // refilled with h+3, two chunks per k-step, so every load has four
-    // k-steps before its LDS write.  A barrier ends each half-stage; because
-    // writes run two half-stages ahead, the B fragments of the first k-step
-    // after a barrier are already read before it.  Weight fragments of k-step
-    // s+8 are loaded into wq slot s % 8 right after the MFMAs of k-step s.
-    u32x4 wq[kPkSteps][2];
+    // h % NSLOT.  While the MFMAs of half-stage h run, the staged registers
+    // sg (half-stage h+2, loaded during h-1) are written to slot h+2 and sg
+    // is refilled with h+3, a quarter of the chunks per k-step, so every load
+    // has four k-steps before its LDS write.  Slot h+2 was last read during
+    // h-1 (three slots) or h-2 (four), and a barrier ends every half-stage.
+    // The B fragment of token fragment j for the next k-step is read into the
+    // same registers right after the last MFMA that uses it, so the reads of
+    // one k-step overlap the MFMAs of the one before.  Weight fragment i of
+    // k-step s+WQ is loaded into wq slot s % WQ right after its last MFMA.
+    u32x4 wq[WQ][2];
     u32x4 sg[JN];
-    u32x4 bA[JN], bB[JN];
+    u32x4 bq[JN];
     // prologue, issued in the steady state's order: half-stages 0 and 1 (to
     // LDS now), k-steps 0..3, then half-stage 2 interleaved with k-steps 4..7
     u32x4 s0[JN], s1[JN];
@@ -219,11 +251,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
 #pragma unroll
     for (int u = 4; u < 8; ++u) {
 #pragma unroll
-      for (int c = 2 * (u - 4); c < 2 * (u - 4) + 2; ++c)
-        if (c < JN) sg[c] = load_chunk(2, c);  // clamped: valid even when nit == 1
+      for (int c = JN * (u - 4) / 4; c < JN * (u - 3) / 4; ++c)
+        sg[c] = load_chunk(2, c);  // clamped: valid even when nit == 1
       __builtin_amdgcn_sched_barrier(0);
+      if (u < WQ) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) wq[u][i] = wload(u, i);
+        for (int i = 0; i < 2; ++i) wq[u][i] = wload(u, i);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -231,7 +265,21 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
 #pragma unroll
     for (int c = 0; c < JN; ++c) tok[HALF + tpos + 256 * c] = s1[c];
     lds_barrier();
-    read_b(0, 0, bA);
+    {
+      const int q = lk ^ bsw;
+#pragma unroll
+      for (int j = 0; j < JN; ++j) bq[j] = tok[bbase + 256 * j + q];
+    }
+    // the accumulators come to life only now, after the prologue's staging
+    // registers are dead (both together would not fit the register file)
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 acc[2][JN];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < JN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // VAR 0: full iteration; 1: the one before the last (no load of
     // half-stage 2t+4); 2: the last (no loads, no LDS writes, no barrier).
@@ -241,51 +289,52 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       static_for<kPkSteps>([&](auto u_c) {
         constexpr int u = decltype(u_c)::value;
         constexpr int ph = u >> 2, uu = u & 3;  // half of the iteration, k-step in it
-        constexpr int n_chunk = (2 * uu + 2 <= JN) ? 2 : (2 * uu < JN ? JN - 2 * uu : 0);
+        constexpr int c_lo = JN * uu / 4, c_hi = JN * (uu + 1) / 4;
+        constexpr int n_chunk = c_hi - c_lo;
         constexpr bool WRITE = VAR < 2;
         constexpr bool LOAD = VAR == 0 || (VAR == 1 && ph == 0);
-        constexpr int n_dsw = WRITE ? n_chunk : 0;
-        constexpr int n_vmem = (LOAD ? n_chunk : 0) + (VAR < 2 ? 2 : 0);
         constexpr bool NEXT_B = u < 7 || VAR < 2;
-        constexpr int n_dsr = NEXT_B ? JN : 0;
+        constexpr bool WLOAD = VAR < 2 || u + WQ < kPkSteps;  // k-step s+WQ still in range
         const int h = 2 * t + ph;
 #pragma unroll
-        for (int c = 2 * uu; c < 2 * uu + n_chunk; ++c) {
-          if (WRITE) tok[((h + 2) & 3) * HALF + tpos + 256 * c] = sg[c];
+        for (int c = c_lo; c < c_hi; ++c) {
+          if (WRITE) slot(h + 2)[tpos + 256 * c] = sg[c];
           if (LOAD) sg[c] = load_chunk(h + 3, c);
         }
-        u32x4(&bc)[JN] = (u & 1) ? bB : bA;
-        u32x4(&bn)[JN] = (u & 1) ? bA : bB;
-        if (u < 7)
-          read_b(t, u + 1, bn);
-        else if (NEXT_B)
-          read_b(t + 1, 0, bn);
+        // next k-step's B fragments: slot and piece
+        const u32x4* nb_slot = slot(u < 7 ? h + (uu == 3 ? 1 : 0) : 2 * t + 2);
+        const int nq = (2 * ((u + 1) & 3) + lk) ^ bsw;
+        // i-major MFMA order: weight fragment 0 is free after the first JN
+        // MFMAs, fragment 1 and every B fragment after their last use
 #pragma unroll
         for (int j = 0; j < JN; ++j)
+          acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wq[u % WQ][0]),
+                                                              as_bf16x8(bq[j]), acc[0][j], 0, 0, 0);
+        if (WLOAD) wq[u % WQ][0] = wload(t * kPkSteps + u + WQ, 0);
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wq[u][i]),
-                                                                as_bf16x8(bc[j]), acc[i][j], 0, 0, 0);
-        if (VAR < 2) {
-#pragma unroll
-          for (int i = 0; i < 2; ++i) wq[u][i] = wload((t + 1) * kPkSteps + u, i);
+        for (int j = 0; j < JN; ++j) {
+          acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wq[u % WQ][1]),
+                                                              as_bf16x8(bq[j]), acc[1][j], 0, 0, 0);
+          if (NEXT_B) bq[j] = nb_slot[bbase + 256 * j + nq];
         }
-        // Issue order inside the k-step: the staged LDS writes first (their
-        // loads are four k-steps old), then the MFMAs with the next k-step's
-        // fragment reads and this k-step's global loads spread between them.
-        constexpr int n_mfma = 2 * JN;
-        constexpr int m_dsr = n_dsr < n_mfma ? n_dsr : n_mfma;
-        constexpr int m_vmem = n_vmem < n_mfma - m_dsr ? n_vmem : n_mfma - m_dsr;
+        if (WLOAD) wq[u % WQ][1] = wload(t * kPkSteps + u + WQ, 1);
+        // Issue order: the staged LDS writes first (their loads are four
+        // k-steps old), the token loads among the first MFMAs, then each B
+        // fragment read after its last MFMA.
+        constexpr int n_dsw = WRITE ? n_chunk : 0;
+        constexpr int n_tl = LOAD ? n_chunk : 0;
         if (n_dsw > 0) __builtin_amdgcn_sched_group_barrier(0x200, n_dsw, 0);
-        static_for<m_dsr>([&](auto) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        });
-        static_for<m_vmem>([&](auto) {
+        static_for<n_tl>([&](auto) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         });
-        __builtin_amdgcn_sched_group_barrier(0x008, n_mfma - m_dsr - m_vmem, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, JN - n_tl, 0);
+        if (WLOAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        static_for<JN>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (NEXT_B) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        });
+        if (WLOAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (uu == 3 && VAR < 2) {
           lds_barrier();
@@ -342,13 +391,18 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
   };
   switch (jn) {
     case 1: run(std::integral_constant<int, 1>()); break;
-    case 2: run(std::integral_constant<int, 2>()); break;
-    case 3: run(std::integral_constant<int, 3>()); break;
-    case 4: run(std::integral_constant<int, 4>()); break;
-    case 5: run(std::integral_constant<int, 5>()); break;
-    case 6: run(std::integral_constant<int, 6>()); break;
-    case 7: run(std::integral_constant<int, 7>()); break;
+    case 2: run(std::integral_constant<int, (2 < JMAX ? 2 : JMAX)>()); break;
+    case 3: run(std::integral_constant<int, (3 < JMAX ? 3 : JMAX)>()); break;
+    case 4: run(std::integral_constant<int, (4 < JMAX ? 4 : JMAX)>()); break;
+    case 5: run(std::integral_constant<int, (5 < JMAX ? 5 : JMAX)>()); break;
+    case 6: run(std::integral_constant<int, (6 < JMAX ? 6 : JMAX)>()); break;
+    case 7: run(std::integral_constant<int, (7 < JMAX ? 7 : JMAX)>()); break;
+    case 8: run(std::integral_constant<int, (8 < JMAX ? 8 : JMAX)>()); break;
+    case 9: run(std::integral_constant<int, (9 < JMAX ? 9 : JMAX)>()); break;
     default: run(std::integral_constant<int, JMAX>()); break;
+  }
+  // every wave is done with the LDS ring and s_tile before the next tile
+  __syncthreads();
   }
 }
 
@@ -378,19 +432,47 @@ hipError_t launch_pack_weights(const moe_config& c, const void* wg, const void* 
   return hipSuccess;
 }
 
-template <bool GATED>
-static hipError_t launch_packed(const moe_config& c, const void* act, const int32_t* offs,
-                                const void* wp, void* out, hipStream_t st) {
-  constexpr int JMAX = 8;
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+#ifndef PK_JMAX_GU
+#define PK_JMAX_GU 8
+#endif
+#ifndef PK_JMAX_DN
+#define PK_JMAX_DN 8
+#endif
+template <bool GATED, int JMAX>
+static hipError_t launch_packed_j(const moe_config& c, const void* act, const int32_t* offs,
+                                  const void* wp, void* out, hipStream_t st) {
+  constexpr int OCC = JMAX <= 4 ? 2 : 1;  // blocks per CU
   const long rows = (long)c.T * c.k;
   const int N = GATED ? c.f : c.d, K = GATED ? c.d : c.f;
   const PackGeom g = pack_geom(N, K, GATED);
-  const long total = (long)g.slabs * worst_row_tiles(rows, c.E, 32 * JMAX);
-  const int blocks = (int)((total + 7) / 8 * 8);
-  grouped_gemm_packed_kernel<GATED, JMAX><<<blocks, 256, 0, st>>>(
+  // OCC blocks per CU (never more blocks than the worst-case tile count)
+  const long worst = (long)g.slabs * worst_row_tiles(rows, c.E, 32 * JMAX);
+  const long cap = ((long)device_cus() * OCC + 7) / 8 * 8;
+  const int blocks = (int)std::min(cap, (worst + 7) / 8 * 8);
+  grouped_gemm_packed_kernel<GATED, JMAX, OCC><<<blocks, 256, 0, st>>>(
       static_cast<const uint16_t*>(act), offs, static_cast<const u32x4*>(wp),
       static_cast<uint16_t*>(out), c.E, N, K, (int)rows, g.slabs, 8);
   return hipGetLastError();
+}
+
+template <bool GATED>
+static hipError_t launch_packed(const moe_config& c, const void* act, const int32_t* offs,
+                                const void* wp, void* out, hipStream_t st) {
+  return launch_packed_j<GATED, GATED ? PK_JMAX_GU : PK_JMAX_DN>(c, act, offs, wp, out, st);
 }
 
 hipError_t launch_ffn_gate_up_packed(const moe_config& c, const void* x_perm, const int32_t* offs,

@@ -11,21 +11,12 @@
 
 namespace moe {
 
-// Called by ONE whole wave (64 lanes) of the block.  Tiles are ordered expert
-// by expert; inside an expert in bands of up to `band` row tiles of TM rows,
-// and inside a band by weight tile with the row tiles fastest, so the tiles
-// running at once on one XCD share one expert's weight rows (across row
-// tiles) and token rows (across weight tiles) in that XCD's L2.  The actual
-// tile count is dealt to the 8 XCDs (the hardware hands blocks to XCDs
-// round-robin) in equal contiguous ranges, so the surplus blocks of the
-// worst-case grid never pile up on one XCD.
-// Writes s_tile = {expert, first row, end row of the expert, weight tile};
-// s_tile[0] = -1 when the block has no tile.  A malformed table is clamped
+// Row tiles of TM rows over every expert: sum_e ceil(c_e / TM), reduced over
+// ONE whole wave (every lane gets the total).  A malformed table is clamped
 // into [0, rows] so that every access stays in bounds.
 template <int TM>
-__device__ __forceinline__ void place_tile(const int32_t* __restrict__ offs, int E, int rows,
-                                           int n_tiles, int band, int lane, int* s_tile) {
-  if (lane == 0) s_tile[0] = -1;
+__device__ __forceinline__ int count_row_tiles(const int32_t* __restrict__ offs, int E, int rows,
+                                               int lane) {
   int total = 0;
   for (int b0 = 0; b0 < E; b0 += 64) {
     const int e = b0 + lane;
@@ -38,10 +29,18 @@ __device__ __forceinline__ void place_tile(const int32_t* __restrict__ offs, int
     for (int o = 32; o > 0; o >>= 1) nt += __shfl_xor(nt, o);
     total += nt;
   }
-  const int n_total = total * n_tiles;
-  const int per_xcd = (n_total + 7) >> 3;
-  const int L = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if ((int)(blockIdx.x >> 3) >= per_xcd || L >= n_total) return;
+  return total;
+}
+
+// Finds tile L (0 <= L < row tiles * n_tiles) in the tile order, called by ONE
+// whole wave.  Tiles are ordered expert by expert; inside an expert in bands
+// of up to `band` row tiles of TM rows, and inside a band by weight tile with
+// the row tiles fastest, so that neighbouring tiles share one expert's weight
+// rows (across row tiles) and token rows (across weight tiles).
+// Writes s_tile = {expert, first row, end row of the expert, weight tile}.
+template <int TM>
+__device__ __forceinline__ void locate_tile(const int32_t* __restrict__ offs, int E, int rows,
+                                            int n_tiles, int band, int L, int lane, int* s_tile) {
   int carry = 0;  // tiles of the experts before this 64-expert chunk
   for (int b0 = 0; b0 < E; b0 += 64) {
     const int e = b0 + lane;
@@ -79,6 +78,24 @@ __device__ __forceinline__ void place_tile(const int32_t* __restrict__ offs, int
     }
     carry += __shfl(incl, 63);
   }
+}
+
+// One block per tile of a grid sized for the worst case, called by ONE whole
+// wave.  The actual tile count (known only on the device) is dealt to the 8
+// XCDs (the hardware hands blocks to XCDs round-robin) in equal contiguous
+// ranges, so the tiles running at once on one XCD are neighbours in the tile
+// order and share weight and token rows in that XCD's L2, and the surplus
+// blocks of the worst-case grid never pile up on one XCD.  s_tile[0] = -1
+// when the block has no tile.
+template <int TM>
+__device__ __forceinline__ void place_tile(const int32_t* __restrict__ offs, int E, int rows,
+                                           int n_tiles, int band, int lane, int* s_tile) {
+  if (lane == 0) s_tile[0] = -1;
+  const int n_total = count_row_tiles<TM>(offs, E, rows, lane) * n_tiles;
+  const int per_xcd = (n_total + 7) >> 3;
+  const int L = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= per_xcd || L >= n_total) return;
+  locate_tile<TM>(offs, E, rows, n_tiles, band, L, lane, s_tile);
 }
 
 // Upper bound of sum_e ceil(c_e / TM) over every row table with `rows` rows.
