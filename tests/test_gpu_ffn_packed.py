@@ -58,6 +58,41 @@ def test_packed_ffn_matches_oracle(case):
     _check(shape, xp_np, offs_np, wg, wu, wd, h, y)
 
 
+# Problems with enough tiles to fill the chip run whole-slab tiles of up to
+# 256 rows (the others half-slab tiles of up to 320 rows): these two shapes
+# reach the whole-slab kernel for both GEMMs (E=64) and for the gate/up GEMM
+# only (E=16), with experts above 256 rows, so both shapes and their ragged
+# tails are covered.  Rows are sampled for the oracle.
+WIDE = [
+    (64, 2048, 1088, 0, 300),
+    (16, 1024, 4096, 200, 700),
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=[f"E{c[0]}-d{c[1]}-f{c[2]}" for c in WIDE])
+def test_packed_ffn_whole_slab_tiles(case):
+    E, d, f, lo, hi = case
+    log(f"[ffn-packed] whole-slab tiles {case[:3]}")
+    rng = np.random.default_rng(E + d + f)
+    counts = rng.integers(lo, hi, size=E)
+    counts[1] = 0
+    A = int(counts.sum())
+    shape = C.E8_D4096.replace(name="ffn-packed-wide", T=A, k=1, E=E, d=d, f=f, ep_ranks=1)
+    offs_np = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    xp_np = I.make_x(shape, seed=71)
+    wg, wu, wd = _weights(shape, 72)
+    dev = [B.to_device(a) for a in (xp_np, wg, wu, wd)]
+    offs = torch.from_numpy(offs_np).cuda()
+    h, y = _run_packed(shape, dev[0], offs, *dev[1:])
+    # every tile's first and last rows, plus a random sample
+    rows = set(rng.choice(A, size=min(A, 384), replace=False).tolist())
+    for e in range(E):
+        r0, r1 = int(offs_np[e]), int(offs_np[e + 1])
+        for r in range(r0, r1, 256):
+            rows.update({r, min(r + 255, r1 - 1)})
+    _check(shape, xp_np, offs_np, wg, wu, wd, h, y, rows=np.array(sorted(rows)))
+
+
 def test_packed_matches_row_major_path():
     """Same sums in the same k order: the packed and row-major paths agree to
     within one bf16 rounding of h (identical in almost every element)."""

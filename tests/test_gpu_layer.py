@@ -22,11 +22,16 @@ from top_routing_expert_amd import inputs as I
 pytestmark = pytest.mark.gpu
 
 
-def _layer_fwd(shape, dev, buf, bufs=True):
+def _layer_fwd(shape, dev, buf, bufs=True, packed=False):
     cfg = B.config(shape)
     keep = {n: buf[n] for n in B.LAYER_BUF_FIELDS} if bufs else None
-    B.moe_layer_fwd(cfg, dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"],
-                    dev["w_down"], buf["out"], keep, B.workspace(cfg, "layer"))
+    if packed:
+        pgu, pd = B.pack_weights(cfg, dev["w_gate"], dev["w_up"], dev["w_down"])
+        B.moe_layer_fwd_packed(cfg, dev["x"], dev["w_router"], dev["bias"], pgu, pd, buf["out"],
+                               keep, B.workspace(cfg, "layer"))
+    else:
+        B.moe_layer_fwd(cfg, dev["x"], dev["w_router"], dev["bias"], dev["w_gate"], dev["w_up"],
+                        dev["w_down"], buf["out"], keep, B.workspace(cfg, "layer"))
     torch.cuda.synchronize()
 
 
@@ -114,17 +119,30 @@ def _sampled_outputs(shape, inp, idx, w, tokens):
 
 
 FULL_SAMPLES = {1: 256, 2: 48, 3: 48, 4: 32, 5: 8}
+# the benchmark's layout (packed expert weights) on every bf16 workload, and
+# the plain weight layout on every workload
+FULL_CASES = [(ci, False) for ci in range(1, 6)] + [(ci, True) for ci in range(2, 6)]
+_inputs_cache = {}
 
 
-@pytest.mark.parametrize("ci", [1, 2, 3, 4, 5], ids=[c.name for c in C.CONFIGS])
-def test_layer_full_size_sampled(ci):
+def _full_inputs(ci):
+    if ci not in _inputs_cache:
+        _inputs_cache.clear()  # one workload's inputs at a time (the largest is ~23 GB)
+        _inputs_cache[ci] = I.make_inputs(C.CONFIGS[ci - 1], seed=ci)
+    return _inputs_cache[ci]
+
+
+@pytest.mark.parametrize("ci,packed", sorted(FULL_CASES),
+                         ids=[f"{C.CONFIGS[c - 1].name}-{'packed' if p else 'rowmajor'}"
+                              for c, p in sorted(FULL_CASES)])
+def test_layer_full_size_sampled(ci, packed):
     shape = C.CONFIGS[ci - 1]
-    log(f"[layer] full {shape.name}: generating inputs")
-    inp = I.make_inputs(shape, seed=ci)
+    log(f"[layer] full {shape.name} ({'packed' if packed else 'row-major'} weights): inputs")
+    inp = _full_inputs(ci)
     log("  uploading")
     dev, buf = upload(inp), alloc(shape)
-    log("  moe_layer_fwd")
-    _layer_fwd(shape, dev, buf, bufs=True)
+    log("  moe_layer_fwd" + ("_packed" if packed else ""))
+    _layer_fwd(shape, dev, buf, bufs=True, packed=packed)
     del dev
     idx, w_gpu, out = host(buf["topk_idx"]), host(buf["topk_w"]), host(buf["out"])
     # routing of every token

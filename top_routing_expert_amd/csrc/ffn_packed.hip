@@ -117,11 +117,93 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl<N>(f, std::make_integer_sequence<int, N>());
 }
 
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource (gfx950) over `bytes` bytes at `base`; every word is
+// made wave-uniform so the descriptor lives in scalar registers.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));  // stride 0
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = kBufferFlags;
+  return r;
 }
 
-// JMAX: 32-token fragments per block tile (tile = 32 JMAX tokens).
+// The main loop issues its loads itself and waits for them with explicit
+// counts: the weight loads (into registers) and the token copies (straight
+// into LDS) share one in-order counter, and a compiler-placed wait for one
+// would also drain the other's far-ahead loads.
+//
+// 16 bytes per lane of a weight stream into registers (buffer_load_dwordx4).
+template <int IMM>
+__device__ __forceinline__ u32x4 wload_async(i32x4 rsrc, uint32_t voff, int soff) {
+  u32x4 v;
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4"
+               : "=v"(v)
+               : "v"(voff), "s"(rsrc), "s"(soff), "n"(IMM));
+  return v;
+}
+// Direct global -> LDS copy: lane L writes LDS bytes [lds + 16 L, lds + 16 L + 16)
+// from sbase + voff (wave-uniform `sbase` and `lds`).
+__device__ __forceinline__ void dma_async(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(lds)
+               : "memory", "m0");
+}
+// Wait until at most N loads are in flight; the weight registers are passed
+// through so that no use of them can be placed before the wait.
+template <int N>
+__device__ __forceinline__ void wait_vm(u32x4& a) {
+  asm volatile("s_waitcnt vmcnt(%1)" : "+v"(a) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void wait_vm(u32x4& a, u32x4& b) {
+  asm volatile("s_waitcnt vmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+// Wait until at most N loads are in flight and this wave's LDS reads are
+// done, then barrier: afterwards every wave's copies issued before the last
+// N loads are in LDS, and no wave still reads a slot about to be refilled.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Load schedule of the main loop (compile-time).  k-step s = 8 t + u of
+// iteration t, half-stage h = 2 t + (u >> 2), uu = u & 3.  Every k-step of a
+// FULL iteration issues, in this order: the token copies of chunks
+// [cl(uu), cl(uu+1)) of half-stage h + D, its wait for weight k-step s, the
+// MFMAs, and WF weight loads of k-step s + 8 (the last one at its end).  The
+// last iteration issues nothing.  The prologue issues the copies of
+// half-stages 0..D-3 and then a pseudo iteration -1 in the FULL pattern, so
+// the counts below hold from the first k-step on.  Loads past the end of the
+// tile read clamped (real) addresses and land in slots nobody reads.
+struct PkSched {
+  int JN, WF, D;
+  constexpr int cl(int uu) const { return JN * uu / 4; }  // first chunk copied at k-step uu
+  constexpr int nc(int uu) const { return cl(uu + 1) - cl(uu); }
+  // loads issued after weight k-step s (issued at the end of k-step s - 8)
+  // up to the wait at the start of k-step s, s in a FULL iteration
+  constexpr int w_full() const { return 2 * JN + 7 * WF; }
+  // the same in the last iteration (no loads of its own), k-step u of it
+  constexpr int w_last(int u) const {
+    int n = 0;
+    for (int k = u + 1; k < 8; ++k) n += nc(k & 3) + WF;
+    return n;
+  }
+  // at the end of half-stage h (before the first read of half-stage h + 1),
+  // loads issued after the last copy of half-stage h + 1 (issued at k-step 3
+  // of half-stage h + 1 - D)
+  constexpr int x_full() const { return WF + (D - 1) * (JN + 4 * WF); }
+  constexpr int x_last() const { return WF + (D - 2) * (JN + 4 * WF); }  // first half of the last iteration
+  // before the first barrier, loads issued after half-stage 0's copies
+  constexpr int x_first() const { return D >= 3 ? 2 * JN + 8 * WF : WF + JN + 4 * WF; }
+};
+
+// JMAX: 32-token fragments per tile (tile = 32 JMAX tokens); WF: 32-row
+// weight fragments per wave (2: a tile spans a whole slab; 1: half a slab, for
+// GEMMs with too few tiles to fill the chip).
 //
 // Persistent: the grid holds one block per CU (a multiple of 8) and every
 // block walks its own list of tiles.  Tiles go out in rounds of one tile per
@@ -132,30 +214,29 @@ __device__ __forceinline__ void lds_barrier() {
 // evens out the per-block totals when tiles differ in size.  A grid of one
 // block per tile would be dispatched in block order, and an XCD whose tiles
 // run long would hold back the dispatch of every other XCD.
-template <bool GATED, int JMAX, int OCC>
-__global__ __launch_bounds__(256, OCC) void grouped_gemm_packed_kernel(
+template <bool GATED, int JMAX, int WF>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offs,
     const u32x4* __restrict__ wp, uint16_t* __restrict__ out, int E, int N, int K, int rows,
     int slabs, int band) {
   constexpr int TM = 32 * JMAX;
-  // k-steps of weight fragments in flight per wave: 8 with one block per CU;
-  // 4 with two, whose other block's waves cover the rest of the latency
-  constexpr int WQ = (OCC == 1 && JMAX <= 8) ? kPkSteps : kPkSteps / 2;
-  constexpr int TN = GATED ? 128 : 256;  // output features per slab
-  constexpr int HALF = TM * 8;           // 16-byte pieces of one 64-wide k half-stage
-  // LDS ring of 64-wide k half-stages: four slots, three for 320-row tiles
-  constexpr int NSLOT = JMAX > 8 ? 3 : 4;
-  static_assert(JMAX <= 10, "at most 10 token fragments per tile");
-  __shared__ u32x4 tok[NSLOT * HALF];
+  constexpr int TN = GATED ? 128 : 256;       // output features per slab
+  constexpr int HB = TM * 128;                // bytes of one 64-wide k half-stage
+  constexpr int NSLOT = 4 * HB <= 150 * 1024 ? 4 : 3;  // LDS ring of half-stages
+  constexpr int D = NSLOT - 1;                // half-stages of copy lookahead
+  constexpr int NT = WF == 2 ? 1 : 2;         // tiles per slab
+  static_assert(JMAX <= 10 && (WF == 1 || WF == 2), "tile shape");
+  __shared__ __attribute__((aligned(16))) unsigned char tokb[NSLOT * HB];
   __shared__ int s_tile[4];
+  __shared__ int s_total;
 
   const int G = (int)gridDim.x;
   const int qp = (G >> 3) * (int)(blockIdx.x & 7) + (int)(blockIdx.x >> 3);
-  __shared__ int s_total;
   if (threadIdx.x < 64) {
-    const int n = count_row_tiles<TM>(offs, E, rows, (int)threadIdx.x) * slabs;
+    const int n = count_row_tiles<TM>(offs, E, rows, (int)threadIdx.x) * slabs * NT;
     if (threadIdx.x == 0) s_total = n;
   }
+  const uint32_t lds0 = (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)tokb;
   for (int round = 0;; ++round) {
   // Per-tile state is recomputed every round: values live across the loop
   // would push the main loop's register allocation past the register file.
@@ -166,189 +247,163 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_packed_kernel(
   if (wave == 0) {  // s_total and s_tile: written and read in order by this one wave
     const int L = round * G + ((round & 1) ? G - 1 - qp : qp);
     if (lane == 0) s_tile[0] = -1;
-    if (L < s_total) locate_tile<TM>(offs, E, rows, slabs, band, L, lane, s_tile);
+    if (L < s_total) locate_tile<TM>(offs, E, rows, slabs * NT, band, L, lane, s_tile);
   }
   __syncthreads();
   const int e = __builtin_amdgcn_readfirstlane(s_tile[0]);
   if (e < 0) break;  // block-uniform; later rounds only hold larger tile numbers
-  const int kp = (K + kPkIterK - 1) / kPkIterK * kPkIterK;
-  const int nit = kp / kPkIterK;
-  const uint32_t wl = (uint32_t)lane * 16u;
-  // the activations as one buffer resource: rows * K * 2 < 2^32 bytes
-  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(act), (short)0, (int)((uint32_t)rows * (uint32_t)K * 2u), kBufferFlags);
-
-  // Token half-stage h = k range [64 h, 64 h + 64) of the tile's rows: LDS
-  // rows of 128 bytes, 16-byte piece q of row r at q ^ ((r >> 1) & 7), so the
-  // 16 lanes served together by a 16-byte LDS read (16 consecutive rows, one
-  // piece) hit 16 different bank groups.  Load chunk c covers tile rows
-  // 32c..32c+31; this lane takes row 32c + 8 wave + lane/8, piece lane & 7.
-  const int tq = lane & 7, trow = 8 * wave + (lane >> 3);
-  const int tpos = trow * 8 + (tq ^ ((trow >> 1) & 7));  // LDS piece in chunk 0
-  // fragment reads: token row 32 j + (lane & 31), piece (2 u' + lk) ^ (row >> 1 & 7)
-  const int lk = lane >> 5, bbase = (lane & 31) * 8, bsw = (lane >> 1) & 7;
   const int row0 = __builtin_amdgcn_readfirstlane(s_tile[1]);
   const int row_end = __builtin_amdgcn_readfirstlane(s_tile[2]);
-  const int slab = __builtin_amdgcn_readfirstlane(s_tile[3]);
+  const int wt = __builtin_amdgcn_readfirstlane(s_tile[3]);
+  const int slab = wt / NT, half = wt % NT;
   const int nrow = min(row_end - row0, TM);
   const int jn = (nrow + 31) >> 5;  // live token fragments, 1..JMAX
-  // This wave's weight stream as a buffer resource (wave-uniform base and
-  // size): a load is one VGPR offset (the lane's 16 bytes) plus a uniform
-  // offset (fragment i of k-step s), so the stream costs no address registers.
-  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<u32x4*>(wp + (((size_t)e * slabs + slab) * 4 + wave) * ((size_t)(kp / 16) * 128)),
-      (short)0, (kp / 16) * 2048, kBufferFlags);
-  auto wload = [&](int s, int i) -> u32x4 {  // fragment i of k-step s
-    return __builtin_amdgcn_raw_buffer_load_b128(wrsrc, (int)wl, s * 2048 + i * 1024, 0);
-  };
+  const int kp = (K + kPkIterK - 1) / kPkIterK * kPkIterK;
+  const int nit = kp / kPkIterK;
+  const int hlast = K / 64 - 1;  // half-stages past K re-read the last real one (zero weights)
+
+  // This wave's weight stream as a buffer resource; fragment i of k-step s is
+  // at s * 2048 + i * 1024 (WF = 1 tiles take fragment `half` of each stream).
+  const i32x4 wrsrc = make_rsrc(
+      wp + (((size_t)e * slabs + slab) * 4 + wave) * ((size_t)(kp / 16) * 128),
+      (uint32_t)(kp / 16) * 2048u);
+  const uint32_t wl = (uint32_t)lane * 16u;
+  const int wfrag0 = WF == 2 ? 0 : half * 1024;
+
+  // Token copies.  Half-stage h = k range [64 h, 64 h + 64) of the tile's rows,
+  // in LDS slot h % NSLOT: rows of 128 bytes, the 16-byte piece q of row r at
+  // q ^ ((r >> 1) & 7), so the 16 lanes served together by a 16-byte LDS read
+  // (16 consecutive rows, one piece) hit 16 different bank groups.  Chunk c =
+  // tile rows 32c..32c+31; this wave copies rows 32c + 8 wave .. + 7 with one
+  // instruction: lane l fills LDS row 32c + 8 wave + l/8, piece l & 7, with
+  // the logical piece (l & 7) ^ swizzle of that row.  Only the last chunk can
+  // reach past the expert's rows; it copies a clamped (real) row instead.
+  const int trow = 8 * wave + (lane >> 3);
+  const int lp = (lane & 7) ^ ((trow >> 1) & 7);
+  const char* abase = reinterpret_cast<const char*>(act);
+  // fragment reads: token row 32 j + (lane & 31), piece (2 uu + lk) ^ ((row >> 1) & 7)
+  const int lk = lane >> 5, bsw = (lane >> 1) & 7;
+  const uint32_t rd0 = (uint32_t)(lane & 31) * 128u;
 
   auto run = [&](auto jn_c) {
     constexpr int JN = decltype(jn_c)::value;
-    // Load chunk c covers tile rows 32c..32c+31.  Only the last chunk can
-    // reach past the expert's rows; it reads a clamped (real) row instead.
-    // The other chunks are this lane's row plus a uniform stride.
-    const uint32_t toff0 = ((uint32_t)(row0 + trow) * (uint32_t)K + 8u * tq) * 2u;
+    constexpr PkSched S{JN, WF, D};
+    const uint32_t toff0 = ((uint32_t)(row0 + trow) * (uint32_t)K + 8u * lp) * 2u;
     const uint32_t tofl =
-        ((uint32_t)(row0 + min(32 * (JN - 1) + trow, nrow - 1)) * (uint32_t)K + 8u * tq) * 2u;
-    const int cstride = 64 * K;  // bytes of 32 rows
-    // Half-stages past K (K % 128 == 64) re-read the last real one: their
-    // weights are zero in the packed image, so they add exact zeros.
-    const int hlast = K / 64 - 1;
-    auto load_chunk = [&](int h, int c) -> u32x4 {
-      const int hb = min(h, hlast) * 128;
-      if (c == JN - 1) return __builtin_amdgcn_raw_buffer_load_b128(arsrc, (int)tofl, hb, 0);
-      return __builtin_amdgcn_raw_buffer_load_b128(arsrc, (int)toff0, hb + c * cstride, 0);
+        ((uint32_t)(row0 + min(32 * (JN - 1) + trow, nrow - 1)) * (uint32_t)K + 8u * lp) * 2u;
+    const size_t cstride = (size_t)64 * K;  // bytes of 32 rows
+    auto copy_chunk = [&](int h, int c) {
+      const char* hb = abase + (size_t)min(h, hlast) * 128;
+      const uint32_t lds = lds0 + (uint32_t)((h % NSLOT) * HB + (32 * c + 8 * wave) * 128);
+      if (c == JN - 1)
+        dma_async(hb, tofl, lds);
+      else
+        dma_async(hb + c * cstride, toff0, lds);
     };
-    auto slot = [&](int h) -> u32x4* { return tok + (h % NSLOT) * HALF; };
+    // weight k-step s (clamped into the stream: loads past the end are re-reads)
+    const int slast = kp / 16 - 1;
+    auto wload = [&](int s, auto i_c) -> u32x4 {
+      constexpr int I = decltype(i_c)::value;
+      return wload_async<I * 1024>(wrsrc, wl, min(s, slast) * 2048 + wfrag0);
+    };
+    auto rdb = [&](int h, int uu, int j) -> u32x4 {
+      const int q = (2 * uu + lk) ^ bsw;
+      return *reinterpret_cast<const u32x4*>(tokb + (h % NSLOT) * HB + j * 4096 + rd0 + q * 16);
+    };
 
-    // Pipeline.  Half-stage h (k range [64 h, 64 h + 64)) lives in LDS slot
-    // h % NSLOT.  While the MFMAs of half-stage h run, the staged registers
-    // sg (half-stage h+2, loaded during h-1) are written to slot h+2 and sg
-    // is refilled with h+3, a quarter of the chunks per k-step, so every load
-    // has four k-steps before its LDS write.  Slot h+2 was last read during
-    // h-1 (three slots) or h-2 (four), and a barrier ends every half-stage.
-    // The B fragment of token fragment j for the next k-step is read into the
-    // same registers right after the last MFMA that uses it, so the reads of
-    // one k-step overlap the MFMAs of the one before.  Weight fragment i of
-    // k-step s+WQ is loaded into wq slot s % WQ right after its last MFMA.
-    u32x4 wq[WQ][2];
-    u32x4 sg[JN];
+    u32x4 wq[8][WF];
     u32x4 bq[JN];
-    // prologue, issued in the steady state's order: half-stages 0 and 1 (to
-    // LDS now), k-steps 0..3, then half-stage 2 interleaved with k-steps 4..7
-    u32x4 s0[JN], s1[JN];
-#pragma unroll
-    for (int c = 0; c < JN; ++c) s0[c] = load_chunk(0, c);
-#pragma unroll
-    for (int c = 0; c < JN; ++c) s1[c] = load_chunk(1, c);
+    // prologue: copies of half-stages 0..D-3, then pseudo iteration -1
+    for (int h = 0; h < D - 2; ++h)
+      static_for<JN>([&](auto c) { copy_chunk(h, c); });
+    static_for<8>([&](auto u_c) {
+      constexpr int u = decltype(u_c)::value;
+      static_for<S.nc(u & 3)>([&](auto cc) { copy_chunk(D - 2 + (u >> 2), S.cl(u & 3) + cc); });
+      wq[u][0] = wload(u, std::integral_constant<int, 0>());
+      if constexpr (WF == 2) wq[u][1] = wload(u, std::integral_constant<int, 1>());
+    });
+    wait_vm_barrier<S.x_first()>();
+    static_for<JN>([&](auto j) { bq[j] = rdb(0, 0, j); });
+    // the accumulators come to life only now
     __builtin_amdgcn_sched_barrier(0);
+    f32x16 acc[WF][JN];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) wq[u][i] = wload(u, i);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int u = 4; u < 8; ++u) {
-#pragma unroll
-      for (int c = JN * (u - 4) / 4; c < JN * (u - 3) / 4; ++c)
-        sg[c] = load_chunk(2, c);  // clamped: valid even when nit == 1
-      __builtin_amdgcn_sched_barrier(0);
-      if (u < WQ) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) wq[u][i] = wload(u, i);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int c = 0; c < JN; ++c) tok[tpos + 256 * c] = s0[c];
-#pragma unroll
-    for (int c = 0; c < JN; ++c) tok[HALF + tpos + 256 * c] = s1[c];
-    lds_barrier();
-    {
-      const int q = lk ^ bsw;
-#pragma unroll
-      for (int j = 0; j < JN; ++j) bq[j] = tok[bbase + 256 * j + q];
-    }
-    // the accumulators come to life only now, after the prologue's staging
-    // registers are dead (both together would not fit the register file)
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 acc[2][JN];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < WF; ++i)
 #pragma unroll
       for (int j = 0; j < JN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // VAR 0: full iteration; 1: the one before the last (no load of
-    // half-stage 2t+4); 2: the last (no loads, no LDS writes, no barrier).
-    auto iter = [&](int t, auto var_c) {
-      constexpr int VAR = decltype(var_c)::value;
+    // LAST = 0: full iteration; 1: the last one (issues no loads)
+    auto iter = [&](int t, auto last_c) {
+      constexpr bool LAST = decltype(last_c)::value;
       __builtin_amdgcn_sched_barrier(0);
-      static_for<kPkSteps>([&](auto u_c) {
+      static_for<8>([&](auto u_c) {
         constexpr int u = decltype(u_c)::value;
-        constexpr int ph = u >> 2, uu = u & 3;  // half of the iteration, k-step in it
-        constexpr int c_lo = JN * uu / 4, c_hi = JN * (uu + 1) / 4;
-        constexpr int n_chunk = c_hi - c_lo;
-        constexpr bool WRITE = VAR < 2;
-        constexpr bool LOAD = VAR == 0 || (VAR == 1 && ph == 0);
-        constexpr bool NEXT_B = u < 7 || VAR < 2;
-        constexpr bool WLOAD = VAR < 2 || u + WQ < kPkSteps;  // k-step s+WQ still in range
+        constexpr int ph = u >> 2, uu = u & 3;
         const int h = 2 * t + ph;
-#pragma unroll
-        for (int c = c_lo; c < c_hi; ++c) {
-          if (WRITE) slot(h + 2)[tpos + 256 * c] = sg[c];
-          if (LOAD) sg[c] = load_chunk(h + 3, c);
+        if constexpr (!LAST)
+          static_for<S.nc(uu)>([&](auto cc) { copy_chunk(h + D, S.cl(uu) + cc); });
+        if constexpr (WF == 2) {
+          wait_vm<LAST ? S.w_last(u) : S.w_full()>(wq[u][0], wq[u][1]);
+        } else {
+          wait_vm<LAST ? S.w_last(u) : S.w_full()>(wq[u][0]);
         }
-        // next k-step's B fragments: slot and piece
-        const u32x4* nb_slot = slot(u < 7 ? h + (uu == 3 ? 1 : 0) : 2 * t + 2);
-        const int nq = (2 * ((u + 1) & 3) + lk) ^ bsw;
-        // i-major MFMA order: weight fragment 0 is free after the first JN
-        // MFMAs, fragment 1 and every B fragment after their last use
+        // The next k-step's B fragments are read during this k-step's MFMAs
+        // when they are in the same half-stage; the first k-step of the next
+        // half-stage reads them after the barrier that publishes its copies.
+        constexpr bool NEXT_B = uu != 3;
+        const int hn = h;
+        constexpr int un = uu + 1;
+        if constexpr (WF == 2) {
+          // i-major: weight fragment 0 is free after the first JN MFMAs,
+          // fragment 1 and every B fragment after their last use
 #pragma unroll
-        for (int j = 0; j < JN; ++j)
-          acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wq[u % WQ][0]),
-                                                              as_bf16x8(bq[j]), acc[0][j], 0, 0, 0);
-        if (WLOAD) wq[u % WQ][0] = wload(t * kPkSteps + u + WQ, 0);
+          for (int j = 0; j < JN; ++j)
+            acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wq[u][0]),
+                                                                as_bf16x8(bq[j]), acc[0][j], 0, 0, 0);
+          if constexpr (!LAST) wq[u][0] = wload(8 * t + u + 8, std::integral_constant<int, 0>());
 #pragma unroll
-        for (int j = 0; j < JN; ++j) {
-          acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wq[u % WQ][1]),
-                                                              as_bf16x8(bq[j]), acc[1][j], 0, 0, 0);
-          if (NEXT_B) bq[j] = nb_slot[bbase + 256 * j + nq];
+          for (int j = 0; j < JN; ++j) {
+            acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wq[u][1]),
+                                                                as_bf16x8(bq[j]), acc[1][j], 0, 0, 0);
+            if (NEXT_B) bq[j] = rdb(hn, un, j);
+          }
+          if constexpr (!LAST) wq[u][1] = wload(8 * t + u + 8, std::integral_constant<int, 1>());
+        } else {
+#pragma unroll
+          for (int j = 0; j < JN; ++j) {
+            acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wq[u][0]),
+                                                                as_bf16x8(bq[j]), acc[0][j], 0, 0, 0);
+            if (NEXT_B) bq[j] = rdb(hn, un, j);
+          }
+          if constexpr (!LAST) wq[u][0] = wload(8 * t + u + 8, std::integral_constant<int, 0>());
         }
-        if (WLOAD) wq[u % WQ][1] = wload(t * kPkSteps + u + WQ, 1);
-        // Issue order: the staged LDS writes first (their loads are four
-        // k-steps old), the token loads among the first MFMAs, then each B
-        // fragment read after its last MFMA.
-        constexpr int n_dsw = WRITE ? n_chunk : 0;
-        constexpr int n_tl = LOAD ? n_chunk : 0;
-        if (n_dsw > 0) __builtin_amdgcn_sched_group_barrier(0x200, n_dsw, 0);
-        static_for<n_tl>([&](auto) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        });
-        __builtin_amdgcn_sched_group_barrier(0x008, JN - n_tl, 0);
-        if (WLOAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        // each B fragment read right after its last MFMA
+        constexpr int NMF = WF * JN;
+        if constexpr (WF == 2) __builtin_amdgcn_sched_group_barrier(0x008, JN, 0);
         static_for<JN>([&](auto) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           if (NEXT_B) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         });
-        if (WLOAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        (void)NMF;
         __builtin_amdgcn_sched_barrier(0);
-        if (uu == 3 && VAR < 2) {
-          lds_barrier();
+        if constexpr (uu == 3 && !(LAST && ph == 1)) {
+          if constexpr (!LAST)
+            wait_vm_barrier<S.x_full()>();
+          else
+            wait_vm_barrier<S.x_last()>();
+          static_for<JN>([&](auto j) { bq[j] = rdb(h + 1, 0, j); });
           __builtin_amdgcn_sched_barrier(0);
         }
       });
     };
     int t = 0;
-    for (; t + 2 < nit; ++t) iter(t, std::integral_constant<int, 0>());
-    if (nit >= 2) {
-      iter(t, std::integral_constant<int, 1>());
-      ++t;
-    }
-    iter(t, std::integral_constant<int, 2>());
+    for (; t + 1 < nit; ++t) iter(t, std::false_type());
+    iter(t, std::true_type());
+    // copies issued past the end are still in flight: drain them before the
+    // next tile reuses the ring
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // epilogue: acc[i][j][4 g + r] = C[fragment row 8 g + 4 lk + r][token lane & 31]
     const int nb = slab * TN + wave * (TN / 4);
@@ -358,7 +413,8 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_packed_kernel(
       if (p >= row_end) continue;
       uint16_t* orow = out + (size_t)p * N;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int ii = 0; ii < WF; ++ii) {
+        const int i = WF == 2 ? ii : half;  // weight fragment of the stream
         if (GATED) {
 #pragma unroll
           for (int g = 0; g < 2; ++g) {
@@ -367,7 +423,7 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_packed_kernel(
             float hv[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float gt = acc[i][j][4 * g + r], up = acc[i][j][4 * g + 8 + r];
+              const float gt = acc[ii][j][4 * g + r], up = acc[ii][j][4 * g + 8 + r];
               hv[r] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
             }
             u32x2 pk;
@@ -381,8 +437,8 @@ __global__ __launch_bounds__(256, OCC) void grouped_gemm_packed_kernel(
             const int n = nb + 32 * i + 8 * g + 4 * lk;
             if (n >= N) continue;
             u32x2 pk;
-            pk.x = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
-            pk.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+            pk.x = pack_bf16x2(acc[ii][j][4 * g], acc[ii][j][4 * g + 1]);
+            pk.y = pack_bf16x2(acc[ii][j][4 * g + 2], acc[ii][j][4 * g + 3]);
             *reinterpret_cast<u32x2*>(orow + n) = pk;
           }
         }
@@ -446,33 +502,36 @@ static int device_cus() {
   return cached[dev];
 }
 
-#ifndef PK_JMAX_GU
-#define PK_JMAX_GU 8
-#endif
-#ifndef PK_JMAX_DN
-#define PK_JMAX_DN 8
-#endif
-template <bool GATED, int JMAX>
-static hipError_t launch_packed_j(const moe_config& c, const void* act, const int32_t* offs,
+template <bool GATED, int JMAX, int WF>
+static hipError_t launch_packed_t(const moe_config& c, const void* act, const int32_t* offs,
                                   const void* wp, void* out, hipStream_t st) {
-  constexpr int OCC = JMAX <= 4 ? 2 : 1;  // blocks per CU
   const long rows = (long)c.T * c.k;
   const int N = GATED ? c.f : c.d, K = GATED ? c.d : c.f;
   const PackGeom g = pack_geom(N, K, GATED);
-  // OCC blocks per CU (never more blocks than the worst-case tile count)
-  const long worst = (long)g.slabs * worst_row_tiles(rows, c.E, 32 * JMAX);
-  const long cap = ((long)device_cus() * OCC + 7) / 8 * 8;
+  // one block per CU, never more blocks than the worst-case tile count
+  const long worst = (long)g.slabs * (WF == 2 ? 1 : 2) * worst_row_tiles(rows, c.E, 32 * JMAX);
+  const long cap = ((long)device_cus() + 7) / 8 * 8;
   const int blocks = (int)std::min(cap, (worst + 7) / 8 * 8);
-  grouped_gemm_packed_kernel<GATED, JMAX, OCC><<<blocks, 256, 0, st>>>(
+  grouped_gemm_packed_kernel<GATED, JMAX, WF><<<blocks, 256, 0, st>>>(
       static_cast<const uint16_t*>(act), offs, static_cast<const u32x4*>(wp),
       static_cast<uint16_t*>(out), c.E, N, K, (int)rows, g.slabs, 8);
   return hipGetLastError();
 }
 
+// Tile shape.  Whole-slab tiles of up to 256 rows (WF = 2, JMAX = 8) unless
+// they are too few to fill the chip twice over -- the down projection of a
+// few experts with some hundred rows each: then half-slab tiles of up to 320
+// rows (WF = 1, JMAX = 10), which double the tile count and cover an expert of
+// up to 320 rows with one tile.
 template <bool GATED>
 static hipError_t launch_packed(const moe_config& c, const void* act, const int32_t* offs,
                                 const void* wp, void* out, hipStream_t st) {
-  return launch_packed_j<GATED, GATED ? PK_JMAX_GU : PK_JMAX_DN>(c, act, offs, wp, out, st);
+  const long rows = (long)c.T * c.k;
+  const PackGeom g = pack_geom(GATED ? c.f : c.d, GATED ? c.d : c.f, GATED);
+  const long typical = (long)g.slabs * std::max<long>(c.E, (rows + 255) / 256);
+  if (typical < 2L * device_cus())
+    return launch_packed_t<GATED, 10, 1>(c, act, offs, wp, out, st);
+  return launch_packed_t<GATED, 8, 2>(c, act, offs, wp, out, st);
 }
 
 hipError_t launch_ffn_gate_up_packed(const moe_config& c, const void* x_perm, const int32_t* offs,
