@@ -1,0 +1,98 @@
+"""Static checks of the packed grouped-GEMM kernels' machine code (CPU only).
+
+The main loop loads weight fragments with asynchronous asm loads and waits for
+them with explicit counts.  The compiler treats an asm output as available as
+soon as the asm statement issues, so the code is only correct if the compiler
+never copies, spills or overwrites such a register before the explicit wait
+(only the matrix instructions after the wait may read it).  This compiles the
+kernel source to gfx950 assembly and checks exactly that."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from top_routing_expert_amd import build as Bld
+
+SRC = os.path.join(Bld.CSRC, "ffn_packed.hip")
+
+
+def _regs(tok):
+    m = re.match(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return {f"{m.group(1)}{i}" for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    return {tok} if re.match(r"[va]\d+$", tok) else set()
+
+
+def in_flight_violations(asm: str, kernel_pat: str = "gemm_packed"):
+    """(kernel, instruction) pairs that read or write a register whose async
+    asm load has not been waited for."""
+    out, body, name = [], None, None
+    for line in asm.split("\n"):
+        if re.match(r"^_Z\w*:", line) and kernel_pat in line:
+            body, name, pending, in_asm = [], line, set(), False
+            continue
+        if body is None:
+            continue
+        if "s_endpgm" in line:
+            body = None
+            continue
+        s = line.strip()
+        if s.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if s.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        ins = s.split(";")[0].strip()
+        if not ins or ins.startswith("."):
+            continue
+        op = ins.split()[0]
+        args = [a.strip() for a in ins[len(op):].split(",")]
+        if in_asm:
+            if op == "buffer_load_dwordx4" and " lds" not in ins:
+                pending |= _regs(args[0])
+            elif op == "s_waitcnt" and "vmcnt" in ins:
+                pending = set()
+            continue
+        if op == "s_waitcnt" and "vmcnt(0)" in ins:
+            pending = set()
+            continue
+        if not pending or op.startswith("v_mfma"):
+            continue
+        touched = set()
+        for a in args:
+            touched |= _regs(a.split()[0] if a else "")
+        if touched & pending:
+            out.append((name, ins))
+    return out
+
+
+def test_checker_flags_a_copy_of_an_in_flight_register():
+    asm = "\n".join([
+        "_Zgemm_packed_k:",
+        ";;#ASMSTART", "buffer_load_dwordx4 v[4:7], v1, s[0:3], s4 offen offset:0", ";;#ASMEND",
+        "v_mov_b32 v20, v5",
+        ";;#ASMSTART", "s_waitcnt vmcnt(0)", ";;#ASMEND",
+        "v_mfma_f32_32x32x16_bf16 a[0:15], v[4:7], v[8:11], a[0:15]",
+        "s_endpgm",
+    ])
+    assert len(in_flight_violations(asm)) == 1
+    ok = asm.replace("v_mov_b32 v20, v5", "v_mov_b32 v20, v9")
+    assert in_flight_violations(ok) == []
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                    reason="hipcc not available")
+def test_packed_kernel_never_touches_in_flight_weight_registers(tmp_path):
+    out = tmp_path / "ffn_packed.s"
+    cmd = [Bld._hipcc(), *Bld.HIPCC_FLAGS, "--cuda-device-only", "-S", SRC, "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    asm = out.read_text()
+    assert asm.count("buffer_load_dwordx4") > 0
+    bad = in_flight_violations(asm)
+    assert bad == [], bad[:5]
+    # no scratch: every spill would be a chance for the above
+    assert not re.search(r"\.private_segment_fixed_size:\s+[1-9]", asm)
