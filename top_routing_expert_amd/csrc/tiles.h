@@ -37,7 +37,7 @@ __device__ __forceinline__ int count_row_tiles(const int32_t* __restrict__ offs,
 // of up to `band` row tiles of TM rows, and inside a band by weight tile with
 // the row tiles fastest, so that neighbouring tiles share one expert's weight
 // rows (across row tiles) and token rows (across weight tiles).
-// Writes s_tile = {expert, first row, end row of the expert, weight tile}.
+// Writes s_tile = {expert, first row, end row, weight tile} of the tile.
 template <int TM>
 __device__ __forceinline__ void locate_tile(const int32_t* __restrict__ offs, int E, int rows,
                                             int n_tiles, int band, int L, int lane, int* s_tile) {
@@ -71,9 +71,13 @@ __device__ __forceinline__ void locate_tile(const int32_t* __restrict__ offs, in
         n = rr / gl;
         m = full * g + rr % gl;
       }
+      // the expert's rows are split evenly over its row tiles (sizes differ
+      // by at most one row): the tiles of one weight tile then run at the
+      // same pace side by side, and the second reads the weights from L2
+      const long c = o1 - o0;
       s_tile[0] = e;
-      s_tile[1] = o0 + m * TM;
-      s_tile[2] = o1;
+      s_tile[1] = o0 + (int)((long)m * c / mt);
+      s_tile[2] = o0 + (int)((long)(m + 1) * c / mt);
       s_tile[3] = n;
     }
     carry += __shfl(incl, 63);
