@@ -32,55 +32,71 @@ __device__ __forceinline__ int count_row_tiles(const int32_t* __restrict__ offs,
   return total;
 }
 
+// The tiles of one expert, located inside its own range: bands of up to
+// `band` row tiles, inside a band by weight tile with the row tiles fastest,
+// so that neighbouring tiles share the expert's weight rows (across row
+// tiles) and token rows (across weight tiles).  The expert's rows are split
+// evenly over its row tiles (sizes differ by at most one row): the tiles of
+// one weight tile then run at the same pace side by side, and the second
+// reads the weights from L2.
+__device__ __forceinline__ void expert_tile(int e, int o0, int o1, int mt, int n_tiles, int band,
+                                            int r, int* s_tile) {
+  const int g = min(band, mt);
+  const int full = mt / g;
+  int n, m;
+  if (r < full * g * n_tiles) {
+    const int bi = r / (g * n_tiles), rr = r - bi * g * n_tiles;
+    n = rr / g;
+    m = bi * g + rr % g;
+  } else {
+    const int gl = mt - full * g, rr = r - full * g * n_tiles;
+    n = rr / gl;
+    m = full * g + rr % gl;
+  }
+  const long c = o1 - o0;
+  s_tile[0] = e;
+  s_tile[1] = o0 + (int)((long)m * c / mt);
+  s_tile[2] = o0 + (int)((long)(m + 1) * c / mt);
+  s_tile[3] = n;
+}
+
 // Finds tile L (0 <= L < row tiles * n_tiles) in the tile order, called by ONE
-// whole wave.  Tiles are ordered expert by expert; inside an expert in bands
-// of up to `band` row tiles of TM rows, and inside a band by weight tile with
-// the row tiles fastest, so that neighbouring tiles share one expert's weight
-// rows (across row tiles) and token rows (across weight tiles).
+// whole wave.  Experts are taken in index order, or -- `sized` -- by the
+// 32-row fragments of their tiles, largest first (then by index): a static
+// schedule then hands out the long tiles before the short ones, so the short
+// ones even out the per-block totals at the end.  (Index order mixes tiles
+// that stream their own weights with tiles that share them through L2, which
+// spreads the HBM load evenly over a long run of tiles.)
 // Writes s_tile = {expert, first row, end row, weight tile} of the tile.
 template <int TM>
 __device__ __forceinline__ void locate_tile(const int32_t* __restrict__ offs, int E, int rows,
-                                            int n_tiles, int band, int L, int lane, int* s_tile) {
-  int carry = 0;  // tiles of the experts before this 64-expert chunk
-  for (int b0 = 0; b0 < E; b0 += 64) {
-    const int e = b0 + lane;
-    int o0 = 0, o1 = 0;
-    if (e < E) {
-      o0 = min(max(offs[e], 0), rows);
-      o1 = min(max(offs[e + 1], o0), rows);
-    }
-    const int mt = (o1 - o0 + TM - 1) / TM;
-    int incl = mt * n_tiles;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    const int excl = carry + incl - mt * n_tiles;
-    if (mt > 0 && L >= excl && L < excl + mt * n_tiles) {
-      const int r = L - excl;
-      const int g = min(band, mt);
-      const int full = mt / g;
-      int n, m;
-      if (r < full * g * n_tiles) {
-        const int bi = r / (g * n_tiles), rr = r - bi * g * n_tiles;
-        n = rr / g;
-        m = bi * g + rr % g;
-      } else {
-        const int gl = mt - full * g, rr = r - full * g * n_tiles;
-        n = rr / gl;
-        m = full * g + rr % gl;
+                                            int n_tiles, int band, int L, int lane, int* s_tile,
+                                            bool sized = false) {
+  int carry = 0;  // tiles before the current chunk of experts
+  for (int cls = sized ? TM / 32 : 0; cls >= 0; --cls) {
+    for (int b0 = 0; b0 < E; b0 += 64) {
+      const int e = b0 + lane;
+      int o0 = 0, o1 = 0;
+      if (e < E) {
+        o0 = min(max(offs[e], 0), rows);
+        o1 = min(max(offs[e + 1], o0), rows);
       }
-      // the expert's rows are split evenly over its row tiles (sizes differ
-      // by at most one row): the tiles of one weight tile then run at the
-      // same pace side by side, and the second reads the weights from L2
-      const long c = o1 - o0;
-      s_tile[0] = e;
-      s_tile[1] = o0 + (int)((long)m * c / mt);
-      s_tile[2] = o0 + (int)((long)(m + 1) * c / mt);
-      s_tile[3] = n;
+      const int mt = (o1 - o0 + TM - 1) / TM;
+      // fragments of the expert's largest tile (0 for an empty expert)
+      const int fr = mt > 0 ? ((o1 - o0 + mt - 1) / mt + 31) / 32 : 0;
+      const bool in = mt > 0 && (!sized || fr == cls);
+      const int cnt = in ? mt * n_tiles : 0;
+      int incl = cnt;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+      }
+      const int excl = carry + incl - cnt;
+      if (in && L >= excl && L < excl + cnt) expert_tile(e, o0, o1, mt, n_tiles, band, L - excl, s_tile);
+      carry += __shfl(incl, 63);
+      if (carry > L) return;  // wave-uniform: the tile is in this chunk
     }
-    carry += __shfl(incl, 63);
   }
 }
 
