@@ -29,15 +29,24 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PHASES = ("route", "permute", "ffn_gate_up", "ffn_down", "combine")
 DOMINANT = "ffn_gate_up"
 CSRC = os.path.join(ROOT, "top_routing_expert_amd", "csrc")
-# per FFN weight layout: (counter summary, kernel source it was taken on, kernel name)
+# per FFN weight layout: (counter summary, kernel sources it was taken on, kernel name)
 FFN_KERNELS = {
     "rowmajor": (os.path.join(ROOT, "profiles", "ffn_gate_up_traffic.json"),
-                 os.path.join(CSRC, "ffn.hip"),
+                 [os.path.join(CSRC, n) for n in ("ffn.hip", "tiles.h", "common.h")],
                  "grouped_gemm_bf16_kernel<gated> (moe_ffn_gate_up)"),
     "packed": (os.path.join(ROOT, "profiles", "ffn_gate_up_packed_traffic.json"),
-               os.path.join(CSRC, "ffn_packed.hip"),
+               [os.path.join(CSRC, n) for n in ("ffn_packed.hip", "tiles.h", "common.h")],
                "grouped_gemm_packed_kernel<gated> (moe_ffn_gate_up_packed)"),
 }
+
+
+def kernel_sources_sha256(paths):
+    """One hash over the kernel's source files (in the given order)."""
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def log(msg):
@@ -100,12 +109,11 @@ def measured_traffic(ffn, workload):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary, or None if there is none, it is for another workload, or the
     kernel source changed since."""
-    traffic_file, kernel_src, _ = FFN_KERNELS[ffn]
+    traffic_file, kernel_srcs, _ = FFN_KERNELS[ffn]
     try:
         with open(traffic_file) as fh:
             t = json.load(fh)
-        with open(kernel_src, "rb") as fh:
-            h = hashlib.sha256(fh.read()).hexdigest()
+        h = kernel_sources_sha256(kernel_srcs)
     except (OSError, ValueError):
         return None
     if t.get("kernel_src_sha256") != h or t.get("workload") != workload:

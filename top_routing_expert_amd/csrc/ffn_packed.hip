@@ -9,14 +9,10 @@
 //
 // Why a packed image.  For the token counts an expert sees in a layer
 // (hundreds of rows), the grouped GEMM streams every weight byte from HBM
-// once while the tokens stay in L2.  Staging the weights through LDS costs
-// LDS bandwidth on the write and on the fragment reads of every wave, and the
-// LDS ring bounds how far ahead the weight stream can run.  Packed once into
-// MFMA fragment order, the weights go straight from HBM into the registers of
-// the one wave that uses them: each wave instruction reads 1 KB of
-// consecutive bytes, and a register queue keeps 8 k-steps (16 KB per wave,
-// 64 KB per CU) in flight.  Only the tokens, shared by all four waves, pass
-// through LDS.
+// once while the tokens stay in L2.  Packed once (at load time) into MFMA
+// fragment order, the weights go straight from HBM into the registers of the
+// one wave that uses them: each wave instruction reads 1 KB of consecutive
+// bytes.  Only the tokens, shared by all four waves, pass through LDS.
 //
 // Packed image of one weight set, per expert (experts back to back):
 //   [slab][wave 0..3][k-step 0..Kp/16-1][fragment 0..1][lane 0..63][8 bf16]
@@ -32,19 +28,24 @@
 //     F..F+31 of W_down with F = 256 slab + 64 w + 32 i.
 //   Rows past the last feature are zero.
 //
-// Kernel (persistent, one block of 4 waves per CU, 256 accumulators per wave):
-//  * tile = one slab x up to 256 token rows of one expert; wave w owns two
-//    32-row weight fragments (64 rows) against all token fragments, so every
-//    weight byte is used by exactly one wave.
-//  * k loop in iterations of 128 (8 MFMA k-steps).  Weight fragments for
+// Kernel (persistent, one block of 4 waves per CU):
+//  * Tile shapes: a whole slab (wave w: weight fragments (w, 0..1), 256
+//    accumulators) x up to 256 token rows of one expert; or, when whole-slab
+//    tiles cannot fill the chip twice over, half a slab (wave w: fragment
+//    (w, half)) x up to 320 rows.  An expert's rows are split evenly over its
+//    row tiles, so the tiles of one slab run side by side and share the
+//    weight stream through L2.
+//  * k loop in iterations of 128 (8 MFMA k-steps).  Weight fragments of
 //    k-step s+8 are loaded into the register slot of k-step s right after the
-//    MFMAs that use it.  Token rows pass through a ring of four 64-wide k
-//    half-stages in LDS (rows of 128 bytes, 16-byte pieces XOR-swizzled with
-//    (row >> 1) & 7 so the 16 lanes of a 16-byte read hit 16 bank groups):
-//    each half-stage is loaded into registers one half-stage ahead and written
-//    two ahead; one barrier per half-stage.
-//  * Operands are read through buffer resources (one address register per
-//    stream); all loads are compiler-visible, so its vmcnt waits are exact.
+//    MFMAs that use it.  Token rows are copied straight from global memory
+//    into a ring of 64-wide k half-stages in LDS (four slots, three for
+//    320-row tiles), D = slots - 1 half-stages ahead; LDS rows of 128 bytes,
+//    16-byte pieces XOR-swizzled with (row >> 1) & 7 so the 16 lanes of a
+//    16-byte read hit 16 bank groups.  One barrier per half-stage.
+//  * Both streams share the in-order load counter, so the kernel issues its
+//    loads itself in a fixed order (PkSched) and waits with exact counts: a
+//    wait for a token half-stage never drains weight loads issued for later
+//    k-steps, and vice versa.
 //  * The main loop is specialised on the number of 32-token fragments that
 //    hold rows; padded token rows read a clamped (real) row and are not
 //    stored; padded k reads zeros.
