@@ -15,7 +15,8 @@ import pytest
 
 from top_routing_expert_amd import build as Bld
 
-SRC = os.path.join(Bld.CSRC, "ffn_packed.hip")
+# (source file, kernel-name substring) of every kernel with asynchronous asm loads
+ASYNC_KERNELS = [("ffn_packed.hip", "gemm_packed"), ("route.hip", "router_skinny")]
 
 
 def _regs(tok):
@@ -85,14 +86,16 @@ def test_checker_flags_a_copy_of_an_in_flight_register():
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not available")
-def test_packed_kernel_never_touches_in_flight_weight_registers(tmp_path):
-    out = tmp_path / "ffn_packed.s"
-    cmd = [Bld._hipcc(), *Bld.HIPCC_FLAGS, "--cuda-device-only", "-S", SRC, "-o", str(out)]
+@pytest.mark.parametrize("src,kernel", ASYNC_KERNELS, ids=[k for _, k in ASYNC_KERNELS])
+def test_kernel_never_touches_in_flight_load_registers(tmp_path, src, kernel):
+    out = tmp_path / (src + ".s")
+    cmd = [Bld._hipcc(), *Bld.HIPCC_FLAGS, "--cuda-device-only", "-S",
+           os.path.join(Bld.CSRC, src), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     asm = out.read_text()
     assert asm.count("buffer_load_dwordx4") > 0
-    bad = in_flight_violations(asm)
+    bad = in_flight_violations(asm, kernel)
     assert bad == [], bad[:5]
     # no scratch: every spill would be a chance for the above
     assert not re.search(r"\.private_segment_fixed_size:\s+[1-9]", asm)

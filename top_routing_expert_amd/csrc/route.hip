@@ -6,7 +6,8 @@
 // section (experts chosen only within the best groups/nodes).
 //
 // gfx950 design
-//  * Gate GEMM (bf16): MFMA 16x16x32, experts on the M side (A operand, staged
+//  * Gate GEMM (bf16), E <= 16: a stream over x, see router_skinny_bf16_kernel.
+//  * Gate GEMM (bf16), E > 16: MFMA 16x16x32, experts on the M side (A operand, staged
 //    through LDS per 64-wide K chunk), tokens on the N side (B operand, read
 //    straight from HBM into registers: every x row is used by exactly one
 //    wave, so it never needs LDS).  A block is 4 waves x 16 tokens and up to
@@ -21,6 +22,8 @@
 #include "common.h"
 
 namespace moe {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // ============================================================== gate GEMM bf16
 // One K chunk = 64 bf16 of every row.  Inside a chunk lane group g = lane/16
@@ -123,8 +126,134 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(const uint16_t* _
   }
 }
 
+// ======================================================= gate GEMM bf16, E <= 16
+// Few experts: the GEMM is a stream over x with E flop per byte.  MFMA
+// 16x16x32 with the experts on the A side (rows past E repeat the last expert
+// and are not stored) and the 16 tokens of a wave on the B side.
+//  * x is read in whole 128-byte lines: one load covers 8 token rows x 128 B
+//    (64 k), two loads a wave's 16 rows.  (The B-operand layout itself would
+//    read 64 B of 16 rows per load; those half-line steps measured 30 % slower
+//    on the T16384-d5120 router.)  Each wave writes its two loads to a
+//    private 2 KB LDS tile (16-byte pieces swizzled by (row >> 1) & 7, so
+//    neither the row-wise writes nor the column-wise fragment reads conflict)
+//    and reads back the B fragments of the two MFMAs of the 64 k.
+//  * The A fragments (Wr, a few hundred KB, L1/L2-resident) are loaded in
+//    MFMA layout.  Lane group g = lane/16 takes piece 4h + g of the 64 k for
+//    MFMA h on both operands, so the products pair up whatever the hardware's
+//    k order inside one MFMA is.
+//  * Loads run kSkinnyDepth k-pairs ahead; no barriers (a wave reads only its
+//    own LDS tile).
+constexpr int kSkinnyDepth = 6;
+
+// Raw buffer resource over `bytes` bytes (word 3: raw, untyped, gfx950).
+__device__ __forceinline__ i32x4 router_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane; issued and waited for explicitly (see below).
+__device__ __forceinline__ u32x4 rload_async(i32x4 rsrc, uint32_t voff, int soff) {
+  u32x4 v;
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen" : "=v"(v) : "v"(voff), "s"(rsrc), "s"(soff));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ void rwait4(u32x4& a, u32x4& b, u32x4& c, u32x4& d) {
+  asm volatile("s_waitcnt vmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
+}
+
+__global__ __launch_bounds__(256) void router_skinny_bf16_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ wr,
+                                                                 float* __restrict__ dst, int T,
+                                                                 int d, int E, int splits) {
+  constexpr int P = kSkinnyDepth;
+  __shared__ u32x4 tile[4][128];  // per wave: 16 rows x 8 pieces
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tok0 = (blockIdx.x * 4 + wave) * 16;
+  const int nkp = d >> 6;  // k-pairs of 64
+  const int kb = (int)((long)blockIdx.y * nkp / splits);
+  const int ke = (int)((long)(blockIdx.y + 1) * nkp / splits);
+  // T * d and E * d are < 2^31 elements (checked by the C ABI): byte offsets fit 32 bits
+  const i32x4 xs = router_rsrc(x, (uint32_t)T * (uint32_t)d * 2u);
+  const i32x4 ws = router_rsrc(wr, (uint32_t)E * (uint32_t)d * 2u);
+  const int lr = lane >> 3, lp = lane & 7;  // x load: row lr (+8), piece lp of the 128 B
+  const uint32_t xo0 = ((uint32_t)min(tok0 + lr, T - 1) * (uint32_t)d + 8u * lp) * 2u;
+  const uint32_t xo1 = ((uint32_t)min(tok0 + 8 + lr, T - 1) * (uint32_t)d + 8u * lp) * 2u;
+  const uint32_t wo = ((uint32_t)min(lane & 15, E - 1) * (uint32_t)d + 8u * (lane >> 4)) * 2u;
+  // LDS: row r, logical piece q at r * 8 + (q ^ ((r >> 1) & 7))
+  u32x4* t = tile[wave];
+  const int wr0 = lr * 8 + (lp ^ ((lr >> 1) & 7));
+  const int wr1 = (lr + 8) * 8 + (lp ^ (((lr + 8) >> 1) & 7));
+  const int fr = lane & 15, fg = lane >> 4;
+  const int rd0 = fr * 8 + ((fg) ^ ((fr >> 1) & 7));      // piece 0 * 4 + g
+  const int rd1 = fr * 8 + ((4 + fg) ^ ((fr >> 1) & 7));  // piece 1 * 4 + g
+
+  // Every k-pair issues exactly four loads (x rows 0-7, x rows 8-15, Wr for
+  // MFMA 0, Wr for MFMA 1) for the pair P ahead -- past the end they re-read
+  // the last pair -- so the wait for pair j leaves the 4 (P - 1) younger
+  // loads in flight.  Asm loads with explicit waits: compiler-placed waits
+  // drained the counter at every loop iteration.
+  u32x4 xa[P], xb[P], w0[P], w1[P];
+  auto issue = [&](int i, int j) {
+    xa[i] = rload_async(xs, xo0, j * 128);
+    xb[i] = rload_async(xs, xo1, j * 128);
+    w0[i] = rload_async(ws, wo, j * 128);
+    w1[i] = rload_async(ws, wo, j * 128 + 64);
+  };
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto consume = [&](int i) {
+    t[wr0] = xa[i];
+    t[wr1] = xb[i];
+    const u32x4 b0 = t[rd0], b1 = t[rd1];
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w0[i]), as_bf16x8(b0), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w1[i]), as_bf16x8(b1), acc, 0, 0, 0);
+  };
+#pragma unroll
+  for (int i = 0; i < P; ++i) issue(i, min(kb + i, ke - 1));
+  int j0 = kb;
+  for (; j0 + P <= ke; j0 += P) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      rwait4<4 * P - 4>(xa[i], xb[i], w0[i], w1[i]);
+      consume(i);
+      issue(i, min(j0 + i + P, ke - 1));
+    }
+  }
+  // the last ke - j0 < P pairs are in slots 0 ..; nothing else is in flight after
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    rwait4<0>(xa[i], xb[i], w0[i], w1[i]);
+    if (j0 + i < ke) consume(i);
+  }
+  // acc[i] = z[token tok0 + (lane & 15)][expert 4 (lane >> 4) + i]
+  const int tok = tok0 + (lane & 15);
+  if (tok < T) {
+    float* drow = dst + ((size_t)blockIdx.y * T + tok) * E;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * (lane >> 4) + i;
+      if (e < E) drow[e] = acc[i];
+    }
+  }
+}
+
+// Split-K factor: enough blocks to cover the CUs (twice for the skinny kernel,
+// whose blocks are latency-bound streams).  Partial logits are summed by the
+// top-k kernel in split order, so the logits stay bitwise reproducible.
 int router_splits(const moe_config& c) {
   if (c.dtype != MOE_BF16 || c.T == 0) return 1;
+  if (c.E <= 16) {
+    const long tiles = div_up(c.T, 64);
+    long s = (512 + tiles - 1) / tiles;
+    if (s > 16) s = 16;
+    if (s > c.d / 64) s = c.d / 64;  // at least one k-pair per split
+    return (int)(s < 1 ? 1 : s);
+  }
   const int nch = c.d / 64;
   const int ec = c.E <= 16 ? 16 : c.E <= 32 ? 32 : c.E <= 64 ? 64 : c.E <= 128 ? 128 : 256;
   const long tiles = (long)div_up(c.T, 64) * div_up(c.E, ec);
@@ -137,6 +266,11 @@ int router_splits(const moe_config& c) {
 
 hipError_t launch_router_gemm_bf16(const uint16_t* x, const uint16_t* wr, float* dst, int T, int d,
                                    int E, int splits, hipStream_t st) {
+  if (E <= 16) {
+    router_skinny_bf16_kernel<<<dim3(div_up(T, 64), splits), 256, 0, st>>>(x, wr, dst, T, d, E,
+                                                                           splits);
+    return hipGetLastError();
+  }
   const int ec = E <= 16 ? 16 : E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256;
   dim3 grid(div_up(T, 64), splits, div_up(E, ec));
   switch (ec) {
