@@ -257,7 +257,10 @@ int router_splits(const moe_config& c) {
   const int nch = c.d / 64;
   const int ec = c.E <= 16 ? 16 : c.E <= 32 ? 32 : c.E <= 64 ? 64 : c.E <= 128 ? 128 : 256;
   const long tiles = (long)div_up(c.T, 64) * div_up(c.E, ec);
-  long s = (1024 + tiles - 1) / tiles;
+  // blocks to aim for: each split adds T x E fp32 partials that the top-k
+  // kernel reads back (measured best: 256 for E <= 64, 512 for E = 256)
+  const long target = c.E <= 64 ? 256 : 512;
+  long s = (target + tiles - 1) / tiles;
   if (s > 16) s = 16;
   if (s > nch) s = nch;
   if (s < 1) s = 1;
