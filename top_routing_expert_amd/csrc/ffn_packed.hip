@@ -200,6 +200,13 @@ struct PkSched {
   constexpr int x_last() const { return WF + (D - 2) * (JN + 4 * WF); }  // first half of the last iteration
   // before the first barrier, loads issued after half-stage 0's copies
   constexpr int x_first() const { return D >= 3 ? 2 * JN + 8 * WF : WF + JN + 4 * WF; }
+  // Early publication (D = 3): the end of half-stage h waits for the copies
+  // of h + 2, so that the B fragments of h + 1's first k-step can be read
+  // before that barrier; the loads issued after the last copy of h + 2 (at
+  // k-step 3 of half-stage h - 1) are the rest of that k-step and half-stage h.
+  constexpr int x_full_early() const { return WF + (D - 2) * (JN + 4 * WF); }
+  // before the first barrier: after half-stage 1's copies (pseudo iteration, first half)
+  constexpr int x_first_early() const { return JN + 5 * WF; }
 };
 
 // JMAX: 32-token fragments per tile (tile = 32 JMAX tokens); WF: 32-row
@@ -323,7 +330,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       wq[u][0] = wload(u, std::integral_constant<int, 0>());
       if constexpr (WF == 2) wq[u][1] = wload(u, std::integral_constant<int, 1>());
     });
-    wait_vm_barrier<S.x_first()>();
+    // With D = 3 every half-stage is published one half-stage before it is
+    // read (so the B fragments of a half-stage's first k-step can be read
+    // during the last k-step of the one before); with the three-slot ring
+    // (D = 2) the copies of h + 1 can only be awaited at the end of h.
+    constexpr bool EARLY = D >= 3;
+    if constexpr (EARLY)
+      wait_vm_barrier<S.x_first_early()>();
+    else
+      wait_vm_barrier<S.x_first()>();
     static_for<JN>([&](auto j) { bq[j] = rdb(0, 0, j); });
     // the accumulators come to life only now
     __builtin_amdgcn_sched_barrier(0);
@@ -351,11 +366,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
           wait_vm<LAST ? S.w_last(u) : S.w_full()>(wq[u][0]);
         }
         // The next k-step's B fragments are read during this k-step's MFMAs
-        // when they are in the same half-stage; the first k-step of the next
-        // half-stage reads them after the barrier that publishes its copies.
-        constexpr bool NEXT_B = uu != 3;
-        const int hn = h;
-        constexpr int un = uu + 1;
+        // (EARLY), or -- D = 2 -- for the first k-step of the next half-stage
+        // after the barrier that publishes its copies.
+        constexpr bool NEXT_B = EARLY ? !(LAST && u == 7) : uu != 3;
+        const int hn = uu == 3 ? h + 1 : h;
+        constexpr int un = (uu + 1) & 3;
         if constexpr (WF == 2) {
           // i-major: weight fragment 0 is free after the first JN MFMAs,
           // fragment 1 and every B fragment after their last use
@@ -389,7 +404,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
         });
         (void)NMF;
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (uu == 3 && !(LAST && ph == 1)) {
+        if constexpr (EARLY) {
+          // publish half-stage h + 2 (the last iteration has nothing left to publish)
+          if constexpr (uu == 3 && !LAST) {
+            wait_vm_barrier<S.x_full_early()>();
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else if constexpr (uu == 3 && !(LAST && ph == 1)) {
           if constexpr (!LAST)
             wait_vm_barrier<S.x_full()>();
           else
