@@ -32,9 +32,11 @@
 //  * Tile shapes: a whole slab (wave w: weight fragments (w, 0..1), 256
 //    accumulators) x up to 256 token rows of one expert; or, when whole-slab
 //    tiles cannot fill the chip twice over, half a slab (wave w: fragment
-//    (w, half)) x up to 320 rows.  An expert's rows are split evenly over its
-//    row tiles, so the tiles of one slab run side by side and share the
-//    weight stream through L2.
+//    (w, half)) x up to 320 rows.  Half-slab tiles of more than 160 rows run
+//    the waves as a 2 x 2 grid (two weight fragments x half the token
+//    fragments each), so every token fragment read from LDS feeds two MFMAs.
+//    An expert's rows are split evenly over its row tiles, so the tiles of
+//    one slab run side by side and share the weight stream through L2.
 //  * k loop in iterations of 128 (8 MFMA k-steps).  Weight fragments of
 //    k-step s+8 are loaded into the register slot of k-step s right after the
 //    MFMAs that use it.  Token rows are copied straight from global memory
@@ -171,42 +173,67 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Wait until at most N loads are in flight, then barrier, leaving this wave's
+// LDS reads in flight: for a barrier after which only slots that no read in
+// flight targets are refilled.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier_reads_in_flight() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 // Load schedule of the main loop (compile-time).  k-step s = 8 t + u of
 // iteration t, half-stage h = 2 t + (u >> 2), uu = u & 3.  Every k-step of a
-// FULL iteration issues, in this order: the token copies of chunks
-// [cl(uu), cl(uu+1)) of half-stage h + D, its wait for weight k-step s, the
-// MFMAs, and WF weight loads of k-step s + 8 (the last one at its end).  The
-// last iteration issues nothing.  The prologue issues the copies of
-// half-stages 0..D-3 and then a pseudo iteration -1 in the FULL pattern, so
-// the counts below hold from the first k-step on.  Loads past the end of the
-// tile read clamped (real) addresses and land in slots nobody reads.
+// FULL iteration starts with its wait for weight k-step s and then issues,
+// spread over its MFMAs so that the four waves never queue a burst of loads
+// at the texture unit at once: the token copies of chunks [cl(uu), cl(uu+1))
+// of half-stage h + D (the first na(uu) of them, "A", and the rest, "B") and
+// WL weight loads of k-step s + 8, in the order A, w0, B, w1 (WL = 2) or A,
+// B, w0 (WL = 1).  The last iteration issues nothing.  The prologue issues
+// the copies of half-stages 0..D-3 and then a pseudo iteration -1 in the FULL
+// order, so the counts below hold from the first k-step on.  Loads past the
+// end of the tile read clamped (real) addresses and land in slots nobody
+// reads.  The last copy of every half-stage is issued in its k-step uu = 3.
 struct PkSched {
-  int JN, WF, D;
+  int JN, WL, D;
   constexpr int cl(int uu) const { return JN * uu / 4; }  // first chunk copied at k-step uu
   constexpr int nc(int uu) const { return cl(uu + 1) - cl(uu); }
-  // loads issued after weight k-step s (issued at the end of k-step s - 8)
-  // up to the wait at the start of k-step s, s in a FULL iteration
-  constexpr int w_full() const { return 2 * JN + 7 * WF; }
+  constexpr int na(int uu) const { return (nc(uu) + 1) / 2; }
+  constexpr int nb(int uu) const { return nc(uu) - na(uu); }
+  // loads issued after the last copy of k-step uu = 3 in that k-step
+  constexpr int tail3() const { return WL == 2 && nb(3) == 0 ? 2 : 1; }
+  // loads issued after weight k-step s (the last load of k-step s - 8) up to
+  // the wait at the start of k-step s: k-steps s-7 .. s-1, s in a FULL iteration
+  constexpr int w_full(int u) const { return 7 * WL + 2 * JN - nc(u & 3); }
   // the same in the last iteration (no loads of its own), k-step u of it
   constexpr int w_last(int u) const {
     int n = 0;
-    for (int k = u + 1; k < 8; ++k) n += nc(k & 3) + WF;
+    for (int k = u + 1; k < 8; ++k) n += nc(k & 3) + WL;
     return n;
   }
-  // at the end of half-stage h (before the first read of half-stage h + 1),
-  // loads issued after the last copy of half-stage h + 1 (issued at k-step 3
-  // of half-stage h + 1 - D)
-  constexpr int x_full() const { return WF + (D - 1) * (JN + 4 * WF); }
-  constexpr int x_last() const { return WF + (D - 2) * (JN + 4 * WF); }  // first half of the last iteration
-  // before the first barrier, loads issued after half-stage 0's copies
-  constexpr int x_first() const { return D >= 3 ? 2 * JN + 8 * WF : WF + JN + 4 * WF; }
-  // Early publication (D = 3): the end of half-stage h waits for the copies
+  // D = 2: at the end of half-stage h, loads issued after the last copy of
+  // half-stage h + 1 (k-step 3 of half-stage h - 1): the rest of that k-step
+  // and half-stage h -- or, in the first half of the last iteration, nothing
+  // more; before the first barrier, after half-stage 0's last copy
+  constexpr int x_full() const { return tail3() + (D - 1) * (JN + 4 * WL); }
+  constexpr int x_last() const { return tail3() + (D - 2) * (JN + 4 * WL); }
+  constexpr int x_first() const { return tail3() + JN + 4 * WL; }
+  // D = 3 (early publication): the end of half-stage h waits for the copies
   // of h + 2, so that the B fragments of h + 1's first k-step can be read
-  // before that barrier; the loads issued after the last copy of h + 2 (at
-  // k-step 3 of half-stage h - 1) are the rest of that k-step and half-stage h.
-  constexpr int x_full_early() const { return WF + (D - 2) * (JN + 4 * WF); }
-  // before the first barrier: after half-stage 1's copies (pseudo iteration, first half)
-  constexpr int x_first_early() const { return JN + 5 * WF; }
+  // before that barrier; their last copy was issued at k-step 3 of half-stage
+  // h - 1.  Before the first barrier: after half-stage 1's last copy (pseudo
+  // iteration, first half).
+  constexpr int x_full_early() const { return tail3() + (D - 2) * (JN + 4 * WL); }
+  constexpr int x_first_early() const { return tail3() + JN + 4 * WL; }
+};
+
+// Specialisation of a tile of J live token fragments: the fragment count
+// (at most JMAX) and whether its waves run as 2 x 2 pairs (half-slab tiles of
+// more than JMAX / 2 fragments).
+template <int J, int JMAX, int WF>
+struct JnSel {
+  static constexpr int jn = J < JMAX ? J : JMAX;
+  using N = std::integral_constant<int, jn>;
+  using P = std::integral_constant<bool, (WF == 1 && 2 * jn > JMAX)>;
 };
 
 // JMAX: 32-token fragments per tile (tile = 32 JMAX tokens); WF: 32-row
@@ -270,13 +297,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
   const int nit = kp / kPkIterK;
   const int hlast = K / 64 - 1;  // half-stages past K re-read the last real one (zero weights)
 
-  // This wave's weight stream as a buffer resource; fragment i of k-step s is
-  // at s * 2048 + i * 1024 (WF = 1 tiles take fragment `half` of each stream).
-  const i32x4 wrsrc = make_rsrc(
-      wp + (((size_t)e * slabs + slab) * 4 + wave) * ((size_t)(kp / 16) * 128),
-      (uint32_t)(kp / 16) * 2048u);
   const uint32_t wl = (uint32_t)lane * 16u;
-  const int wfrag0 = WF == 2 ? 0 : half * 1024;
+  const uint32_t sbytes = (uint32_t)(kp / 16) * 2048u;  // one packed weight stream
 
   // Token copies.  Half-stage h = k range [64 h, 64 h + 64) of the tile's rows,
   // in LDS slot h % NSLOT: rows of 128 bytes, the 16-byte piece q of row r at
@@ -293,9 +315,30 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
   const int lk = lane >> 5, bsw = (lane >> 1) & 7;
   const uint32_t rd0 = (uint32_t)(lane & 31) * 128u;
 
-  auto run = [&](auto jn_c) {
+  // PAIR (half-slab tiles of more than JMAX / 2 fragments): the waves form a
+  // 2 x 2 grid, wave 2a + b computing the slab's fragments `half` of packed
+  // streams 2a and 2a + 1 on token fragments [b JW, b JW + JW), so that every
+  // token fragment read from LDS feeds two MFMAs.  Otherwise wave w computes
+  // its own stream's fragments (both, or `half`) on every token fragment.
+  auto run = [&](auto jn_c, auto pair_c) {
     constexpr int JN = decltype(jn_c)::value;
-    constexpr PkSched S{JN, WF, D};
+    constexpr bool PAIR = decltype(pair_c)::value;
+    constexpr int WL = PAIR ? 2 : WF;              // weight fragments of this wave
+    constexpr int JW = PAIR ? (JN + 1) / 2 : JN;  // token fragments of this wave
+    const int jb = PAIR ? (wave & 1) * JW : 0;
+    // With JN odd the second pair's last fragment (JN) lies past the tile's
+    // rows; it reads stale LDS rows of the slot and is never stored.
+    const int pw = PAIR ? (wave & ~1) : wave;      // first packed stream of this wave
+    static_assert(!PAIR || JN % 2 == 0 || JN < JMAX, "fragment JN must lie inside the slot");
+    static_assert(D == 2 || D == 3, "ring depth");
+    constexpr PkSched S{JN, WL, D};
+    // The wave's weight stream(s) as one buffer resource: fragment i of
+    // k-step s of stream pw + q at q * sbytes + s * 2048 + i * 1024.
+    const i32x4 wrsrc =
+        make_rsrc(wp + (((size_t)e * slabs + slab) * 4 + pw) * ((size_t)(kp / 16) * 128),
+                  (PAIR ? 2u : 1u) * sbytes);
+    const uint32_t wl1 = wl + (PAIR ? sbytes : 0u);
+    const int wfrag0 = WF == 2 ? 0 : half * 1024;
     const uint32_t toff0 = ((uint32_t)(row0 + trow) * (uint32_t)K + 8u * lp) * 2u;
     const uint32_t tofl =
         ((uint32_t)(row0 + min(32 * (JN - 1) + trow, nrow - 1)) * (uint32_t)K + 8u * lp) * 2u;
@@ -312,23 +355,28 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     const int slast = kp / 16 - 1;
     auto wload = [&](int s, auto i_c) -> u32x4 {
       constexpr int I = decltype(i_c)::value;
-      return wload_async<I * 1024>(wrsrc, wl, min(s, slast) * 2048 + wfrag0);
+      if constexpr (PAIR)
+        return wload_async<0>(wrsrc, I ? wl1 : wl, min(s, slast) * 2048 + wfrag0);
+      else
+        return wload_async<I * 1024>(wrsrc, wl, min(s, slast) * 2048 + wfrag0);
     };
     auto rdb = [&](int h, int uu, int j) -> u32x4 {
       const int q = (2 * uu + lk) ^ bsw;
       return *reinterpret_cast<const u32x4*>(tokb + (h % NSLOT) * HB + j * 4096 + rd0 + q * 16);
     };
 
-    u32x4 wq[8][WF];
-    u32x4 bq[JN];
+    u32x4 wq[8][WL];
+    u32x4 bq[JW];
     // prologue: copies of half-stages 0..D-3, then pseudo iteration -1
     for (int h = 0; h < D - 2; ++h)
       static_for<JN>([&](auto c) { copy_chunk(h, c); });
     static_for<8>([&](auto u_c) {
-      constexpr int u = decltype(u_c)::value;
-      static_for<S.nc(u & 3)>([&](auto cc) { copy_chunk(D - 2 + (u >> 2), S.cl(u & 3) + cc); });
-      wq[u][0] = wload(u, std::integral_constant<int, 0>());
-      if constexpr (WF == 2) wq[u][1] = wload(u, std::integral_constant<int, 1>());
+      constexpr int u = decltype(u_c)::value, uu = u & 3;
+      // the order of a FULL k-step: A, w0, B, w1 or A, B, w0
+      static_for<S.na(uu)>([&](auto cc) { copy_chunk(D - 2 + (u >> 2), S.cl(uu) + cc); });
+      if constexpr (WL == 2) wq[u][0] = wload(u, std::integral_constant<int, 0>());
+      static_for<S.nb(uu)>([&](auto cc) { copy_chunk(D - 2 + (u >> 2), S.cl(uu) + S.na(uu) + cc); });
+      wq[u][WL - 1] = wload(u, std::integral_constant<int, WL - 1>());
     });
     // With D = 3 every half-stage is published one half-stage before it is
     // read (so the B fragments of a half-stage's first k-step can be read
@@ -339,14 +387,14 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       wait_vm_barrier<S.x_first_early()>();
     else
       wait_vm_barrier<S.x_first()>();
-    static_for<JN>([&](auto j) { bq[j] = rdb(0, 0, j); });
+    static_for<JW>([&](auto j) { bq[j] = rdb(0, 0, jb + j); });
     // the accumulators come to life only now
     __builtin_amdgcn_sched_barrier(0);
-    f32x16 acc[WF][JN];
+    f32x16 acc[WL][JW];
 #pragma unroll
-    for (int i = 0; i < WF; ++i)
+    for (int i = 0; i < WL; ++i)
 #pragma unroll
-      for (int j = 0; j < JN; ++j)
+      for (int j = 0; j < JW; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -358,12 +406,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
         constexpr int u = decltype(u_c)::value;
         constexpr int ph = u >> 2, uu = u & 3;
         const int h = 2 * t + ph;
-        if constexpr (!LAST)
-          static_for<S.nc(uu)>([&](auto cc) { copy_chunk(h + D, S.cl(uu) + cc); });
-        if constexpr (WF == 2) {
-          wait_vm<LAST ? S.w_last(u) : S.w_full()>(wq[u][0], wq[u][1]);
+        if constexpr (WL == 2) {
+          wait_vm<LAST ? S.w_last(u) : S.w_full(u)>(wq[u][0], wq[u][1]);
         } else {
-          wait_vm<LAST ? S.w_last(u) : S.w_full()>(wq[u][0]);
+          wait_vm<LAST ? S.w_last(u) : S.w_full(u)>(wq[u][0]);
         }
         // The next k-step's B fragments are read during this k-step's MFMAs
         // (EARLY), or -- D = 2 -- for the first k-step of the next half-stage
@@ -371,43 +417,70 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
         constexpr bool NEXT_B = EARLY ? !(LAST && u == 7) : uu != 3;
         const int hn = uu == 3 ? h + 1 : h;
         constexpr int un = (uu + 1) & 3;
-        if constexpr (WF == 2) {
-          // i-major: weight fragment 0 is free after the first JN MFMAs,
-          // fragment 1 and every B fragment after their last use
-#pragma unroll
-          for (int j = 0; j < JN; ++j)
-            acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wq[u][0]),
-                                                                as_bf16x8(bq[j]), acc[0][j], 0, 0, 0);
-          if constexpr (!LAST) wq[u][0] = wload(8 * t + u + 8, std::integral_constant<int, 0>());
-#pragma unroll
-          for (int j = 0; j < JN; ++j) {
-            acc[1][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wq[u][1]),
-                                                                as_bf16x8(bq[j]), acc[1][j], 0, 0, 0);
-            if (NEXT_B) bq[j] = rdb(hn, un, j);
+        // MFMAs of weight fragment I on token fragments [J0, J1), each B
+        // fragment read again right after its last MFMA of the k-step
+        auto mf = [&](auto i_c, auto j0_c, auto j1_c) {
+          constexpr int I = decltype(i_c)::value, J0 = decltype(j0_c)::value;
+          constexpr int J1 = decltype(j1_c)::value;
+          constexpr bool RD = NEXT_B && I == WL - 1;
+          static_for<J1 - J0>([&](auto jj) {
+            constexpr int j = J0 + decltype(jj)::value;
+            acc[I][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wq[u][I]),
+                                                                as_bf16x8(bq[j]), acc[I][j], 0, 0, 0);
+            if constexpr (RD) bq[j] = rdb(hn, un, jb + j);
+          });
+          static_for<J1 - J0>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if constexpr (RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        // token copies of chunks [C0, C0 + NCP) of half-stage h + D
+        auto copies = [&](auto c0_c, auto n_c) {
+          if constexpr (!LAST) {
+            static_for<decltype(n_c)::value>(
+                [&](auto cc) { copy_chunk(h + D, decltype(c0_c)::value + cc); });
+            __builtin_amdgcn_sched_barrier(0);
           }
-          if constexpr (!LAST) wq[u][1] = wload(8 * t + u + 8, std::integral_constant<int, 1>());
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using CA = std::integral_constant<int, S.cl(uu)>;
+        using NA = std::integral_constant<int, S.na(uu)>;
+        using CB = std::integral_constant<int, S.cl(uu) + S.na(uu)>;
+        using NB = std::integral_constant<int, S.nb(uu)>;
+        using JE = std::integral_constant<int, JW>;
+        if constexpr (WL == 2) {
+          // i-major: weight fragment 0 is free after the first JW MFMAs,
+          // fragment 1 after the last; the copies sit halfway through each half
+          using PA = std::integral_constant<int, (JW / 2 > 1 ? JW / 2 : 1)>;
+          mf(I0(), I0(), PA());
+          copies(CA(), NA());
+          mf(I0(), PA(), JE());
+          if constexpr (!LAST) wq[u][0] = wload(8 * t + u + 8, I0());
+          __builtin_amdgcn_sched_barrier(0);
+          mf(I1(), I0(), PA());
+          copies(CB(), NB());
+          mf(I1(), PA(), JE());
+          if constexpr (!LAST) wq[u][1] = wload(8 * t + u + 8, I1());
         } else {
-#pragma unroll
-          for (int j = 0; j < JN; ++j) {
-            acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wq[u][0]),
-                                                                as_bf16x8(bq[j]), acc[0][j], 0, 0, 0);
-            if (NEXT_B) bq[j] = rdb(hn, un, j);
-          }
-          if constexpr (!LAST) wq[u][0] = wload(8 * t + u + 8, std::integral_constant<int, 0>());
+          using PA = std::integral_constant<int, (JW / 3 > 1 ? JW / 3 : 1)>;
+          using PB = std::integral_constant<int, (2 * JW / 3 > PA::value ? 2 * JW / 3 : PA::value)>;
+          mf(I0(), I0(), PA());
+          copies(CA(), NA());
+          mf(I0(), PA(), PB());
+          copies(CB(), NB());
+          mf(I0(), PB(), JE());
+          if constexpr (!LAST) wq[u][0] = wload(8 * t + u + 8, I0());
         }
-        // each B fragment read right after its last MFMA
-        constexpr int NMF = WF * JN;
-        if constexpr (WF == 2) __builtin_amdgcn_sched_group_barrier(0x008, JN, 0);
-        static_for<JN>([&](auto) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (NEXT_B) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        });
-        (void)NMF;
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (EARLY) {
-          // publish half-stage h + 2 (the last iteration has nothing left to publish)
+          // publish half-stage h + 2 (the last iteration has nothing left to
+          // publish).  The reads in flight here are of half-stage h + 1; the
+          // copies issued after this barrier refill slot h, whose reads were
+          // all consumed by this half-stage's MFMAs.
           if constexpr (uu == 3 && !LAST) {
-            wait_vm_barrier<S.x_full_early()>();
+            wait_vm_barrier_reads_in_flight<S.x_full_early()>();
             __builtin_amdgcn_sched_barrier(0);
           }
         } else if constexpr (uu == 3 && !(LAST && ph == 1)) {
@@ -415,7 +488,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
             wait_vm_barrier<S.x_full()>();
           else
             wait_vm_barrier<S.x_last()>();
-          static_for<JN>([&](auto j) { bq[j] = rdb(h + 1, 0, j); });
+          static_for<JW>([&](auto j) { bq[j] = rdb(h + 1, 0, jb + j); });
           __builtin_amdgcn_sched_barrier(0);
         }
       });
@@ -427,16 +500,16 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     // next tile reuses the ring
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // epilogue: acc[i][j][4 g + r] = C[fragment row 8 g + 4 lk + r][token lane & 31]
-    const int nb = slab * TN + wave * (TN / 4);
+    // epilogue: acc[ii][jj][4 g + r] = C[fragment row 8 g + 4 lk + r][token lane & 31]
 #pragma unroll
-    for (int j = 0; j < JN; ++j) {
-      const int p = row0 + 32 * j + (lane & 31);
+    for (int jj = 0; jj < JW; ++jj) {
+      const int p = row0 + 32 * (jb + jj) + (lane & 31);
       if (p >= row_end) continue;
       uint16_t* orow = out + (size_t)p * N;
 #pragma unroll
-      for (int ii = 0; ii < WF; ++ii) {
+      for (int ii = 0; ii < WL; ++ii) {
         const int i = WF == 2 ? ii : half;  // weight fragment of the stream
+        const int nb = slab * TN + (PAIR ? pw + ii : wave) * (TN / 4);
         if (GATED) {
 #pragma unroll
           for (int g = 0; g < 2; ++g) {
@@ -445,7 +518,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
             float hv[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float gt = acc[ii][j][4 * g + r], up = acc[ii][j][4 * g + 8 + r];
+              const float gt = acc[ii][jj][4 * g + r], up = acc[ii][jj][4 * g + 8 + r];
               hv[r] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
             }
             u32x2 pk;
@@ -459,25 +532,27 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
             const int n = nb + 32 * i + 8 * g + 4 * lk;
             if (n >= N) continue;
             u32x2 pk;
-            pk.x = pack_bf16x2(acc[ii][j][4 * g], acc[ii][j][4 * g + 1]);
-            pk.y = pack_bf16x2(acc[ii][j][4 * g + 2], acc[ii][j][4 * g + 3]);
+            pk.x = pack_bf16x2(acc[ii][jj][4 * g], acc[ii][jj][4 * g + 1]);
+            pk.y = pack_bf16x2(acc[ii][jj][4 * g + 2], acc[ii][jj][4 * g + 3]);
             *reinterpret_cast<u32x2*>(orow + n) = pk;
           }
         }
       }
     }
   };
+  // (run is called straight from the switch: a lambda around it makes the
+  // compiler treat the copy operands as divergent)
   switch (jn) {
-    case 1: run(std::integral_constant<int, 1>()); break;
-    case 2: run(std::integral_constant<int, (2 < JMAX ? 2 : JMAX)>()); break;
-    case 3: run(std::integral_constant<int, (3 < JMAX ? 3 : JMAX)>()); break;
-    case 4: run(std::integral_constant<int, (4 < JMAX ? 4 : JMAX)>()); break;
-    case 5: run(std::integral_constant<int, (5 < JMAX ? 5 : JMAX)>()); break;
-    case 6: run(std::integral_constant<int, (6 < JMAX ? 6 : JMAX)>()); break;
-    case 7: run(std::integral_constant<int, (7 < JMAX ? 7 : JMAX)>()); break;
-    case 8: run(std::integral_constant<int, (8 < JMAX ? 8 : JMAX)>()); break;
-    case 9: run(std::integral_constant<int, (9 < JMAX ? 9 : JMAX)>()); break;
-    default: run(std::integral_constant<int, JMAX>()); break;
+    case 1: { using Q = JnSel<1, JMAX, WF>; run(typename Q::N(), typename Q::P()); } break;
+    case 2: { using Q = JnSel<2, JMAX, WF>; run(typename Q::N(), typename Q::P()); } break;
+    case 3: { using Q = JnSel<3, JMAX, WF>; run(typename Q::N(), typename Q::P()); } break;
+    case 4: { using Q = JnSel<4, JMAX, WF>; run(typename Q::N(), typename Q::P()); } break;
+    case 5: { using Q = JnSel<5, JMAX, WF>; run(typename Q::N(), typename Q::P()); } break;
+    case 6: { using Q = JnSel<6, JMAX, WF>; run(typename Q::N(), typename Q::P()); } break;
+    case 7: { using Q = JnSel<7, JMAX, WF>; run(typename Q::N(), typename Q::P()); } break;
+    case 8: { using Q = JnSel<8, JMAX, WF>; run(typename Q::N(), typename Q::P()); } break;
+    case 9: { using Q = JnSel<9, JMAX, WF>; run(typename Q::N(), typename Q::P()); } break;
+    default: { using Q = JnSel<JMAX, JMAX, WF>; run(typename Q::N(), typename Q::P()); } break;
   }
   // every wave is done with the LDS ring and s_tile before the next tile
   __syncthreads();
