@@ -62,6 +62,7 @@ namespace moe {
 
 constexpr int kPkIterK = 128;  // k per main-loop iteration
 constexpr int kPkSteps = 8;    // MFMA k-steps (16 wide) per iteration
+constexpr int kCopySteps = 4;  // k-steps of a half-stage over which its copies are spread
 // Word 3 of a raw (untyped, unswizzled) buffer resource on gfx950.
 constexpr int kBufferFlags = 0x00020000;
 
@@ -192,15 +193,26 @@ __device__ __forceinline__ void wait_vm_barrier_reads_in_flight() {
 // the copies of half-stages 0..D-3 and then a pseudo iteration -1 in the FULL
 // order, so the counts below hold from the first k-step on.  Loads past the
 // end of the tile read clamped (real) addresses and land in slots nobody
-// reads.  The last copy of every half-stage is issued in its k-step uu = 3.
+// reads.  A half-stage's copies go out over its first KC k-steps.  The
+// loads share one in-order counter, so a wait for a half-stage's copies also
+// waits for every weight load issued before its last copy.
 struct PkSched {
-  int JN, WL, D;
-  constexpr int cl(int uu) const { return JN * uu / 4; }  // first chunk copied at k-step uu
+  int JN, WL, D, KC;  // KC: k-steps of a half-stage that issue its copies (1, 2 or 4)
+  constexpr int cl(int uu) const { return JN * (uu < KC ? uu : KC) / KC; }  // first chunk of k-step uu
   constexpr int nc(int uu) const { return cl(uu + 1) - cl(uu); }
   constexpr int na(int uu) const { return (nc(uu) + 1) / 2; }
   constexpr int nb(int uu) const { return nc(uu) - na(uu); }
-  // loads issued after the last copy of k-step uu = 3 in that k-step
-  constexpr int tail3() const { return WL == 2 && nb(3) == 0 ? 2 : 1; }
+  // loads issued in k-step uu after its last copy
+  constexpr int tail(int uu) const { return WL == 2 && nb(uu) == 0 ? 2 : 1; }
+  // the k-step of a half-stage that issues its last copy
+  constexpr int lastk() const {
+    int k = 0;
+    for (int q = 0; q < 4; ++q)
+      if (nc(q) > 0) k = q;
+    return k;
+  }
+  // loads issued after the last copy of a half-stage, to the end of that half-stage
+  constexpr int rest() const { return tail(lastk()) + (3 - lastk()) * WL; }
   // loads issued after weight k-step s (the last load of k-step s - 8) up to
   // the wait at the start of k-step s: k-steps s-7 .. s-1, s in a FULL iteration
   constexpr int w_full(int u) const { return 7 * WL + 2 * JN - nc(u & 3); }
@@ -211,19 +223,22 @@ struct PkSched {
     return n;
   }
   // D = 2: at the end of half-stage h, loads issued after the last copy of
-  // half-stage h + 1 (k-step 3 of half-stage h - 1): the rest of that k-step
-  // and half-stage h -- or, in the first half of the last iteration, nothing
-  // more; before the first barrier, after half-stage 0's last copy
-  constexpr int x_full() const { return tail3() + (D - 1) * (JN + 4 * WL); }
-  constexpr int x_last() const { return tail3() + (D - 2) * (JN + 4 * WL); }
-  constexpr int x_first() const { return tail3() + JN + 4 * WL; }
-  // D = 3 (early publication): the end of half-stage h waits for the copies
+  // half-stage h + 1 (issued during half-stage h - 1): the rest of that
+  // half-stage and half-stage h -- or, in the first half of the last
+  // iteration, nothing more; before the first barrier, after half-stage 0's
+  // last copy
+  constexpr int x_full() const { return rest() + (D - 1) * (JN + 4 * WL); }
+  constexpr int x_last() const { return rest() + (D - 2) * (JN + 4 * WL); }
+  constexpr int x_first() const { return rest() + JN + 4 * WL; }
+  // D >= 3 (early publication): the end of half-stage h waits for the copies
   // of h + 2, so that the B fragments of h + 1's first k-step can be read
-  // before that barrier; their last copy was issued at k-step 3 of half-stage
-  // h - 1.  Before the first barrier: after half-stage 1's last copy (pseudo
-  // iteration, first half).
-  constexpr int x_full_early() const { return tail3() + (D - 2) * (JN + 4 * WL); }
-  constexpr int x_first_early() const { return tail3() + JN + 4 * WL; }
+  // before that barrier; they were issued during half-stage h + 2 - D.
+  // Before the first barrier: after half-stage 1's last copy (pseudo
+  // iteration, first half, for D = 3; the prologue for D = 4).
+  constexpr int x_full_early() const { return rest() + (D - 2) * (JN + 4 * WL); }
+  constexpr int x_first_early() const {
+    return D == 3 ? rest() + JN + 4 * WL : (D - 2) * JN + 8 * WL;
+  }
 };
 
 // Specialisation of a tile of J live token fragments: the fragment count
@@ -330,8 +345,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     // rows; it reads stale LDS rows of the slot and is never stored.
     const int pw = PAIR ? (wave & ~1) : wave;      // first packed stream of this wave
     static_assert(!PAIR || JN % 2 == 0 || JN < JMAX, "fragment JN must lie inside the slot");
-    static_assert(D == 2 || D == 3, "ring depth");
-    constexpr PkSched S{JN, WL, D};
+    static_assert(D >= 2 && D <= 4, "ring depth");
+    constexpr PkSched S{JN, WL, D, kCopySteps};
     // The wave's weight stream(s) as one buffer resource: fragment i of
     // k-step s of stream pw + q at q * sbytes + s * 2048 + i * 1024.
     const i32x4 wrsrc =
