@@ -68,6 +68,11 @@ CASES = [
     (300, 64, 8, 1, 1, "bf16", "random"),
     (256, 64, 8, 2, 2, "f32", "random"),
     (333, 68, 8, 3, 8, "f32", "skew"),
+    # batches of at most 4 chunks of 256 tokens with E <= 256 count and scan
+    # in one block; larger ones in two kernels
+    (1024, 64, 256, 8, 8, "bf16", "random"),   # 4 chunks, E = 256: one block
+    (1025, 64, 8, 2, 2, "bf16", "hot"),        # 5 chunks: two kernels, one token in the last
+    (4096, 64, 64, 2, 8, "bf16", "skew"),      # 16 chunks
 ]
 
 

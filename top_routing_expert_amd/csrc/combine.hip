@@ -5,8 +5,8 @@
 // gate weights on the token's home device).
 //
 // gfx950 design: one wave per token, 16-byte vector gathers of the k expert
-// rows (each row contiguous), fp32 FMAs in a fixed j order, one 16-byte store
-// per lane.  HBM traffic is the algorithmic minimum: every y_perm row is read
+// rows (each row contiguous; up to 8 gathers per lane in flight), fp32 FMAs
+// in a fixed j order, one 16-byte store per lane and vector.  HBM traffic is the algorithmic minimum: every y_perm row is read
 // once and every out row written once.
 #include "common.h"
 
@@ -14,6 +14,10 @@ namespace moe {
 
 constexpr int kMaxKC = 16;
 
+// KC: k rounded up to 1, 2, 4, 8 or kMaxKC; U: 16-byte vectors per lane in
+// flight per expert row, so that every lane keeps U * KC <= 8 loads in flight
+// (a token's row is read in few memory round trips).
+template <int KC, int U>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(const u32x4* __restrict__ y,
                                                            const int32_t* __restrict__ slot_of,
                                                            const float* __restrict__ topk_w,
@@ -29,35 +33,44 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const u32x4* __restri
     p = p < 0 ? 0 : (p >= T * k ? T * k - 1 : p);  // keep every access in bounds
     g = topk_w[(size_t)t * k + lane];
   }
-  int pj[kMaxKC];
-  float gj[kMaxKC];
+  int pj[KC];
+  float gj[KC];
 #pragma unroll
-  for (int j = 0; j < kMaxKC; ++j) {
+  for (int j = 0; j < KC; ++j) {
     pj[j] = __shfl(p, j);
     gj[j] = __shfl(g, j);
   }
-  for (int v = lane; v < row_vecs; v += 64) {
-    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int v0 = lane; v0 < row_vecs; v0 += 64 * U) {
+    u32x4 w[U][KC];
 #pragma unroll
-    for (int j = 0; j < kMaxKC; ++j) {
-      if (j < k) {
-        const u32x4 w = y[(size_t)pj[j] * row_vecs + v];
-        a[0] = fmaf(gj[j], bf16_lo(w.x), a[0]);
-        a[1] = fmaf(gj[j], bf16_hi(w.x), a[1]);
-        a[2] = fmaf(gj[j], bf16_lo(w.y), a[2]);
-        a[3] = fmaf(gj[j], bf16_hi(w.y), a[3]);
-        a[4] = fmaf(gj[j], bf16_lo(w.z), a[4]);
-        a[5] = fmaf(gj[j], bf16_hi(w.z), a[5]);
-        a[6] = fmaf(gj[j], bf16_lo(w.w), a[6]);
-        a[7] = fmaf(gj[j], bf16_hi(w.w), a[7]);
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < KC; ++j)
+        if (j < k && v0 + 64 * u < row_vecs) w[u][j] = y[(size_t)pj[j] * row_vecs + v0 + 64 * u];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (v0 + 64 * u >= row_vecs) break;
+      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        if (j < k) {
+          a[0] = fmaf(gj[j], bf16_lo(w[u][j].x), a[0]);
+          a[1] = fmaf(gj[j], bf16_hi(w[u][j].x), a[1]);
+          a[2] = fmaf(gj[j], bf16_lo(w[u][j].y), a[2]);
+          a[3] = fmaf(gj[j], bf16_hi(w[u][j].y), a[3]);
+          a[4] = fmaf(gj[j], bf16_lo(w[u][j].z), a[4]);
+          a[5] = fmaf(gj[j], bf16_hi(w[u][j].z), a[5]);
+          a[6] = fmaf(gj[j], bf16_lo(w[u][j].w), a[6]);
+          a[7] = fmaf(gj[j], bf16_hi(w[u][j].w), a[7]);
+        }
       }
+      u32x4 o;
+      o.x = pack_bf16x2(a[0], a[1]);
+      o.y = pack_bf16x2(a[2], a[3]);
+      o.z = pack_bf16x2(a[4], a[5]);
+      o.w = pack_bf16x2(a[6], a[7]);
+      out[(size_t)t * row_vecs + v0 + 64 * u] = o;
     }
-    u32x4 o;
-    o.x = pack_bf16x2(a[0], a[1]);
-    o.y = pack_bf16x2(a[2], a[3]);
-    o.z = pack_bf16x2(a[4], a[5]);
-    o.w = pack_bf16x2(a[6], a[7]);
-    out[(size_t)t * row_vecs + v] = o;
   }
 }
 
@@ -103,8 +116,19 @@ hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t
                           const float* topk_w, void* out, hipStream_t st) {
   const dim3 grid(div_up(c.T, 4));
   if (c.dtype == MOE_BF16) {
-    combine_bf16_kernel<<<grid, 256, 0, st>>>(static_cast<const u32x4*>(y_perm), slot_of, topk_w,
-                                              static_cast<u32x4*>(out), c.T, c.k, c.d / 8);
+    auto* yv = static_cast<const u32x4*>(y_perm);
+    auto* ov = static_cast<u32x4*>(out);
+    const int rv = c.d / 8;
+    if (c.k <= 1)
+      combine_bf16_kernel<1, 8><<<grid, 256, 0, st>>>(yv, slot_of, topk_w, ov, c.T, c.k, rv);
+    else if (c.k <= 2)
+      combine_bf16_kernel<2, 4><<<grid, 256, 0, st>>>(yv, slot_of, topk_w, ov, c.T, c.k, rv);
+    else if (c.k <= 4)
+      combine_bf16_kernel<4, 2><<<grid, 256, 0, st>>>(yv, slot_of, topk_w, ov, c.T, c.k, rv);
+    else if (c.k <= 8)
+      combine_bf16_kernel<8, 1><<<grid, 256, 0, st>>>(yv, slot_of, topk_w, ov, c.T, c.k, rv);
+    else
+      combine_bf16_kernel<kMaxKC, 1><<<grid, 256, 0, st>>>(yv, slot_of, topk_w, ov, c.T, c.k, rv);
   } else {
     combine_f32_kernel<<<grid, 256, 0, st>>>(static_cast<const float4*>(y_perm), slot_of, topk_w,
                                              static_cast<float4*>(out), c.T, c.k, c.d / 4);

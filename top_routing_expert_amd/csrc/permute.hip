@@ -16,7 +16,9 @@
 //     routed to e".  Writes the per-chunk counts and each pair's chunk rank.
 //  2. scan  : one block turns the per-chunk counts into per-chunk bases
 //     (exclusive over chunks) and the totals into expert_offsets and
-//     rank_offsets.
+//     rank_offsets.  Batches of at most four chunks (E <= 256) run 1 and 2
+//     as one block (one launch fewer; for more chunks the parallel count
+//     blocks win).
 //  3. scatter: one wave per token computes its k slots, writes slot_of /
 //     src_of, reads the token row once and stores it to its k slots with
 //     16-byte vector accesses (x is read once; x_perm written once).
@@ -65,29 +67,14 @@ __global__ __launch_bounds__(256) void perm_count_kernel(const int32_t* __restri
   }
 }
 
-// counts[c][e] -> exclusive base over chunks (in place); totals -> offsets.
-__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ counts, int nchunk,
-                                                         int E, int R,
-                                                         int32_t* __restrict__ expert_offsets,
-                                                         int32_t* __restrict__ rank_offsets) {
-  __shared__ int32_t s_excl[1025];
-  __shared__ int32_t s_wave[16];
+// Exclusive scan of the per-expert totals over the experts (one block of 1024
+// threads; thread e < E holds expert e's total) -> expert_offsets [E + 1] and
+// rank_offsets [R + 1].
+__device__ __forceinline__ void scan_expert_totals(int total, int E, int R,
+                                                   int32_t* __restrict__ expert_offsets,
+                                                   int32_t* __restrict__ rank_offsets,
+                                                   int32_t* s_excl, int32_t* s_wave) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int total = 0;
-  if (tid < E) {
-    constexpr int B = 16;
-    for (int c0 = 0; c0 < nchunk; c0 += B) {
-      int v[B];
-#pragma unroll
-      for (int u = 0; u < B; ++u) v[u] = (c0 + u < nchunk) ? counts[(size_t)(c0 + u) * E + tid] : 0;
-#pragma unroll
-      for (int u = 0; u < B; ++u) {
-        if (c0 + u < nchunk) counts[(size_t)(c0 + u) * E + tid] = total;
-        total += v[u];
-      }
-    }
-  }
-  // block-wide exclusive scan of `total` over experts
   int incl = total;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -117,6 +104,98 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ c
     expert_offsets[E] = s_excl[E];
     rank_offsets[R] = s_excl[E];
   }
+}
+
+// counts[c][e] -> exclusive base over chunks (in place); totals -> offsets.
+__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t* __restrict__ counts, int nchunk,
+                                                         int E, int R,
+                                                         int32_t* __restrict__ expert_offsets,
+                                                         int32_t* __restrict__ rank_offsets) {
+  __shared__ int32_t s_excl[1025];
+  __shared__ int32_t s_wave[16];
+  const int tid = threadIdx.x;
+  int total = 0;
+  if (tid < E) {
+    constexpr int B = 16;
+    for (int c0 = 0; c0 < nchunk; c0 += B) {
+      int v[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) v[u] = (c0 + u < nchunk) ? counts[(size_t)(c0 + u) * E + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        if (c0 + u < nchunk) counts[(size_t)(c0 + u) * E + tid] = total;
+        total += v[u];
+      }
+    }
+  }
+  scan_expert_totals(total, E, R, expert_offsets, rank_offsets, s_excl, s_wave);
+}
+
+// Small batches (at most kFusedChunks chunks, E <= kFusedMaxE): count and scan
+// in one block of 1024 threads, four chunks per pass (four waves per chunk,
+// exactly as perm_count_kernel), the per-chunk counts kept in LDS.  Writes the
+// same outputs as perm_count_kernel followed by perm_scan_kernel.  The kernel
+// handles any number of passes; it is launched for one.
+constexpr int kFusedChunks = 4;
+constexpr int kFusedMaxE = 256;
+
+__global__ __launch_bounds__(1024) void perm_count_scan_kernel(
+    const int32_t* __restrict__ topk_idx, int T, int k, int E, int R, int nchunk,
+    int32_t* __restrict__ base, int32_t* __restrict__ rank, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ rank_offsets) {
+  extern __shared__ unsigned long long masks[];  // [16 waves][E], then int32 cnt[nchunk][E]
+  int32_t* cnt = reinterpret_cast<int32_t*>(masks + 16 * E);
+  __shared__ int32_t s_excl[kFusedMaxE + 1];
+  __shared__ int32_t s_wave[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int cw = w & 3, cs = w >> 2;  // wave inside its chunk, chunk inside the pass
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int c0 = 0; c0 < nchunk; c0 += 4) {
+    for (int i = tid; i < 16 * E; i += 1024) masks[i] = 0ull;
+    __syncthreads();
+    const int c = c0 + cs;
+    const int t = c * kChunk + (tid & (kChunk - 1));
+    const bool live = c < nchunk && t < T;
+    int ev[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      ev[j] = 0;
+      if (j < k && live) {
+        int e = topk_idx[(size_t)t * k + j];
+        e = e < 0 ? 0 : (e >= E ? E - 1 : e);  // keep every access in bounds
+        ev[j] = e;
+        atomicOr(&masks[w * E + e], 1ull << lane);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      if (j < k && live) {
+        const int e = ev[j];
+        int r = __popcll(masks[w * E + e] & below);
+        for (int v = 0; v < cw; ++v) r += __popcll(masks[(cs * 4 + v) * E + e]);
+        rank[(size_t)t * k + j] = r;
+      }
+    }
+    for (int i = tid; i < 4 * E; i += 1024) {
+      const int sl = i / E, e = i - sl * E;
+      if (c0 + sl < nchunk) {
+        int n = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) n += __popcll(masks[(sl * 4 + v) * E + e]);
+        cnt[(c0 + sl) * E + e] = n;
+      }
+    }
+    __syncthreads();  // masks are cleared by the next pass
+  }
+  int total = 0;
+  if (tid < E) {
+    for (int c = 0; c < nchunk; ++c) {
+      base[(size_t)c * E + tid] = total;
+      total += cnt[c * E + tid];
+    }
+  }
+  scan_expert_totals(total, E, R, expert_offsets, rank_offsets, s_excl, s_wave);
 }
 
 __global__ __launch_bounds__(256) void perm_scatter_kernel(
@@ -170,13 +249,22 @@ hipError_t launch_permute(const moe_config& c, const void* x, const int32_t* top
   int32_t* counts = static_cast<int32_t*>(ws);
   int32_t* rank = reinterpret_cast<int32_t*>(static_cast<char*>(ws) +
                                              align256((size_t)nchunk * c.E * sizeof(int32_t)));
-  perm_count_kernel<<<nchunk, 256, 4 * c.E * sizeof(unsigned long long), st>>>(topk_idx, c.T, c.k,
-                                                                              c.E, counts, rank);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  perm_scan_kernel<<<1, 1024, 0, st>>>(counts, nchunk, c.E, c.ep_ranks, expert_offsets,
-                                       rank_offsets);
-  err = hipGetLastError();
+  hipError_t err;
+  if (nchunk <= kFusedChunks && c.E <= kFusedMaxE) {
+    const size_t lds = 16 * (size_t)c.E * sizeof(unsigned long long) +
+                       (size_t)nchunk * c.E * sizeof(int32_t);
+    perm_count_scan_kernel<<<1, 1024, lds, st>>>(topk_idx, c.T, c.k, c.E, c.ep_ranks, nchunk,
+                                                 counts, rank, expert_offsets, rank_offsets);
+    err = hipGetLastError();
+  } else {
+    perm_count_kernel<<<nchunk, 256, 4 * c.E * sizeof(unsigned long long), st>>>(
+        topk_idx, c.T, c.k, c.E, counts, rank);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    perm_scan_kernel<<<1, 1024, 0, st>>>(counts, nchunk, c.E, c.ep_ranks, expert_offsets,
+                                         rank_offsets);
+    err = hipGetLastError();
+  }
   if (err != hipSuccess) return err;
   const int elem = c.dtype == MOE_BF16 ? 2 : 4;
   const int row_vecs = (int)((size_t)c.d * elem / 16);

@@ -23,6 +23,8 @@
 
 namespace moe {
 
+constexpr int kMaxSplits = 16;  // split-K partials of the router GEMM (summed by top-k)
+
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // ============================================================== gate GEMM bf16
@@ -250,7 +252,7 @@ int router_splits(const moe_config& c) {
   if (c.E <= 16) {
     const long tiles = div_up(c.T, 64);
     long s = (512 + tiles - 1) / tiles;
-    if (s > 16) s = 16;
+    if (s > kMaxSplits) s = kMaxSplits;
     if (s > c.d / 64) s = c.d / 64;  // at least one k-pair per split
     return (int)(s < 1 ? 1 : s);
   }
@@ -261,7 +263,7 @@ int router_splits(const moe_config& c) {
   // kernel reads back (measured best: 256 for E <= 64, 512 for E = 256)
   const long target = c.E <= 64 ? 256 : 512;
   long s = (target + tiles - 1) / tiles;
-  if (s > 16) s = 16;
+  if (s > kMaxSplits) s = kMaxSplits;
   if (s > nch) s = nch;
   if (s < 1) s = 1;
   return (int)s;
@@ -347,7 +349,9 @@ __device__ __forceinline__ float ord_key_inv(uint32_t k) {
 
 constexpr int kMaxEPL = 16;  // E <= 1024 with 64 lanes per token
 
-template <int LPT>
+// EPL: scores per lane (ceil(E / LPT): 1 for E <= 64), so the code holds only
+// the loops a layer of this size needs.
+template <int LPT, int EPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ partial, int splits,
                                                    const float* __restrict__ bias,
                                                    float* __restrict__ logits_out,
@@ -363,14 +367,22 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
   const int epl = (E + LPT - 1) / LPT;
 
   // scores s = z + b (one fp32 add), -0 -> +0; key32 = order-preserving bits
-  uint32_t key[kMaxEPL];
+  uint32_t key[EPL];
 #pragma unroll
-  for (int i = 0; i < kMaxEPL; ++i) {
+  for (int i = 0; i < EPL; ++i) {
     key[i] = 0u;
     const int e = q + i * LPT;
     if (i < epl && e < E && live) {
-      float z = partial[(size_t)t * E + e];
-      for (int s = 1; s < splits; ++s) z += partial[((size_t)s * T + t) * E + e];
+      // every partial is loaded before the first add (one memory latency),
+      // then summed in split order
+      float pv[kMaxSplits];
+#pragma unroll
+      for (int s = 0; s < kMaxSplits; ++s)
+        pv[s] = s < splits ? partial[((size_t)s * T + t) * E + e] : 0.f;
+      float z = pv[0];
+#pragma unroll
+      for (int s = 1; s < kMaxSplits; ++s)
+        if (s < splits) z += pv[s];
       if (logits_out) logits_out[(size_t)t * E + e] = z;
       float sc = bias ? __fadd_rn(z, bias[e]) : z;
       uint32_t u = __float_as_uint(sc);
@@ -388,7 +400,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
     for (int g = 0; g < n_group; ++g) {
       uint32_t m = 0u;
 #pragma unroll
-      for (int i = 0; i < kMaxEPL; ++i) {
+      for (int i = 0; i < EPL; ++i) {
         const int e = q + i * LPT;
         if (i < epl && e < E && e / gsz == g) m = key[i] > m ? key[i] : m;
       }
@@ -414,7 +426,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
   for (int r = 0; r < nsel; ++r) {
     unsigned long long best = 0ull;
 #pragma unroll
-    for (int i = 0; i < kMaxEPL; ++i) {
+    for (int i = 0; i < EPL; ++i) {
       const int e = q + i * LPT;
       const bool ok = i < epl && e < E && !((taken >> i) & 1u) &&
                       (!grouped || ((kept >> (e / gsz)) & 1ull));
@@ -443,7 +455,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
   } else {
     float part = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxEPL; ++i) {
+    for (int i = 0; i < EPL; ++i) {
       const int e = q + i * LPT;
       if (i < epl && e < E) part += expf(ord_key_inv(key[i]) - s_max);
     }
@@ -457,22 +469,30 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ par
 
 hipError_t launch_topk(const moe_config& c, const float* partial, int splits, const float* bias,
                        float* logits_out, int32_t* topk_idx, float* topk_w, hipStream_t st) {
+  if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
   int lpt = 1;
   while (lpt < c.E && lpt < 64) lpt <<= 1;
   if (lpt < 2) lpt = 2;
   const int tpb = 4 * (64 / lpt);
   const dim3 grid(div_up(c.T, tpb));
-#define MOE_TOPK(L)                                                                        \
-  topk_kernel<L><<<grid, 256, 0, st>>>(partial, splits, bias, logits_out, topk_idx, topk_w, \
-                                       c.T, c.E, c.k, c.n_group, c.topk_group, c.presel,    \
-                                       c.renorm)
+#define MOE_TOPK(L, P)                                                                        \
+  topk_kernel<L, P><<<grid, 256, 0, st>>>(partial, splits, bias, logits_out, topk_idx, topk_w, \
+                                          c.T, c.E, c.k, c.n_group, c.topk_group, c.presel,    \
+                                          c.renorm)
   switch (lpt) {
-    case 2: MOE_TOPK(2); break;
-    case 4: MOE_TOPK(4); break;
-    case 8: MOE_TOPK(8); break;
-    case 16: MOE_TOPK(16); break;
-    case 32: MOE_TOPK(32); break;
-    default: MOE_TOPK(64); break;
+    case 2: MOE_TOPK(2, 1); break;
+    case 4: MOE_TOPK(4, 1); break;
+    case 8: MOE_TOPK(8, 1); break;
+    case 16: MOE_TOPK(16, 1); break;
+    case 32: MOE_TOPK(32, 1); break;
+    default:
+      if (c.E <= 64)
+        MOE_TOPK(64, 1);
+      else if (c.E <= 256)
+        MOE_TOPK(64, 4);
+      else
+        MOE_TOPK(64, kMaxEPL);
+      break;
   }
 #undef MOE_TOPK
   return hipGetLastError();
