@@ -26,19 +26,60 @@ def _regs(tok):
     return {tok} if re.match(r"[va]\d+$", tok) else set()
 
 
-def in_flight_violations(asm: str, kernel_pat: str = "gemm_packed"):
-    """(kernel, instruction) pairs that read or write a register whose async
-    asm load has not been waited for."""
+def _kernel_bodies(asm: str, kernel_pat: str):
+    """(name, instruction lines) of every kernel whose symbol matches."""
     out, body, name = [], None, None
     for line in asm.split("\n"):
         if re.match(r"^_Z\w*:", line) and kernel_pat in line:
-            body, name, pending, in_asm = [], line, set(), False
+            body, name = [], line
             continue
         if body is None:
             continue
+        body.append(line)
         if "s_endpgm" in line:
+            out.append((name, body))
             body = None
+    return out
+
+
+def _blocks(lines):
+    """Basic blocks of a kernel body: list of (label, instructions, successor
+    labels).  A block ends at a label or after a branch / s_endpgm."""
+    blocks, cur, label = [], [], "entry"
+    n = 0
+
+    def close(succ):
+        nonlocal cur, label, n
+        blocks.append([label, cur, succ])
+        n += 1
+        cur, label = [], f"_fall{n}"
+
+    for line in lines:
+        m = re.match(r"^(\.\w+):", line)
+        if m:
+            close([m.group(1)])  # falls through into the label (may be empty)
+            label = m.group(1)
             continue
+        cur.append(line)
+        ins = line.strip().split(";")[0].strip()
+        op = ins.split()[0] if ins else ""
+        if op == "s_branch":
+            close([ins.split()[1]])
+        elif op.startswith("s_cbranch"):
+            close([ins.split()[1], f"_fall{n + 1}"])
+        elif op == "s_endpgm":
+            close([])
+    if cur:
+        close([])
+    return blocks
+
+
+def _transfer(lines, pending, report):
+    """Walk one block: returns the pending set at its end; report(ins) for
+    every non-asm instruction that touches a pending register."""
+    in_asm = False
+    pending = set(pending)
+    for line in lines:
         s = line.strip()
         if s.startswith(";;#ASMSTART"):
             in_asm = True
@@ -66,7 +107,38 @@ def in_flight_violations(asm: str, kernel_pat: str = "gemm_packed"):
         for a in args:
             touched |= _regs(a.split()[0] if a else "")
         if touched & pending:
-            out.append((name, ins))
+            report(ins)
+    return pending
+
+
+def in_flight_violations(asm: str, kernel_pat: str = "gemm_packed"):
+    """(kernel, instruction) pairs that read or write a register whose async
+    asm load has not been waited for on some path through the kernel's
+    control flow (any explicit asm vmcnt wait counts as waiting for all of
+    them: the waits' counts are checked by the schedule, this checks that
+    the compiler leaves the registers alone in between)."""
+    out = []
+    for name, lines in _kernel_bodies(asm, kernel_pat):
+        blocks = _blocks(lines)
+        index = {b[0]: k for k, b in enumerate(blocks)}
+        entry_in = [set() for _ in blocks]
+        work = list(range(len(blocks)))
+        while work:
+            k = work.pop(0)
+            end = _transfer(blocks[k][1], entry_in[k], lambda ins: None)
+            for t in blocks[k][2]:
+                if t in index:
+                    q = index[t]
+                    if not end <= entry_in[q]:
+                        entry_in[q] |= end
+                        work.append(q)
+        seen = set()
+        for k, b in enumerate(blocks):
+            def rep(ins):
+                if ins not in seen:
+                    seen.add(ins)
+                    out.append((name, ins))
+            _transfer(b[1], entry_in[k], rep)
     return out
 
 
@@ -82,6 +154,25 @@ def test_checker_flags_a_copy_of_an_in_flight_register():
     assert len(in_flight_violations(asm)) == 1
     ok = asm.replace("v_mov_b32 v20, v5", "v_mov_b32 v20, v9")
     assert in_flight_violations(ok) == []
+
+
+def test_checker_follows_control_flow():
+    load = [";;#ASMSTART", "buffer_load_dwordx4 v[4:7], v1, s[0:3], s4 offen offset:0", ";;#ASMEND"]
+    wait = [";;#ASMSTART", "s_waitcnt vmcnt(0)", ";;#ASMEND"]
+    # the load at the bottom of a loop is still in flight at its top
+    loop = "\n".join(["_Zgemm_packed_k:", ".LBB0_1:", "v_mov_b32 v20, v5", *wait,
+                      "v_mfma_f32_32x32x16_bf16 a[0:15], v[4:7], v[8:11], a[0:15]", *load,
+                      "s_cbranch_scc1 .LBB0_1", "s_endpgm"])
+    assert len(in_flight_violations(loop)) == 1
+    # ... and at the target of a conditional branch's fall-through label
+    fall = "\n".join(["_Zgemm_packed_k:", *load, "s_cbranch_scc1 .LBB0_2", ".LBB0_3:",
+                      "v_mov_b32 v20, v6", ".LBB0_2:", *wait, "s_endpgm"])
+    assert len(in_flight_violations(fall)) == 1
+    # a block after an unconditional branch is not reached from the load
+    other = "\n".join(["_Zgemm_packed_k:", *load, *wait, "s_branch .LBB0_4", *load,
+                       "s_branch .LBB0_5", ".LBB0_6:", "v_mov_b32 v20, v6", ".LBB0_5:", *wait,
+                       ".LBB0_4:", "s_endpgm"])
+    assert in_flight_violations(other) == []
 
 
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
