@@ -180,6 +180,8 @@ int moe_route(const moe_config* cfg, const void* x, const void* w_router, const 
  *   slot_of        [T*k] int32 out: slot_of[t*k+j] = p(t,j).
  *   src_of         [T*k] int32 out: src_of[p] = t*k+j (inverse of slot_of).
  *   x_perm         [T*k, d] (dtype) out: x_perm[p] = x[t], bit-exact copies.
+ *   x and x_perm may both be NULL: then only the index outputs are written
+ *   (for moe_ffn_gate_up_packed_gather, which reads the rows itself).
  */
 int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
                 int32_t* expert_offsets, int32_t* rank_offsets, int32_t* slot_of,
@@ -278,6 +280,29 @@ int moe_ffn_gate_up_packed(const moe_config* cfg, const void* x_perm,
                            void* stream);
 int moe_ffn_down_packed(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
                         const void* packed_down, void* y_perm, void* stream);
+
+/*
+ * moe_ffn_gate_up_packed with the dispatch gather fused into the first GEMM's
+ * operand load ([V4-overlap] Waved-EP section: the gather folded into the
+ * expert GEMM): row p of expert e's range reads token row x[src_of[p] / k]
+ * instead of x_perm[p], so x_perm is never written or read.  Same h, bit for
+ * bit, as moe_ffn_gate_up_packed on the x_perm that moe_permute would write.
+ *   x       [T, d] bf16 in (16-byte aligned), token order.
+ *   src_of  [T*k] int32 in, from moe_permute (values outside [0, T*k) are
+ *           clamped to a valid token row, never read out of bounds).
+ * The sub-table rule applies: expert_offsets and packed_gate_up may be offset
+ * to one rank's experts; src_of stays the whole table.
+ */
+int moe_ffn_gate_up_packed_gather(const moe_config* cfg, const void* x, const int32_t* src_of,
+                                  const int32_t* expert_offsets, const void* packed_gate_up,
+                                  void* h, void* stream);
+
+/*
+ * moe_layer_fwd_packed: when bufs->x_perm is NULL (or bufs is NULL), the
+ * dispatch writes indices only and the first GEMM gathers its rows
+ * (moe_ffn_gate_up_packed_gather); a given bufs->x_perm is written as by
+ * moe_permute and read by moe_ffn_gate_up_packed.  Both give the same out.
+ */
 int moe_layer_fwd_packed(const moe_config* cfg, const void* x, const void* w_router,
                          const float* bias, const void* packed_gate_up, const void* packed_down,
                          void* out, const moe_layer_bufs* bufs, void* ws, size_t ws_bytes,

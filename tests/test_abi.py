@@ -29,6 +29,26 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+def _declared_param_counts():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(moe_\w+)\s*\(([^;{]*?)\)\s*;", src):
+        params = [p for p in m.group(2).split(",") if p.strip() and p.strip() != "void"]
+        out[m.group(1)] = len(params)
+    return out
+
+
+def test_binding_declares_every_signature():
+    """Without argtypes ctypes would pass device pointers as 32-bit ints."""
+    L = B.lib()
+    counts = _declared_param_counts()
+    for name in B.EXPORTS:
+        f = getattr(L, name)
+        assert f.argtypes is not None, name
+        assert len(f.argtypes) == counts[name], (name, len(f.argtypes), counts[name])
+
+
 def test_strerror():
     assert B.strerror(0) == "ok"
     for s in (-1, -2, -3):

@@ -188,3 +188,92 @@ def test_packed_layer_matches_oracle(name):
     assert np.array_equal(host(buf["expert_offsets"]), ref["offsets"])
     err = rel_err(host(buf["out"]), ref["out"])
     assert err <= TOL_LAYER["bf16"], err
+
+
+def _dispatch(shape, seed):
+    """x in token order and the library's own dispatch of a random top-k."""
+    rng = np.random.default_rng(seed)
+    T, E, k = shape.T, shape.E, shape.k
+    idx_np = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    cfg = B.config(shape)
+    A = T * k
+    x = B.to_device(I.make_x(shape, seed=seed + 1))
+    idx = torch.from_numpy(idx_np).cuda()
+    offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    roffs = torch.empty(shape.ep_ranks + 1, dtype=torch.int32, device="cuda")
+    slot = torch.empty(A, dtype=torch.int32, device="cuda")
+    src = torch.empty(A, dtype=torch.int32, device="cuda")
+    xp = torch.empty((A, shape.d), dtype=torch.bfloat16, device="cuda")
+    B.moe_permute(cfg, x, idx, offs, roffs, slot, src, xp, B.workspace(cfg, "permute"))
+    return x, src, offs, xp
+
+
+GATHER = [
+    # (E, d, f, T, k): half-slab tiles of 1..10 fragments (2 x 2 pairs above 5),
+    # and whole-slab tiles (E=64, f=1088)
+    (8, 256, 448, 700, 2),
+    (4, 320, 192, 333, 3),
+    (64, 2048, 1088, 4000, 2),
+]
+
+
+@pytest.mark.parametrize("case", GATHER, ids=[f"E{c[0]}-d{c[1]}-f{c[2]}-T{c[3]}" for c in GATHER])
+def test_packed_gather_equals_x_perm_path(case):
+    """The gather reads x[src_of[p] / k] where the plain kernel reads x_perm[p]:
+    same operands, same sums, so h is bit for bit the same."""
+    E, d, f, T, k = case
+    log(f"[ffn-packed] gather {case}")
+    shape = C.E8_D4096.replace(name="ffn-gather", T=T, k=k, E=E, d=d, f=f, ep_ranks=1)
+    x, src, offs, xp = _dispatch(shape, 81)
+    cfg = B.config(shape)
+    wg, wu, _ = _weights(shape, 82)
+    pgu, _ = B.pack_weights(cfg, B.to_device(wg), B.to_device(wu), None)
+    h1 = torch.empty((T * k, f), dtype=torch.bfloat16, device="cuda")
+    h2 = torch.full((T * k, f), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    B.moe_ffn_gate_up_packed(cfg, xp, offs, pgu, h1)
+    B.moe_ffn_gate_up_packed_gather(cfg, x, src, offs, pgu, h2)
+    torch.cuda.synchronize()
+    assert torch.equal(h1.view(torch.int16), h2.view(torch.int16))
+
+
+def test_packed_gather_subtable():
+    """One rank's experts: offsets and weights offset to the rank, src_of whole."""
+    log("[ffn-packed] gather sub-table")
+    E, R, d, f, T, k = 16, 4, 256, 320, 900, 2
+    shape = C.E8_D4096.replace(name="ffn-gather-sub", T=T, k=k, E=E, d=d, f=f, ep_ranks=R)
+    x, src, offs, xp = _dispatch(shape, 91)
+    cfg = B.config(shape)
+    wg, wu, _ = _weights(shape, 92)
+    pgu, _ = B.pack_weights(cfg, B.to_device(wg), B.to_device(wu), None)
+    gu_bytes, _ = B.packed_weight_bytes(cfg)
+    per = E // R
+    e0 = 2 * per
+    sub = B.config(shape, E=per)
+    h1 = torch.full((T * k, f), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    h2 = torch.full((T * k, f), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    B.moe_ffn_gate_up_packed(sub, xp, offs[e0:], pgu[e0 * (gu_bytes // E):], h1)
+    B.moe_ffn_gate_up_packed_gather(sub, x, src, offs[e0:], pgu[e0 * (gu_bytes // E):], h2)
+    torch.cuda.synchronize()
+    assert torch.equal(h1.view(torch.int16), h2.view(torch.int16))
+    r0, r1 = int(offs[e0]), int(offs[e0 + per])
+    assert bool((h2[:r0].view(torch.int16) == 7).all()) and bool((h2[r1:].view(torch.int16) == 7).all())
+
+
+def test_packed_layer_gather_equals_materialised():
+    """moe_layer_fwd_packed with a caller x_perm (written and read) and without
+    (gathered inside the first GEMM): the same out, bit for bit."""
+    shape = C.SMALL["e64"]
+    log(f"[layer-packed] gather vs x_perm {shape.name}")
+    inp = I.make_inputs(shape, seed=63)
+    dev = upload(inp)
+    cfg = B.config(shape)
+    pgu, pd = B.pack_weights(cfg, dev["w_gate"], dev["w_up"], dev["w_down"])
+    outs = []
+    for keep_xperm in (False, True):
+        buf = alloc(shape)
+        bufs = {"x_perm": buf["x_perm"]} if keep_xperm else {}
+        B.moe_layer_fwd_packed(cfg, dev["x"], dev["w_router"], dev["bias"], pgu, pd, buf["out"],
+                               bufs, B.workspace(cfg, "layer"))
+        torch.cuda.synchronize()
+        outs.append(buf["out"].view(torch.int16).clone())
+    assert torch.equal(outs[0], outs[1])

@@ -120,3 +120,29 @@ def test_permute_deterministic():
     for u, v in zip(a, b):
         assert torch.equal(u.view(torch.int16) if u.dtype == torch.bfloat16 else u,
                            v.view(torch.int16) if v.dtype == torch.bfloat16 else v)
+
+
+@pytest.mark.parametrize("T,E,k", [(1000, 64, 2), (300, 8, 1), (4099, 256, 8)])
+def test_permute_indices_only(T, E, k):
+    """x and x_perm NULL: the same index outputs, no row copies."""
+    log(f"[permute] indices only T={T} E={E} k={k}")
+    rng = np.random.default_rng(T + E)
+    shape = C.E8_D4096.replace(name="perm-idx", T=T, d=64, E=E, k=k, ep_ranks=4)
+    idx_np = _topk("random", T, E, k, rng)
+    x_np = I.make_x(shape, seed=3)
+    _, offs, roffs, slot, src, _ = _run(shape, x_np, idx_np)
+    cfg = B.config(shape)
+    A = T * k
+    idx = torch.from_numpy(idx_np).cuda()
+    offs2 = torch.full_like(offs, -7)
+    roffs2 = torch.full_like(roffs, -7)
+    slot2 = torch.full((A,), -7, dtype=torch.int32, device="cuda")
+    src2 = torch.full((A,), -7, dtype=torch.int32, device="cuda")
+    B.moe_permute(cfg, None, idx, offs2, roffs2, slot2, src2, None, B.workspace(cfg, "permute"))
+    torch.cuda.synchronize()
+    for a, b in ((offs, offs2), (roffs, roffs2), (slot, slot2), (src, src2)):
+        assert torch.equal(a, b)
+    # one of x / x_perm alone is rejected
+    with pytest.raises(RuntimeError):
+        B.moe_permute(cfg, B.to_device(x_np), idx, offs2, roffs2, slot2, src2, None,
+                      B.workspace(cfg, "permute"))

@@ -29,7 +29,7 @@ LAYER_BUF_FIELDS = ("logits", "topk_idx", "topk_w", "expert_offsets", "rank_offs
 EXPORTS = ("moe_strerror", "moe_validate", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_ffn_gate_up", "moe_ffn_down", "moe_grouped_ffn", "moe_combine", "moe_layer_fwd",
            "moe_packed_weight_bytes", "moe_pack_weights", "moe_ffn_gate_up_packed",
-           "moe_ffn_down_packed", "moe_layer_fwd_packed")
+           "moe_ffn_gate_up_packed_gather", "moe_ffn_down_packed", "moe_layer_fwd_packed")
 
 
 class MoEConfig(ctypes.Structure):
@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
         L.moe_packed_weight_bytes.argtypes = [cfgp, ctypes.POINTER(sz), ctypes.POINTER(sz)]
         L.moe_pack_weights.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
         L.moe_ffn_gate_up_packed.argtypes = [cfgp, vp, vp, vp, vp, vp]
+        L.moe_ffn_gate_up_packed_gather.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
         L.moe_ffn_down_packed.argtypes = [cfgp, vp, vp, vp, vp, vp]
         L.moe_layer_fwd_packed.argtypes = [cfgp, vp, vp, vp, vp, vp, vp,
                                            ctypes.POINTER(MoELayerBufs), vp, sz, vp]
@@ -212,10 +213,11 @@ def moe_pack_weights(cfg, w_gate, w_up, w_down, packed_gate_up, packed_down, str
 
 
 def pack_weights(cfg, w_gate, w_up, w_down, device="cuda", stream=None):
-    """Allocates the two packed images (uint8 device tensors) and fills them."""
+    """Allocates the packed images (uint8 device tensors) and fills them; an
+    image whose weights are None is neither allocated nor written (None)."""
     gu, dn = packed_weight_bytes(cfg)
-    pgu = torch.empty(gu, dtype=torch.uint8, device=device)
-    pd = torch.empty(dn, dtype=torch.uint8, device=device)
+    pgu = torch.empty(gu, dtype=torch.uint8, device=device) if w_gate is not None else None
+    pd = torch.empty(dn, dtype=torch.uint8, device=device) if w_down is not None else None
     moe_pack_weights(cfg, w_gate, w_up, w_down, pgu, pd, stream)
     return pgu, pd
 
@@ -224,6 +226,13 @@ def moe_ffn_gate_up_packed(cfg, x_perm, expert_offsets, packed_gate_up, h, strea
     _check("moe_ffn_gate_up_packed",
            lib().moe_ffn_gate_up_packed(ctypes.byref(cfg), _ptr(x_perm), _ptr(expert_offsets),
                                         _ptr(packed_gate_up), _ptr(h), _stream(stream)))
+
+
+def moe_ffn_gate_up_packed_gather(cfg, x, src_of, expert_offsets, packed_gate_up, h, stream=None):
+    _check("moe_ffn_gate_up_packed_gather",
+           lib().moe_ffn_gate_up_packed_gather(ctypes.byref(cfg), _ptr(x), _ptr(src_of),
+                                               _ptr(expert_offsets), _ptr(packed_gate_up), _ptr(h),
+                                               _stream(stream)))
 
 
 def moe_ffn_down_packed(cfg, h, expert_offsets, packed_down, y_perm, stream=None):

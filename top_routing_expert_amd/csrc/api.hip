@@ -134,11 +134,13 @@ int do_ffn(const moe_config& c, const void* xperm, const int32_t* offs, const vo
   return MOE_OK;
 }
 
-int do_ffn_packed(const moe_config& c, const void* xperm, const int32_t* offs, const void* pgu,
-                  const void* pd, void* h, void* y, hipStream_t st) {
+// src non-NULL: `act` is x in token order and the first GEMM gathers its rows.
+int do_ffn_packed(const moe_config& c, const void* act, const int32_t* src, const int32_t* offs,
+                  const void* pgu, const void* pd, void* h, void* y, hipStream_t st) {
   if (c.T == 0) return MOE_OK;
   if (pgu) {
-    hipError_t e = launch_ffn_gate_up_packed(c, xperm, offs, pgu, h, st);
+    hipError_t e = src ? launch_ffn_gate_up_packed_gather(c, act, src, offs, pgu, h, st)
+                       : launch_ffn_gate_up_packed(c, act, offs, pgu, h, st);
     if (e != hipSuccess) return MOE_EHIP;
   }
   if (pd) return status_of(launch_ffn_down_packed(c, h, offs, pd, y, st));
@@ -167,12 +169,14 @@ int do_combine(const moe_config& c, const void* y, const int32_t* slot, const fl
 }
 
 // moe_layer_fwd body shared by the row-major and packed-weight variants;
-// `ffn(x_perm, offs, h, y, stream)` runs the grouped FFN.  Routing checks and
-// the FFN's own argument checks have passed.
+// `ffn(act, src, offs, h, y, stream)` runs the grouped FFN on act = x_perm
+// (src NULL) or, with `gather` and no caller x_perm, on act = x with the rows
+// gathered through src = src_of.  Routing checks and the FFN's own argument
+// checks have passed.
 template <typename Ffn>
 int run_layer(const moe_config& c, const void* x, const void* w_router, const float* bias,
               void* out, const moe_layer_bufs* bufs, void* ws, size_t ws_bytes, void* stream,
-              Ffn&& ffn) {
+              bool gather, Ffn&& ffn) {
   const LayerLayout L = layer_layout(c, bufs);
   int s;
   if ((s = check_ws(L.total, ws, ws_bytes)) != MOE_OK) return s;
@@ -193,8 +197,11 @@ int run_layer(const moe_config& c, const void* x, const void* w_router, const fl
   void* y = pick(b.y_perm, L.y);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if ((s = do_route(c, x, w_router, bias, logits, idx, w, scratch, st)) != MOE_OK) return s;
-  if ((s = do_permute(c, x, idx, offs, roffs, slot, src, xperm, scratch, st)) != MOE_OK) return s;
-  if ((s = ffn(xperm, offs, h, y, st)) != MOE_OK) return s;
+  const bool g = gather && !b.x_perm;
+  if ((s = do_permute(c, g ? nullptr : x, idx, offs, roffs, slot, src, g ? nullptr : xperm,
+                      scratch, st)) != MOE_OK)
+    return s;
+  if ((s = ffn(g ? x : xperm, g ? src : nullptr, offs, h, y, st)) != MOE_OK) return s;
   return do_combine(c, y, slot, w, out, st);
 }
 
@@ -263,7 +270,8 @@ int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
   const moe_config& c = *cfg;
   if (!expert_offsets || !rank_offsets) return MOE_EINVAL;
   if (c.T > 0) {
-    if (!x || !topk_idx || !slot_of || !src_of || !x_perm) return MOE_EINVAL;
+    // x and x_perm both NULL: index outputs only
+    if (!topk_idx || !slot_of || !src_of || (!x != !x_perm)) return MOE_EINVAL;
     if ((s = check_ws(permute_ws_bytes(c), ws, ws_bytes)) != MOE_OK) return s;
   }
   return do_permute(c, x, topk_idx, expert_offsets, rank_offsets, slot_of, src_of, x_perm, ws,
@@ -314,8 +322,9 @@ int moe_layer_fwd(const moe_config* cfg, const void* x, const void* w_router, co
   int s = check_routing(cfg);
   if (s != MOE_OK) return s;
   if (cfg->T > 0 && (!x || !w_router || !w_gate || !w_up || !w_down || !out)) return MOE_EINVAL;
-  return run_layer(*cfg, x, w_router, bias, out, bufs, ws, ws_bytes, stream,
-                   [&](const void* xp, const int32_t* offs, void* h, void* y, hipStream_t st) {
+  return run_layer(*cfg, x, w_router, bias, out, bufs, ws, ws_bytes, stream, /*gather=*/false,
+                   [&](const void* xp, const int32_t*, const int32_t* offs, void* h, void* y,
+                       hipStream_t st) {
                      return do_ffn(*cfg, xp, offs, w_gate, w_up, w_down, h, y, st);
                    });
 }
@@ -350,7 +359,19 @@ int moe_ffn_gate_up_packed(const moe_config* cfg, const void* x_perm,
   if (cfg->T > 0 && (!x_perm || !expert_offsets || !packed_gate_up || !h || !aligned16(x_perm) ||
                      !aligned16(packed_gate_up) || !aligned16(h)))
     return MOE_EINVAL;
-  return do_ffn_packed(*cfg, x_perm, expert_offsets, packed_gate_up, nullptr, h, nullptr,
+  return do_ffn_packed(*cfg, x_perm, nullptr, expert_offsets, packed_gate_up, nullptr, h,
+                       nullptr, static_cast<hipStream_t>(stream));
+}
+
+int moe_ffn_gate_up_packed_gather(const moe_config* cfg, const void* x, const int32_t* src_of,
+                                  const int32_t* expert_offsets, const void* packed_gate_up,
+                                  void* h, void* stream) {
+  int s = check_packed(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->T > 0 && (!x || !src_of || !expert_offsets || !packed_gate_up || !h ||
+                     !aligned16(x) || !aligned16(packed_gate_up) || !aligned16(h)))
+    return MOE_EINVAL;
+  return do_ffn_packed(*cfg, x, src_of, expert_offsets, packed_gate_up, nullptr, h, nullptr,
                        static_cast<hipStream_t>(stream));
 }
 
@@ -361,8 +382,8 @@ int moe_ffn_down_packed(const moe_config* cfg, const void* h, const int32_t* exp
   if (cfg->T > 0 && (!h || !expert_offsets || !packed_down || !y_perm || !aligned16(h) ||
                      !aligned16(packed_down) || !aligned16(y_perm)))
     return MOE_EINVAL;
-  return do_ffn_packed(*cfg, nullptr, expert_offsets, nullptr, packed_down, const_cast<void*>(h),
-                       y_perm, static_cast<hipStream_t>(stream));
+  return do_ffn_packed(*cfg, nullptr, nullptr, expert_offsets, nullptr, packed_down,
+                       const_cast<void*>(h), y_perm, static_cast<hipStream_t>(stream));
 }
 
 int moe_layer_fwd_packed(const moe_config* cfg, const void* x, const void* w_router,
@@ -372,15 +393,17 @@ int moe_layer_fwd_packed(const moe_config* cfg, const void* x, const void* w_rou
   int s = check_routing(cfg);
   if (s != MOE_OK) return s;
   if ((s = check_packed(cfg)) != MOE_OK) return s;
-  if (cfg->T > 0 && (!x || !w_router || !packed_gate_up || !packed_down || !out ||
+  if (cfg->T > 0 && (!x || !w_router || !packed_gate_up || !packed_down || !out || !aligned16(x) ||
                      !aligned16(packed_gate_up) || !aligned16(packed_down)))
     return MOE_EINVAL;
   if (bufs && ((bufs->x_perm && !aligned16(bufs->x_perm)) || (bufs->h && !aligned16(bufs->h)) ||
                (bufs->y_perm && !aligned16(bufs->y_perm))))
     return MOE_EINVAL;
-  return run_layer(*cfg, x, w_router, bias, out, bufs, ws, ws_bytes, stream,
-                   [&](const void* xp, const int32_t* offs, void* h, void* y, hipStream_t st) {
-                     return do_ffn_packed(*cfg, xp, offs, packed_gate_up, packed_down, h, y, st);
+  return run_layer(*cfg, x, w_router, bias, out, bufs, ws, ws_bytes, stream, /*gather=*/true,
+                   [&](const void* act, const int32_t* src, const int32_t* offs, void* h, void* y,
+                       hipStream_t st) {
+                     return do_ffn_packed(*cfg, act, src, offs, packed_gate_up, packed_down, h, y,
+                                          st);
                    });
 }
 

@@ -76,6 +76,9 @@ hipError_t launch_pack_weights(const moe_config& c, const void* wg, const void* 
                                void* packed_gate_up, void* packed_down, hipStream_t st);
 hipError_t launch_ffn_gate_up_packed(const moe_config& c, const void* x_perm, const int32_t* offs,
                                      const void* packed_gate_up, void* h, hipStream_t st);
+hipError_t launch_ffn_gate_up_packed_gather(const moe_config& c, const void* x,
+                                            const int32_t* src_of, const int32_t* offs,
+                                            const void* pgu, void* h, hipStream_t st);
 hipError_t launch_ffn_down_packed(const moe_config& c, const void* h, const int32_t* offs,
                                   const void* packed_down, void* y, hipStream_t st);
 

@@ -264,11 +264,15 @@ struct JnSel {
 // evens out the per-block totals when tiles differ in size.  A grid of one
 // block per tile would be dispatched in block order, and an XCD whose tiles
 // run long would hold back the dispatch of every other XCD.
-template <bool GATED, int JMAX, int WF>
+//
+// GATHER: the activation rows are gathered from token order: tile row p reads
+// act row src_of[p] / gk (clamped into [0, gtokens)), so the permuted copy of
+// the activations is never written.
+template <bool GATED, int JMAX, int WF, bool GATHER>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offs,
     const u32x4* __restrict__ wp, uint16_t* __restrict__ out, int E, int N, int K, int rows,
-    int slabs, int band, bool sized) {
+    int slabs, int band, bool sized, const int32_t* __restrict__ src_of, int gk, int gtokens) {
   constexpr int TM = 32 * JMAX;
   constexpr int TN = GATED ? 128 : 256;       // output features per slab
   constexpr int HB = TM * 128;                // bytes of one 64-wide k half-stage
@@ -358,10 +362,27 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     const uint32_t tofl =
         ((uint32_t)(row0 + min(32 * (JN - 1) + trow, nrow - 1)) * (uint32_t)K + 8u * lp) * 2u;
     const size_t cstride = (size_t)64 * K;  // bytes of 32 rows
+    // GATHER: byte offset of this lane's source row for every chunk
+    uint32_t goff[GATHER ? JN : 1];
+    if constexpr (GATHER) {
+#pragma unroll
+      for (int c = 0; c < JN; ++c) {
+        const int p = row0 + min(32 * c + trow, nrow - 1);
+        const int t = min(max(src_of[p] / gk, 0), gtokens - 1);
+        goff[c] = ((uint32_t)t * (uint32_t)K + 8u * lp) * 2u;
+      }
+      // The compiler waits for its own loads with counts that do not know of
+      // the asm loads below: every offset is final before the first of them.
+#pragma unroll
+      for (int c = 0; c < JN; ++c) asm volatile("" : "+v"(goff[c]));
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     auto copy_chunk = [&](int h, int c) {
       const char* hb = abase + (size_t)min(h, hlast) * 128;
       const uint32_t lds = lds0 + (uint32_t)((h % NSLOT) * HB + (32 * c + 8 * wave) * 128);
-      if (c == JN - 1)
+      if constexpr (GATHER)
+        dma_async(hb, goff[c], lds);
+      else if (c == JN - 1)
         dma_async(hb, tofl, lds);
       else
         dma_async(hb + c * cstride, toff0, lds);
@@ -620,9 +641,10 @@ static int device_cus() {
 // the E=8/16 and E=64/256 workloads).
 constexpr int kSizedMaxExperts = 16;
 
-template <bool GATED, int JMAX, int WF>
+template <bool GATED, int JMAX, int WF, bool GATHER>
 static hipError_t launch_packed_t(const moe_config& c, const void* act, const int32_t* offs,
-                                  const void* wp, void* out, hipStream_t st) {
+                                  const void* wp, void* out, const int32_t* src_of,
+                                  hipStream_t st) {
   const long rows = (long)c.T * c.k;
   const int N = GATED ? c.f : c.d, K = GATED ? c.d : c.f;
   const PackGeom g = pack_geom(N, K, GATED);
@@ -630,10 +652,10 @@ static hipError_t launch_packed_t(const moe_config& c, const void* act, const in
   const long worst = (long)g.slabs * (WF == 2 ? 1 : 2) * worst_row_tiles(rows, c.E, 32 * JMAX);
   const long cap = ((long)device_cus() + 7) / 8 * 8;
   const int blocks = (int)std::min(cap, (worst + 7) / 8 * 8);
-  grouped_gemm_packed_kernel<GATED, JMAX, WF><<<blocks, 256, 0, st>>>(
+  grouped_gemm_packed_kernel<GATED, JMAX, WF, GATHER><<<blocks, 256, 0, st>>>(
       static_cast<const uint16_t*>(act), offs, static_cast<const u32x4*>(wp),
       static_cast<uint16_t*>(out), c.E, N, K, (int)rows, g.slabs, 8,
-      /*sized=*/c.E <= kSizedMaxExperts);
+      /*sized=*/c.E <= kSizedMaxExperts, src_of, c.k, c.T);
   return hipGetLastError();
 }
 
@@ -642,25 +664,32 @@ static hipError_t launch_packed_t(const moe_config& c, const void* act, const in
 // few experts with some hundred rows each: then half-slab tiles of up to 320
 // rows (WF = 1, JMAX = 10), which double the tile count and cover an expert of
 // up to 320 rows with one tile.
-template <bool GATED>
+template <bool GATED, bool GATHER>
 static hipError_t launch_packed(const moe_config& c, const void* act, const int32_t* offs,
-                                const void* wp, void* out, hipStream_t st) {
+                                const void* wp, void* out, const int32_t* src_of,
+                                hipStream_t st) {
   const long rows = (long)c.T * c.k;
   const PackGeom g = pack_geom(GATED ? c.f : c.d, GATED ? c.d : c.f, GATED);
   const long typical = (long)g.slabs * std::max<long>(c.E, (rows + 255) / 256);
   if (typical < 2L * device_cus())
-    return launch_packed_t<GATED, 10, 1>(c, act, offs, wp, out, st);
-  return launch_packed_t<GATED, 8, 2>(c, act, offs, wp, out, st);
+    return launch_packed_t<GATED, 10, 1, GATHER>(c, act, offs, wp, out, src_of, st);
+  return launch_packed_t<GATED, 8, 2, GATHER>(c, act, offs, wp, out, src_of, st);
 }
 
 hipError_t launch_ffn_gate_up_packed(const moe_config& c, const void* x_perm, const int32_t* offs,
                                      const void* pgu, void* h, hipStream_t st) {
-  return launch_packed<true>(c, x_perm, offs, pgu, h, st);
+  return launch_packed<true, false>(c, x_perm, offs, pgu, h, nullptr, st);
+}
+
+hipError_t launch_ffn_gate_up_packed_gather(const moe_config& c, const void* x,
+                                            const int32_t* src_of, const int32_t* offs,
+                                            const void* pgu, void* h, hipStream_t st) {
+  return launch_packed<true, true>(c, x, offs, pgu, h, src_of, st);
 }
 
 hipError_t launch_ffn_down_packed(const moe_config& c, const void* h, const int32_t* offs,
                                   const void* pd, void* y, hipStream_t st) {
-  return launch_packed<false>(c, h, offs, pd, y, st);
+  return launch_packed<false, false>(c, h, offs, pd, y, nullptr, st);
 }
 
 }  // namespace moe

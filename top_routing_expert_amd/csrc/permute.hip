@@ -21,7 +21,8 @@
 //     blocks win).
 //  3. scatter: one wave per token computes its k slots, writes slot_of /
 //     src_of, reads the token row once and stores it to its k slots with
-//     16-byte vector accesses (x is read once; x_perm written once).
+//     16-byte vector accesses (x is read once; x_perm written once).  With no
+//     x_perm it writes the indices only.
 #include "common.h"
 
 namespace moe {
@@ -214,6 +215,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
     slot_of[(size_t)t * k + lane] = p;
     src_of[p] = t * k + lane;
   }
+  if (!x_perm) return;  // index outputs only (the first GEMM gathers the rows)
   int pj[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) pj[j] = __shfl(p, j);
