@@ -3,7 +3,10 @@
 
 One step = one pass of the whole path over one batch of synthetic tokens:
 moe_route -> moe_permute -> moe_ffn_gate_up -> moe_ffn_down -> moe_combine,
-each a C-ABI call that enqueues the HIP kernels on the current stream.
+each a C-ABI call that enqueues the HIP kernels on the current stream.  With
+the packed FFN the dispatch's row gather runs inside the first GEMM by default
+(moe_permute writes the indices, moe_ffn_gate_up_packed_gather reads the token
+rows through src_of); --dispatch copy materialises x_perm first.
 Inputs are resident in HBM before timing starts.  W warm-up steps, then K
 timed steps bracketed by device synchronisation; HIP events recorded on the
 same stream between the calls give each kernel's average duration inside the
@@ -66,6 +69,9 @@ def parse():
     ap.add_argument("--ffn", choices=sorted(FFN_KERNELS), default="packed",
                     help="expert-weight layout of the grouped FFN: packed once at load time "
                          "(moe_pack_weights) or the plain [E,f,d] / [E,d,f] arrays")
+    ap.add_argument("--dispatch", choices=("gather", "copy"), default="gather",
+                    help="packed FFN: gather the token rows inside the first GEMM (the dispatch "
+                         "writes indices only) or copy them to x_perm first")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     a = ap.parse_args()
@@ -76,16 +82,19 @@ def parse():
     return a
 
 
-def algorithmic(shape, counts):
-    """Algorithmic HBM bytes and flops of one launch of every phase."""
+def algorithmic(shape, counts, gather=False):
+    """Algorithmic HBM bytes and flops of one launch of every phase.  With the
+    gather fused into the first GEMM, the dispatch writes indices only and the
+    first GEMM reads the token rows (and src_of) instead of x_perm."""
     s = 2 if shape.dtype == "bf16" else 4
     T, d, E, k, f = shape.T, shape.d, shape.E, shape.k, shape.f
     A = T * k
     e_nz = int((counts > 0).sum())
     return {
         "route": dict(bytes=T * d * s + E * d * s + T * E * 4 + 8 * A, flops=2 * T * d * E),
-        "permute": dict(bytes=T * d * s + A * d * s + 4 * A + 8 * A + 8 * (E + 1), flops=0),
-        "ffn_gate_up": dict(bytes=2 * e_nz * f * d * s + A * d * s + A * f * s,
+        "permute": dict(bytes=(0 if gather else T * d * s + A * d * s) + 4 * A + 8 * A + 8 * (E + 1),
+                        flops=0),
+        "ffn_gate_up": dict(bytes=2 * e_nz * f * d * s + A * d * s + A * f * s + (4 * A if gather else 0),
                             flops=2 * A * d * 2 * f),
         "ffn_down": dict(bytes=e_nz * d * f * s + A * f * s + A * d * s, flops=2 * A * f * d),
         "combine": dict(bytes=A * d * s + T * d * s + 8 * A, flops=2 * A * d),
@@ -105,10 +114,10 @@ def roofline_of(work, ms):
                 frac=tfl / PEAK_BF16_TFLOPS, gbs=gbs, hbm_frac=gbs / PEAK_HBM_GBS, ai=ai)
 
 
-def measured_traffic(ffn, workload):
+def measured_traffic(ffn, workload, dispatch):
     """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None if there is none, it is for another workload, or the
-    kernel source changed since."""
+    summary, or None if there is none, it is for another workload or dispatch
+    mode, or the kernel source changed since."""
     traffic_file, kernel_srcs, _ = FFN_KERNELS[ffn]
     try:
         with open(traffic_file) as fh:
@@ -116,7 +125,8 @@ def measured_traffic(ffn, workload):
         h = kernel_sources_sha256(kernel_srcs)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_src_sha256") != h or t.get("workload") != workload:
+    if (t.get("kernel_src_sha256") != h or t.get("workload") != workload or
+            t.get("dispatch", "copy") != dispatch):
         return None
     return t.get("bytes_per_launch")
 
@@ -169,6 +179,9 @@ def main():
     shape = a.shape
     if shape.dtype != "bf16":
         a.ffn = "rowmajor"  # packed images are bf16 only
+    if a.ffn != "packed":
+        a.dispatch = "copy"  # the gather is a packed-FFN kernel
+    gather = a.dispatch == "gather"
     log(f"workload {shape.name}: generating inputs")
     from top_routing_expert_amd import configs as C
     inp = I.make_inputs(shape, seed=C.CONFIGS.index(shape) + 1)
@@ -185,7 +198,7 @@ def main():
         roffs=torch.empty(R + 1, dtype=torch.int32, device="cuda"),
         slot=torch.empty(A, dtype=torch.int32, device="cuda"),
         src=torch.empty(A, dtype=torch.int32, device="cuda"),
-        xp=torch.empty((A, d), dtype=dt, device="cuda"),
+        xp=None if gather else torch.empty((A, d), dtype=dt, device="cuda"),
         h=torch.empty((A, f), dtype=dt, device="cuda"),
         y=torch.empty((A, d), dtype=dt, device="cuda"),
         out=torch.empty((T, d), dtype=dt, device="cuda"),
@@ -198,9 +211,14 @@ def main():
         pgu, pd = B.pack_weights(cfg, dev["w_gate"], dev["w_up"], dev["w_down"], stream=stream)
         torch.cuda.synchronize()
         dev["w_gate"] = dev["w_up"] = dev["w_down"] = None
+        if a.dispatch == "gather":
+            gate_up = lambda: B.moe_ffn_gate_up_packed_gather(cfg, dev["x"], buf["src"],
+                                                               buf["offs"], pgu, buf["h"], stream)
+        else:
+            gate_up = lambda: B.moe_ffn_gate_up_packed(cfg, buf["xp"], buf["offs"], pgu,
+                                                        buf["h"], stream)
         ffn_calls = {
-            "ffn_gate_up": lambda: B.moe_ffn_gate_up_packed(cfg, buf["xp"], buf["offs"], pgu,
-                                                            buf["h"], stream),
+            "ffn_gate_up": gate_up,
             "ffn_down": lambda: B.moe_ffn_down_packed(cfg, buf["h"], buf["offs"], pd, buf["y"],
                                                       stream),
         }
@@ -215,8 +233,9 @@ def main():
     calls = {
         "route": lambda: B.moe_route(cfg, dev["x"], dev["w_router"], dev["bias"], buf["logits"],
                                      buf["idx"], buf["w"], ws_r, stream),
-        "permute": lambda: B.moe_permute(cfg, dev["x"], buf["idx"], buf["offs"], buf["roffs"],
-                                         buf["slot"], buf["src"], buf["xp"], ws_p, stream),
+        "permute": lambda: B.moe_permute(cfg, None if gather else dev["x"], buf["idx"], buf["offs"],
+                                         buf["roffs"], buf["slot"], buf["src"],
+                                         None if gather else buf["xp"], ws_p, stream),
         **ffn_calls,
         "combine": lambda: B.moe_combine(cfg, buf["y"], buf["slot"], buf["w"], buf["out"], stream),
     }
@@ -246,10 +265,10 @@ def main():
     phase_ms = {p: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
                                   for s in range(a.steps)])) for i, p in enumerate(PHASES)}
     ms_per_step = elapsed * 1e3 / a.steps
-    work = algorithmic(shape, counts)
+    work = algorithmic(shape, counts, gather)
     phases = {p: dict(ms=phase_ms[p], **roofline_of(work[p], phase_ms[p])) for p in PHASES}
     dom = phases[DOMINANT]
-    traffic = measured_traffic(a.ffn, shape.name)
+    traffic = measured_traffic(a.ffn, shape.name, a.dispatch)
     roofline = {"bound": dom["bound"], "achieved": round(dom["achieved"], 3),
                 "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4),
                 "traffic": traffic, "kernel": FFN_KERNELS[a.ffn][2],
@@ -276,7 +295,7 @@ def main():
         "config": {"workload": shape.name, "T": T, "d": d, "E": E, "k": k, "f": f,
                    "n_group": shape.n_group, "topk_group": shape.topk_group,
                    "presel": shape.presel, "renorm": shape.renorm, "ep_ranks": R,
-                   "ffn_weights": a.ffn, "parallelism": "single GPU"},
+                   "ffn_weights": a.ffn, "dispatch": a.dispatch, "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "phases": {p: {kk: (round(v, 5) if isinstance(v, float) else v) for kk, v in ph.items()}
