@@ -220,6 +220,58 @@ def permute(topk_idx, E: int, ep_ranks: int = 1) -> dict:
     }
 
 
+# ----------------------------------------------------------------------------
+# Routing diagnostics (by-products of a2 / a3)
+# ----------------------------------------------------------------------------
+def route_stats(logits32, bias, topk_idx, E: int, ep_ranks: int = 1, presel: int = 0) -> dict:
+    """Load-balance diagnostics of one batch's routing.
+
+    [SyncTax] §5.1 reports the activation frequency of every expert and the
+    entropy of the routing as its load-balance measure (ideal log2 E bits:
+    4.0 for 16 experts); [EP-V4] §6.2 reports per-expert activation shares
+    against the ideal 1/E.  Readings (the pages give no formulas): the
+    histogram is the number of (token, choice) pairs per expert (the
+    dispatch's c_e); the load entropy is -sum_e q_e log2 q_e over the shares
+    q_e = c_e / (T k), terms with q_e = 0 dropped; the maximum load ratio is
+    E * max_e c_e / (T k) (1 = perfectly even); the per-rank load sums the
+    histogram over each rank's contiguous block of E/R experts.  The token
+    entropy is the mean over tokens of -sum_e p_e log2 p_e, p = softmax over
+    all E experts of the fp32 scores s = z + b; the pre-selection gap
+    (presel P > 0) is the mean over tokens of the softmax mass outside the P
+    pre-selected experts (order: s desc, e asc), i.e. what the partial
+    softmax over P leaves out.  A batch of no tokens gives zeros.
+    """
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    T = idx.shape[0]
+    hist = np.bincount(idx.reshape(-1), minlength=E)[:E]
+    rank_load = hist.reshape(ep_ranks, E // ep_ranks).sum(axis=1)
+    A = idx.size
+    load_entropy = max_ratio = token_entropy = gap = 0.0
+    if A:
+        q = hist / A
+        nz = q > 0
+        load_entropy = float(-(q[nz] * np.log2(q[nz])).sum())
+        max_ratio = float(E * hist.max() / A)
+    if T:
+        s = scores(logits32, bias).astype(np.float64)
+        ex = np.exp(s - s.max(axis=1, keepdims=True))
+        p = ex / ex.sum(axis=1, keepdims=True)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            plogp = np.where(p > 0, p * np.log2(p), 0.0)
+        token_entropy = float((-plogp.sum(axis=1)).mean())
+        if presel:
+            top = _order_desc(s)[:, :presel]
+            gap = float((1.0 - np.take_along_axis(p, top, axis=1).sum(axis=1)).mean())
+    return {
+        "hist": hist.astype(np.int32),
+        "rank_load": rank_load.astype(np.int32),
+        "token_entropy_bits": token_entropy,
+        "presel_gap": gap,
+        "load_entropy_bits": load_entropy,
+        "max_load_ratio": max_ratio,
+    }
+
+
 def gather_rows(x, src_of, k: int) -> np.ndarray:
     """x_perm[p] = x[src_of[p] // k]: a plain row copy (bit patterns kept)."""
     return np.asarray(x)[np.asarray(src_of) // k]

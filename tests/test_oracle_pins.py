@@ -300,6 +300,43 @@ def pin_routing_statistics():
     assert g["max_entropy_bits_E16"] - 0.01 < ent <= g["max_entropy_bits_E16"] + 1e-12
 
 
+def pin_route_stats_closed_forms():
+    g = _golden("routing_statistics.json")
+    # equal scores: softmax is 1/E, entropy log2 E, the top-P keep P/E of the mass
+    z = np.zeros((5, 16), np.float32)
+    idx = np.tile(np.arange(16, dtype=np.int32).reshape(8, 2), (1, 1))[:5]
+    r = om.route_stats(z, None, idx, 16, presel=4)
+    assert r["token_entropy_bits"] == pytest.approx(g["max_entropy_bits_E16"], abs=1e-12)
+    assert r["presel_gap"] == pytest.approx(0.75, abs=1e-12)
+    # one dominant expert: entropy and gap vanish
+    z = np.zeros((3, 8), np.float32)
+    z[:, 3] = 60.0
+    r = om.route_stats(z, None, np.array([[3, 0]] * 3, np.int32), 8, presel=1)
+    assert r["token_entropy_bits"] < 1e-20 and r["presel_gap"] < 1e-20
+    # the bias enters the scores: a bias that cancels z gives equal scores
+    zb = np.array([[1.0, -1.0, 0.5, 0.0]], np.float32)
+    r = om.route_stats(zb, -zb[0], np.array([[0, 1]], np.int32), 4, presel=2)
+    assert r["token_entropy_bits"] == pytest.approx(2.0, abs=1e-12)
+    assert r["presel_gap"] == pytest.approx(0.5, abs=1e-12)
+    # an even histogram: load entropy log2 E (the pages' ideal: 4.0 bits for
+    # 16 experts), every share 1/E, maximum load ratio 1
+    idx = np.arange(64, dtype=np.int32).reshape(32, 2) % 16
+    r = om.route_stats(np.zeros((32, 16), np.float32), None, idx, 16, ep_ranks=4)
+    assert r["load_entropy_bits"] == pytest.approx(g["max_entropy_bits_E16"], abs=1e-12)
+    assert r["max_load_ratio"] == pytest.approx(1.0)
+    assert r["hist"].tolist() == [4] * 16 and r["rank_load"].tolist() == [16] * 4
+    # every token on the same k = 2 experts: log2 k bits, ratio E / k
+    idx = np.tile(np.array([[5, 9]], np.int32), (7, 1))
+    r = om.route_stats(np.zeros((7, 12), np.float32), None, idx, 12, ep_ranks=3)
+    assert r["load_entropy_bits"] == pytest.approx(1.0, abs=1e-12)
+    assert r["max_load_ratio"] == pytest.approx(6.0)
+    assert r["hist"][5] == 7 and r["hist"][9] == 7 and r["hist"].sum() == 14
+    assert r["rank_load"].tolist() == [0, 7, 7]
+    # no tokens: zeros
+    r = om.route_stats(np.zeros((0, 4), np.float32), None, np.zeros((0, 2), np.int32), 4)
+    assert r["load_entropy_bits"] == 0.0 and r["token_entropy_bits"] == 0.0
+
+
 def pin_widen_bf16():
     bits = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x4049, 0x7F7F], np.uint16)
     got = om.widen_bf16(bits)
@@ -375,6 +412,19 @@ def _gates_no_max_exp_sign(s, sel, k, presel=0, renorm=1):
 
 _ORIG = {n: getattr(om, n) for n in ("gates", "permute", "combine")}
 
+def _route_stats_natural_log(logits32, bias, topk_idx, E, ep_ranks=1, presel=0):
+    r = _ORIG_ROUTE_STATS(logits32, bias, topk_idx, E, ep_ranks, presel)
+    r["load_entropy_bits"] *= np.log(2.0)
+    r["token_entropy_bits"] *= np.log(2.0)
+    return r
+
+
+def _route_stats_first_choice_only(logits32, bias, topk_idx, E, ep_ranks=1, presel=0):
+    return _ORIG_ROUTE_STATS(logits32, bias, np.asarray(topk_idx)[:, :1], E, ep_ranks, presel)
+
+
+_ORIG_ROUTE_STATS = om.route_stats
+
 MUTANTS = {
     "ties-to-highest-index": ("_order_desc", _ties_to_highest),
     "bias-dropped": ("scores", _scores_without_bias),
@@ -385,6 +435,8 @@ MUTANTS = {
     "group-score-mean": ("_eligible", _eligible_mean_group),
     "rank-offsets-wrong": ("permute", _rank_offsets_by_rank_index),
     "gates-reversed": ("gates", _gates_no_max_exp_sign),
+    "stats-entropy-in-nats": ("route_stats", _route_stats_natural_log),
+    "stats-histogram-first-choice": ("route_stats", _route_stats_first_choice_only),
 }
 
 
