@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--dispatch", choices=("gather", "copy"), default="gather",
                     help="packed FFN: gather the token rows inside the first GEMM (the dispatch "
                          "writes indices only) or copy them to x_perm first")
+    ap.add_argument("--diagnostics", action="store_true",
+                    help="also time the routing diagnostics (moe_route_stats) after the dispatch; "
+                         "reported as its own phase and included in the step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     a = ap.parse_args()
@@ -98,6 +101,8 @@ def algorithmic(shape, counts, gather=False):
                             flops=2 * A * d * 2 * f),
         "ffn_down": dict(bytes=e_nz * d * f * s + A * f * s + A * d * s, flops=2 * A * f * d),
         "combine": dict(bytes=A * d * s + T * d * s + 8 * A, flops=2 * A * d),
+        # logits read once (plus the bias), per-token partials out and back, offsets in
+        "route_stats": dict(bytes=T * E * 4 + E * 4 + 16 * T + 8 * (E + 1), flops=0),
     }
 
 
@@ -239,11 +244,21 @@ def main():
         **ffn_calls,
         "combine": lambda: B.moe_combine(cfg, buf["y"], buf["slot"], buf["w"], buf["out"], stream),
     }
+    phases_run = PHASES
+    if a.diagnostics:
+        buf["hist"] = torch.empty(E, dtype=torch.int32, device="cuda")
+        buf["rload"] = torch.empty(R, dtype=torch.int32, device="cuda")
+        buf["stats"] = torch.empty(4, dtype=torch.float32, device="cuda")
+        ws_s = B.workspace(cfg, "route_stats")
+        calls["route_stats"] = lambda: B.moe_route_stats(cfg, buf["logits"], dev["bias"], buf["offs"],
+                                                         buf["roffs"], buf["hist"], buf["rload"],
+                                                         buf["stats"], ws_s, stream)
+        phases_run = PHASES[:2] + ("route_stats",) + PHASES[2:]
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        for i, p in enumerate(PHASES):
+        for i, p in enumerate(phases_run):
             calls[p]()
             if ev is not None:
                 ev[i + 1].record(stream)
@@ -253,7 +268,7 @@ def main():
         step()
     torch.cuda.synchronize()
     counts = np.diff(B.to_host_bits(buf["offs"]).astype(np.int64))
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(PHASES) + 1)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases_run) + 1)]
               for _ in range(a.steps)]
     log(f"timing {a.steps} steps")
     torch.cuda.synchronize()
@@ -263,10 +278,10 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     phase_ms = {p: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
-                                  for s in range(a.steps)])) for i, p in enumerate(PHASES)}
+                                  for s in range(a.steps)])) for i, p in enumerate(phases_run)}
     ms_per_step = elapsed * 1e3 / a.steps
     work = algorithmic(shape, counts, gather)
-    phases = {p: dict(ms=phase_ms[p], **roofline_of(work[p], phase_ms[p])) for p in PHASES}
+    phases = {p: dict(ms=phase_ms[p], **roofline_of(work[p], phase_ms[p])) for p in phases_run}
     dom = phases[DOMINANT]
     traffic = measured_traffic(a.ffn, shape.name, a.dispatch)
     roofline = {"bound": dom["bound"], "achieved": round(dom["achieved"], 3),

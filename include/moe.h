@@ -75,7 +75,8 @@ enum moe_entry {
   MOE_ENTRY_PERMUTE = 2,
   MOE_ENTRY_FFN = 3,
   MOE_ENTRY_COMBINE = 4,
-  MOE_ENTRY_LAYER = 5
+  MOE_ENTRY_LAYER = 5,
+  MOE_ENTRY_ROUTE_STATS = 6
 };
 
 /*
@@ -280,6 +281,30 @@ int moe_ffn_gate_up_packed(const moe_config* cfg, const void* x_perm,
                            void* stream);
 int moe_ffn_down_packed(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
                         const void* packed_down, void* y_perm, void* stream);
+
+/*
+ * Routing diagnostics of one batch: the load-balance report of [SyncTax] §5.1
+ * (per-expert activation frequency; the entropy of the routing, ideal log2 E
+ * bits) and [EP-V4] §6.2 (per-expert activation shares, ideal 1/E).
+ *   logits         [T, E] fp32 in: z as moe_route wrote it (before the bias).
+ *   bias           [E] fp32 in or NULL (the same as for moe_route).
+ *   expert_offsets [E+1], rank_offsets [R+1] int32 in: from moe_permute.
+ *   hist           [E] int32 out: (token, choice) pairs per expert.
+ *   rank_load      [R] int32 out: pairs per rank (contiguous blocks of E/R).
+ *   stats          [4] fp32 out:
+ *     [0] mean over tokens of -sum_e p_e log2 p_e, p = softmax over all E
+ *         experts of the fp32 scores s = z + b;
+ *     [1] mean over tokens of the softmax mass outside the presel experts
+ *         ranked first by (s desc, e asc) -- what the partial softmax over
+ *         the pre-selection leaves out; 0 when presel = 0;
+ *     [2] -sum_e q_e log2 q_e, q = hist / (T k), zero shares dropped;
+ *     [3] E * max_e hist[e] / (T k) (1 = perfectly even).
+ *   ws: moe_workspace_bytes(MOE_ENTRY_ROUTE_STATS).  T = 0 writes zeros.
+ *   The sums run in a fixed order: the report is bitwise reproducible.
+ */
+int moe_route_stats(const moe_config* cfg, const float* logits, const float* bias,
+                    const int32_t* expert_offsets, const int32_t* rank_offsets, int32_t* hist,
+                    int32_t* rank_load, float* stats, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_ffn_gate_up_packed with the dispatch gather fused into the first GEMM's

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi35
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3
 MOE_F32, MOE_BF16 = 0, 1
-ENTRY = {"route": 1, "permute": 2, "ffn": 3, "combine": 4, "layer": 5}
+ENTRY = {"route": 1, "permute": 2, "ffn": 3, "combine": 4, "layer": 5, "route_stats": 6}
 
 CONFIG_FIELDS = ("T", "d", "E", "k", "f", "n_group", "topk_group", "presel", "renorm",
                  "ep_ranks", "dtype")
@@ -29,7 +29,8 @@ LAYER_BUF_FIELDS = ("logits", "topk_idx", "topk_w", "expert_offsets", "rank_offs
 EXPORTS = ("moe_strerror", "moe_validate", "moe_workspace_bytes", "moe_route", "moe_permute",
            "moe_ffn_gate_up", "moe_ffn_down", "moe_grouped_ffn", "moe_combine", "moe_layer_fwd",
            "moe_packed_weight_bytes", "moe_pack_weights", "moe_ffn_gate_up_packed",
-           "moe_ffn_gate_up_packed_gather", "moe_ffn_down_packed", "moe_layer_fwd_packed")
+           "moe_ffn_gate_up_packed_gather", "moe_ffn_down_packed", "moe_layer_fwd_packed",
+           "moe_route_stats")
 
 
 class MoEConfig(ctypes.Structure):
@@ -74,6 +75,7 @@ def lib() -> ctypes.CDLL:
         L.moe_pack_weights.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
         L.moe_ffn_gate_up_packed.argtypes = [cfgp, vp, vp, vp, vp, vp]
         L.moe_ffn_gate_up_packed_gather.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
+        L.moe_route_stats.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_ffn_down_packed.argtypes = [cfgp, vp, vp, vp, vp, vp]
         L.moe_layer_fwd_packed.argtypes = [cfgp, vp, vp, vp, vp, vp, vp,
                                            ctypes.POINTER(MoELayerBufs), vp, sz, vp]
@@ -233,6 +235,15 @@ def moe_ffn_gate_up_packed_gather(cfg, x, src_of, expert_offsets, packed_gate_up
            lib().moe_ffn_gate_up_packed_gather(ctypes.byref(cfg), _ptr(x), _ptr(src_of),
                                                _ptr(expert_offsets), _ptr(packed_gate_up), _ptr(h),
                                                _stream(stream)))
+
+
+def moe_route_stats(cfg, logits, bias, expert_offsets, rank_offsets, hist, rank_load, stats,
+                    ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check("moe_route_stats",
+           lib().moe_route_stats(ctypes.byref(cfg), _ptr(logits), _ptr(bias), _ptr(expert_offsets),
+                                 _ptr(rank_offsets), _ptr(hist), _ptr(rank_load), _ptr(stats), wp,
+                                 wn, _stream(stream)))
 
 
 def moe_ffn_down_packed(cfg, h, expert_offsets, packed_down, y_perm, stream=None):

@@ -242,6 +242,10 @@ int moe_workspace_bytes(const moe_config* cfg, int entry, size_t* bytes) {
       if ((s = check_routing(cfg)) != MOE_OK) return s;
       *bytes = layer_layout(*cfg, nullptr).total;
       return MOE_OK;
+    case MOE_ENTRY_ROUTE_STATS:
+      if ((s = check_routing(cfg)) != MOE_OK) return s;
+      *bytes = cfg->T ? align256(route_stats_ws_bytes(*cfg)) : 0;
+      return MOE_OK;
     default:
       return MOE_EINVAL;
   }
@@ -361,6 +365,20 @@ int moe_ffn_gate_up_packed(const moe_config* cfg, const void* x_perm,
     return MOE_EINVAL;
   return do_ffn_packed(*cfg, x_perm, nullptr, expert_offsets, packed_gate_up, nullptr, h,
                        nullptr, static_cast<hipStream_t>(stream));
+}
+
+int moe_route_stats(const moe_config* cfg, const float* logits, const float* bias,
+                    const int32_t* expert_offsets, const int32_t* rank_offsets, int32_t* hist,
+                    int32_t* rank_load, float* stats, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_routing(cfg);
+  if (s != MOE_OK) return s;
+  if (!hist || !rank_load || !stats) return MOE_EINVAL;
+  if (cfg->T > 0) {
+    if (!logits || !expert_offsets || !rank_offsets) return MOE_EINVAL;
+    if ((s = check_ws(route_stats_ws_bytes(*cfg), ws, ws_bytes)) != MOE_OK) return s;
+  }
+  return status_of(launch_route_stats(*cfg, logits, bias, expert_offsets, rank_offsets, hist,
+                                      rank_load, stats, ws, static_cast<hipStream_t>(stream)));
 }
 
 int moe_ffn_gate_up_packed_gather(const moe_config* cfg, const void* x, const int32_t* src_of,

@@ -82,6 +82,10 @@ hipError_t launch_ffn_gate_up_packed_gather(const moe_config& c, const void* x,
 hipError_t launch_ffn_down_packed(const moe_config& c, const void* h, const int32_t* offs,
                                   const void* packed_down, void* y, hipStream_t st);
 
+size_t route_stats_ws_bytes(const moe_config& c);
+hipError_t launch_route_stats(const moe_config& c, const float* logits, const float* bias,
+                              const int32_t* offs, const int32_t* roffs, int32_t* hist,
+                              int32_t* rank_load, float* stats, void* ws, hipStream_t st);
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_of,
                           const float* topk_w, void* out, hipStream_t st);
 
