@@ -272,6 +272,77 @@ def route_stats(logits32, bias, topk_idx, E: int, ep_ranks: int = 1, presel: int
     }
 
 
+# ----------------------------------------------------------------------------
+# Per-token FP8 compression of the dispatch payload ([SyncTax] §3.1)
+# ----------------------------------------------------------------------------
+F8_MAX = 448.0  # largest finite E4M3 value: 1.75 * 2^8
+
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+    infinities, S.1111.111 = NaN) -> float64, exactly."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e4 = (c >> 3) & 0xF
+    m3 = c & 0x7
+    mag = np.where(e4 == 0, m3 * 2.0 ** -9, (1.0 + m3 / 8.0) * np.exp2(e4 - 7.0))
+    return sign * mag
+
+
+def fp8_e4m3_encode(v) -> np.ndarray:
+    """float32 values with |v| <= 448 -> E4M3 codes, rounding to nearest,
+    ties to the even code.  Below 2^-6 the step is 2^-9 (subnormals); in the
+    binade [2^e, 2^(e+1)) it is 2^(e-3).  Every step is exact in float32."""
+    v = np.asarray(v, dtype=np.float32)
+    sign = np.signbit(v).astype(np.int64) << 7
+    a = np.abs(v).astype(np.float32)
+    sub = a < np.float32(2.0 ** -6)
+    m_sub = np.rint(a * np.float32(512.0)).astype(np.int64)        # 0 .. 8 (8 = 2^-6)
+    f, E = np.frexp(a)                                              # a = f 2^E, f in [0.5, 1)
+    e = E.astype(np.int64) - 1
+    mant = np.ldexp(f, 1).astype(np.float32)                        # [1, 2)
+    m = np.rint((mant - np.float32(1.0)) * np.float32(8.0)).astype(np.int64)
+    up = m == 8
+    e = np.where(up, e + 1, e)
+    m = np.where(up, 0, m)
+    normal = ((e + 7) << 3) | m
+    return (np.where(sub, m_sub, normal) | sign).astype(np.uint8)
+
+
+def round_bf16(v32) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (finite values)."""
+    b = np.asarray(v32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def quantize_rows_fp8(x_bits) -> tuple:
+    """Per-token affine FP8: each row's [min, max] is mapped onto [-448, 448]
+    ([SyncTax] §3.1: every token's vector gets its own min/max and an affine
+    map, so one outlier does not widen every token's range).  Readings: the
+    centre z = (max + min) / 2 and the scale s = ((max - min) / 2) / 448 are
+    float32, v = (x - z) / s in float32 (0 for a constant row, s = 0), clamped
+    to +-448 and rounded to E4M3 by fp8_e4m3_encode.  Returns (codes uint8
+    [T, d], scale float32 [T], zero float32 [T])."""
+    x = widen_bf16(np.asarray(x_bits, dtype=np.uint16)).astype(np.float32)
+    hi = x.max(axis=1)
+    lo = x.min(axis=1)
+    z = ((hi + lo) * np.float32(0.5)).astype(np.float32)
+    hr = ((hi - lo) * np.float32(0.5)).astype(np.float32)
+    s = (hr / np.float32(F8_MAX)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = np.where(s[:, None] > 0, (x - z[:, None]) / s[:, None], np.float32(0.0)).astype(np.float32)
+    v = np.clip(v, np.float32(-F8_MAX), np.float32(F8_MAX))
+    return fp8_e4m3_encode(v), s, z
+
+
+def dequantize_rows_fp8(codes, scale, zero) -> np.ndarray:
+    """x^ = code * s + z (float32 multiply, then float32 add), rounded to bf16."""
+    q = fp8_e4m3_decode(codes).astype(np.float32)
+    s = np.asarray(scale, np.float32)[:, None]
+    z = np.asarray(zero, np.float32)[:, None]
+    return round_bf16(((q * s).astype(np.float32) + z).astype(np.float32))
+
+
 def gather_rows(x, src_of, k: int) -> np.ndarray:
     """x_perm[p] = x[src_of[p] // k]: a plain row copy (bit patterns kept)."""
     return np.asarray(x)[np.asarray(src_of) // k]

@@ -337,6 +337,51 @@ def pin_route_stats_closed_forms():
     assert r["load_entropy_bits"] == 0.0 and r["token_entropy_bits"] == 0.0
 
 
+def pin_fp8_e4m3_codes():
+    """The E4M3 format's own fixed points and rounding ([SyncTax] §3.1 FP8)."""
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    vals = om.fp8_e4m3_decode(finite)
+    # every finite code encodes its own value back (-0 keeps its sign bit)
+    assert np.array_equal(om.fp8_e4m3_encode(vals.astype(np.float32)), finite)
+    # the magnitudes are strictly increasing with the code
+    pos = vals[finite < 0x80]
+    assert np.all(np.diff(pos) > 0)
+    fixed = {448.0: 0x7E, -448.0: 0xFE, 1.0: 0x38, 2.0 ** -9: 0x01, 2.0 ** -6: 0x08,
+             0.9375: 0x37, 240.0: 0x77, 0.0: 0x00}
+    for v, c in fixed.items():
+        assert int(om.fp8_e4m3_encode(np.float32(v))) == c, (v, c)
+    # ties go to the even code: 1 + 1/16 -> 1.0, 1 + 3/16 -> 1.25, 2^-10 -> 0, 3 2^-10 -> 2^-8
+    ties = {1.0625: 0x38, 1.1875: 0x3A, 2.0 ** -10: 0x00, 3 * 2.0 ** -10: 0x02}
+    for v, c in ties.items():
+        assert int(om.fp8_e4m3_encode(np.float32(v))) == c, (v, c)
+
+
+def pin_fp8_row_quantization():
+    bits = om.round_bf16(np.array([[-3.0, 5.0, 1.0, 2.0], [0.75] * 4], np.float32))
+    codes, s, z = om.quantize_rows_fp8(bits)
+    # row 0: centre 1, half-range 4: the extremes land on -+448, the centre on 0
+    assert z[0] == 1.0 and s[0] == np.float32(4.0) / np.float32(448.0)
+    assert codes[0, 0] == 0xFE and codes[0, 1] == 0x7E and codes[0, 2] == 0x00
+    # 2.0 maps to 112 = 1.75 * 2^6 (E4M3 exact)
+    assert codes[0, 3] == 0x6E
+    # a constant row: scale 0, codes 0, and it comes back exactly
+    assert s[1] == 0.0 and not codes[1].any()
+    back = om.dequantize_rows_fp8(codes, s, z)
+    assert np.array_equal(back[1], bits[1])
+    # bf16 rounding of the decode: even ties
+    assert om.round_bf16(np.float32(1.0 + 2.0 ** -8)).item() == 0x3F80
+    assert om.round_bf16(np.float32(1.0 + 3 * 2.0 ** -8)).item() == 0x3F82
+    # error bound on random rows: E4M3 keeps 3 mantissa bits of v, so
+    # |x - x^| <= half-range / 16 (plus the bf16 rounding of x^)
+    rng = np.random.default_rng(5)
+    x = om.round_bf16(rng.standard_normal((64, 96)).astype(np.float32))
+    codes, s, z = om.quantize_rows_fp8(x)
+    xf = om.widen_bf16(x)
+    xr = om.widen_bf16(om.dequantize_rows_fp8(codes, s, z))
+    hr = s.astype(np.float64) * 448.0
+    assert np.all(np.abs(xr - xf) <= hr[:, None] / 16 + np.abs(xf) * 2.0 ** -8 + 1e-30)
+
+
 def pin_widen_bf16():
     bits = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x4049, 0x7F7F], np.uint16)
     got = om.widen_bf16(bits)
@@ -425,6 +470,30 @@ def _route_stats_first_choice_only(logits32, bias, topk_idx, E, ep_ranks=1, pres
 
 _ORIG_ROUTE_STATS = om.route_stats
 
+
+def _fp8_round_half_up(v):
+    v = np.asarray(v, np.float32)
+    orig = np.rint
+    try:
+        np_rint = lambda y: np.floor(np.asarray(y) + np.float32(0.5))
+        om.np.rint = np_rint
+        return _ORIG_FP8_ENCODE(v)
+    finally:
+        om.np.rint = orig
+
+
+def _quantize_full_range_scale(x_bits):
+    x = om.widen_bf16(np.asarray(x_bits, dtype=np.uint16)).astype(np.float32)
+    hi, lo = x.max(1), x.min(1)
+    z = ((hi + lo) * np.float32(0.5)).astype(np.float32)
+    s = ((hi - lo) / np.float32(448.0)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = np.where(s[:, None] > 0, (x - z[:, None]) / s[:, None], np.float32(0.0)).astype(np.float32)
+    return om.fp8_e4m3_encode(np.clip(v, -448, 448)), s, z
+
+
+_ORIG_FP8_ENCODE = om.fp8_e4m3_encode
+
 MUTANTS = {
     "ties-to-highest-index": ("_order_desc", _ties_to_highest),
     "bias-dropped": ("scores", _scores_without_bias),
@@ -437,6 +506,8 @@ MUTANTS = {
     "gates-reversed": ("gates", _gates_no_max_exp_sign),
     "stats-entropy-in-nats": ("route_stats", _route_stats_natural_log),
     "stats-histogram-first-choice": ("route_stats", _route_stats_first_choice_only),
+    "fp8-round-half-up": ("fp8_e4m3_encode", _fp8_round_half_up),
+    "fp8-scale-full-range": ("quantize_rows_fp8", _quantize_full_range_scale),
 }
 
 
