@@ -69,9 +69,10 @@ def parse():
     ap.add_argument("--ffn", choices=sorted(FFN_KERNELS), default="packed",
                     help="expert-weight layout of the grouped FFN: packed once at load time "
                          "(moe_pack_weights) or the plain [E,f,d] / [E,d,f] arrays")
-    ap.add_argument("--dispatch", choices=("gather", "copy"), default="gather",
+    ap.add_argument("--dispatch", choices=("gather", "copy", "fp8"), default="gather",
                     help="packed FFN: gather the token rows inside the first GEMM (the dispatch "
-                         "writes indices only) or copy them to x_perm first")
+                         "writes indices only), copy them to x_perm first, or send them as "
+                         "per-token FP8 (quantize, then decode into x_perm in expert order)")
     ap.add_argument("--diagnostics", action="store_true",
                     help="also time the routing diagnostics (moe_route_stats) after the dispatch; "
                          "reported as its own phase and included in the step")
@@ -103,6 +104,10 @@ def algorithmic(shape, counts, gather=False):
         "combine": dict(bytes=A * d * s + T * d * s + 8 * A, flops=2 * A * d),
         # logits read once (plus the bias), per-token partials out and back, offsets in
         "route_stats": dict(bytes=T * E * 4 + E * 4 + 16 * T + 8 * (E + 1), flops=0),
+        # the row in, one byte per element and (scale, zero) out
+        "fp8_quantize": dict(bytes=T * d * s + T * d + 8 * T, flops=0),
+        # codes of each row's token (and its scale) in, src_of in, the bf16 row out
+        "fp8_dequantize": dict(bytes=A * d + 8 * A + 4 * A + A * d * s, flops=0),
     }
 
 
@@ -187,6 +192,7 @@ def main():
     if a.ffn != "packed":
         a.dispatch = "copy"  # the gather is a packed-FFN kernel
     gather = a.dispatch == "gather"
+    fp8 = a.dispatch == "fp8"
     log(f"workload {shape.name}: generating inputs")
     from top_routing_expert_amd import configs as C
     inp = I.make_inputs(shape, seed=C.CONFIGS.index(shape) + 1)
@@ -204,6 +210,8 @@ def main():
         slot=torch.empty(A, dtype=torch.int32, device="cuda"),
         src=torch.empty(A, dtype=torch.int32, device="cuda"),
         xp=None if gather else torch.empty((A, d), dtype=dt, device="cuda"),
+        codes=torch.empty((T, d), dtype=torch.uint8, device="cuda") if fp8 else None,
+        sz=torch.empty((T, 2), dtype=torch.float32, device="cuda") if fp8 else None,
         h=torch.empty((A, f), dtype=dt, device="cuda"),
         y=torch.empty((A, d), dtype=dt, device="cuda"),
         out=torch.empty((T, d), dtype=dt, device="cuda"),
@@ -238,13 +246,19 @@ def main():
     calls = {
         "route": lambda: B.moe_route(cfg, dev["x"], dev["w_router"], dev["bias"], buf["logits"],
                                      buf["idx"], buf["w"], ws_r, stream),
-        "permute": lambda: B.moe_permute(cfg, None if gather else dev["x"], buf["idx"], buf["offs"],
-                                         buf["roffs"], buf["slot"], buf["src"],
-                                         None if gather else buf["xp"], ws_p, stream),
+        "permute": lambda: B.moe_permute(cfg, None if (gather or fp8) else dev["x"], buf["idx"],
+                                         buf["offs"], buf["roffs"], buf["slot"], buf["src"],
+                                         None if (gather or fp8) else buf["xp"], ws_p, stream),
         **ffn_calls,
         "combine": lambda: B.moe_combine(cfg, buf["y"], buf["slot"], buf["w"], buf["out"], stream),
     }
     phases_run = PHASES
+    if fp8:
+        calls["fp8_quantize"] = lambda: B.moe_quantize_fp8(cfg, dev["x"], buf["codes"], buf["sz"],
+                                                           stream)
+        calls["fp8_dequantize"] = lambda: B.moe_dequantize_fp8(cfg, buf["codes"], buf["src"],
+                                                               buf["sz"], buf["xp"], stream)
+        phases_run = PHASES[:2] + ("fp8_quantize", "fp8_dequantize") + PHASES[2:]
     if a.diagnostics:
         buf["hist"] = torch.empty(E, dtype=torch.int32, device="cuda")
         buf["rload"] = torch.empty(R, dtype=torch.int32, device="cuda")
@@ -253,7 +267,7 @@ def main():
         calls["route_stats"] = lambda: B.moe_route_stats(cfg, buf["logits"], dev["bias"], buf["offs"],
                                                          buf["roffs"], buf["hist"], buf["rload"],
                                                          buf["stats"], ws_s, stream)
-        phases_run = PHASES[:2] + ("route_stats",) + PHASES[2:]
+        phases_run = phases_run[:2] + ("route_stats",) + phases_run[2:]
 
     def step(ev=None):
         if ev is not None:

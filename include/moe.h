@@ -307,6 +307,30 @@ int moe_route_stats(const moe_config* cfg, const float* logits, const float* bia
                     int32_t* rank_load, float* stats, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Per-token FP8 compression of the dispatch payload ([SyncTax] §3.1: the
+ * token vectors that cross the all-to-all are quantised to FP8 with their own
+ * min / max and an affine map, one byte per element).  bf16, d <= 8192.
+ * moe_quantize_fp8 (sender): for every token t,
+ *   z = (max_i x[t,i] + min_i x[t,i]) / 2, s = ((max - min) / 2) / 448 (float32),
+ *   codes[t,i] = E4M3((x[t,i] - z) / s), clamped to +-448, rounded to nearest
+ *   (ties to the even code); a constant row gets s = 0 and codes 0.
+ *   x [T, d] bf16 in; codes [T, d] uint8 out; scale_zero [T, 2] fp32 out (s, z).
+ *   E4M3: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits, largest 448.
+ * moe_dequantize_fp8 (receiver, in expert order): for every row p of the
+ *   dispatch layout, x_perm[p,i] = bf16(code * s + z) of token src_of[p] / k
+ *   (float32 multiply and add, bf16 round to nearest even).
+ *   codes, scale_zero as written by moe_quantize_fp8; src_of [T*k] from
+ *   moe_permute (a value outside [0, T*k) is clamped to a valid token);
+ *   x_perm [T*k, d] bf16 out, then the grouped FFN as usual.
+ * |x - x_perm| <= (max - min) / 32 per token, plus the bf16 rounding.
+ * Returns MOE_EUNSUPPORTED unless dtype is MOE_BF16 and d <= 8192.
+ */
+int moe_quantize_fp8(const moe_config* cfg, const void* x, uint8_t* codes, float* scale_zero,
+                     void* stream);
+int moe_dequantize_fp8(const moe_config* cfg, const uint8_t* codes, const int32_t* src_of,
+                       const float* scale_zero, void* x_perm, void* stream);
+
+/*
  * moe_ffn_gate_up_packed with the dispatch gather fused into the first GEMM's
  * operand load ([V4-overlap] Waved-EP section: the gather folded into the
  * expert GEMM): row p of expert e's range reads token row x[src_of[p] / k]

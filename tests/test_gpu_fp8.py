@@ -1,0 +1,125 @@
+"""Per-token FP8 dispatch compression: codes and (scale, zero) bit-exact
+against the oracle's float32 replay, the receiver's decoded x_perm bit-exact,
+and a whole layer on the FP8 dispatch against the oracle run on the same
+decoded rows."""
+import numpy as np
+import pytest
+import torch
+
+from _gpu import TOL_LAYER, alloc, host, log, rel_err, upload
+from oracle import moe_oracle as om
+from top_routing_expert_amd import binding as B
+from top_routing_expert_amd import configs as C
+from top_routing_expert_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(T, d, seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((T, d)) * rng.choice([1e-3, 1.0, 30.0], size=(T, 1))).astype(np.float32)
+    if T >= 4:
+        x[0] = 0.75                         # constant row: scale 0
+        x[1, :] = 0.0
+        x[1, ::2] = -0.0                    # zeros of both signs
+        x[2, 5 % d] = 1e4                   # one outlier widens only its own row
+        x[3] = np.linspace(-2.0, 3.0, d)    # many exact ties of the rounding
+    return om.round_bf16(x)
+
+
+def _quantize(shape, bits):
+    cfg = B.config(shape)
+    x = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    codes = torch.full((shape.T, shape.d), 0x55, dtype=torch.uint8, device="cuda")
+    sz = torch.full((shape.T, 2), -7.0, dtype=torch.float32, device="cuda")
+    B.moe_quantize_fp8(cfg, x, codes, sz)
+    torch.cuda.synchronize()
+    return x, codes, sz
+
+
+@pytest.mark.parametrize("T,d", [(1, 64), (7, 320), (257, 4096), (33, 7168), (9, 8192)])
+def test_quantize_matches_oracle(T, d):
+    log(f"[fp8] quantize T={T} d={d}")
+    shape = C.E8_D4096.replace(name="fp8", T=T, d=d, k=1)
+    bits = _rows(T, d, T + d)
+    _, codes, sz = _quantize(shape, bits)
+    c_ref, s_ref, z_ref = om.quantize_rows_fp8(bits)
+    assert np.array_equal(host(codes), c_ref)
+    got = host(sz)
+    assert np.array_equal(got[:, 0].view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(got[:, 1].view(np.uint32), z_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("T,d,E,k", [(300, 256, 8, 2), (1000, 7168, 64, 8)])
+def test_dequantize_gather_matches_oracle(T, d, E, k):
+    log(f"[fp8] dequantize-gather T={T} d={d} E={E} k={k}")
+    shape = C.E8_D4096.replace(name="fp8-deq", T=T, d=d, E=E, k=k, ep_ranks=1)
+    bits = _rows(T, d, 17)
+    _, codes, sz = _quantize(shape, bits)
+    rng = np.random.default_rng(18)
+    idx_np = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    cfg = B.config(shape)
+    A = T * k
+    offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    roffs = torch.empty(2, dtype=torch.int32, device="cuda")
+    slot = torch.empty(A, dtype=torch.int32, device="cuda")
+    src = torch.empty(A, dtype=torch.int32, device="cuda")
+    B.moe_permute(cfg, None, torch.from_numpy(idx_np).cuda(), offs, roffs, slot, src, None,
+                  B.workspace(cfg, "permute"))
+    xp = torch.full((A, d), 7, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    B.moe_dequantize_fp8(cfg, codes, src, sz, xp)
+    torch.cuda.synchronize()
+    c_ref, s_ref, z_ref = om.quantize_rows_fp8(bits)
+    deq = om.dequantize_rows_fp8(c_ref, s_ref, z_ref)
+    want = om.gather_rows(deq, host(src), k)
+    assert np.array_equal(host(xp).view(np.uint16), want)
+    # the error bound of the format: half-range / 16 per token, plus bf16 rounding
+    xf = om.widen_bf16(bits)
+    xr = om.widen_bf16(deq)
+    hr = s_ref.astype(np.float64) * 448.0
+    assert np.all(np.abs(xr - xf) <= hr[:, None] / 16 + np.abs(xf) * 2.0 ** -8 + 1e-30)
+
+
+@pytest.mark.parametrize("name", ["e8", "e64"])
+def test_layer_on_fp8_dispatch(name):
+    """route -> indices -> quantize -> decode in expert order -> packed FFN ->
+    combine, against the oracle FFN and combine on the decoded rows."""
+    shape = C.SMALL[name]
+    log(f"[fp8] layer {shape.name}")
+    inp = I.make_inputs(shape, seed=91)
+    dev = upload(inp)
+    buf = alloc(shape)
+    cfg = B.config(shape)
+    B.moe_route(cfg, dev["x"], dev["w_router"], dev["bias"], buf["logits"], buf["topk_idx"],
+                buf["topk_w"], B.workspace(cfg, "route"))
+    B.moe_permute(cfg, None, buf["topk_idx"], buf["expert_offsets"], buf["rank_offsets"],
+                  buf["slot_of"], buf["src_of"], None, B.workspace(cfg, "permute"))
+    codes = torch.empty((shape.T, shape.d), dtype=torch.uint8, device="cuda")
+    sz = torch.empty((shape.T, 2), dtype=torch.float32, device="cuda")
+    B.moe_quantize_fp8(cfg, dev["x"], codes, sz)
+    B.moe_dequantize_fp8(cfg, codes, buf["src_of"], sz, buf["x_perm"])
+    pgu, pd = B.pack_weights(cfg, dev["w_gate"], dev["w_up"], dev["w_down"])
+    B.moe_ffn_gate_up_packed(cfg, buf["x_perm"], buf["expert_offsets"], pgu, buf["h"])
+    B.moe_ffn_down_packed(cfg, buf["h"], buf["expert_offsets"], pd, buf["y_perm"])
+    B.moe_combine(cfg, buf["y_perm"], buf["slot_of"], buf["topk_w"], buf["out"])
+    torch.cuda.synchronize()
+    idx, w, _ = om.route(host(buf["logits"]), inp["bias"], k=shape.k, n_group=shape.n_group,
+                         topk_group=shape.topk_group, presel=shape.presel, renorm=shape.renorm)
+    assert np.array_equal(host(buf["topk_idx"]), idx)
+    perm = om.permute(idx, shape.E, shape.ep_ranks)
+    c_ref, s_ref, z_ref = om.quantize_rows_fp8(inp["x"])
+    x_hat = om.widen_bf16(om.dequantize_rows_fp8(c_ref, s_ref, z_ref))
+    y, _ = om.grouped_ffn(om.gather_rows(x_hat, perm["src_of"], shape.k), perm["offsets"],
+                          inp["w_gate"], inp["w_up"], inp["w_down"])
+    ref = om.combine(y, perm["slot_of"], w)
+    err = rel_err(host(buf["out"]), ref)
+    assert err <= TOL_LAYER["bf16"], err
+
+
+def test_fp8_rejects_unsupported_rows():
+    shape = C.E8_D4096.replace(name="fp8-wide", T=4, d=8256, k=1)
+    with pytest.raises(RuntimeError):
+        B.moe_quantize_fp8(B.config(shape), torch.empty((4, 8256), dtype=torch.bfloat16,
+                                                        device="cuda"),
+                           torch.empty((4, 8256), dtype=torch.uint8, device="cuda"),
+                           torch.empty((4, 2), dtype=torch.float32, device="cuda"))

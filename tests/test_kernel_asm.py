@@ -190,3 +190,36 @@ def test_kernel_never_touches_in_flight_load_registers(tmp_path, src, kernel):
     assert bad == [], bad[:5]
     # no scratch: every spill would be a chance for the above
     assert not re.search(r"\.private_segment_fixed_size:\s+[1-9]", asm)
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                    reason="hipcc not available")
+def test_fp8_decode_rounds_twice(tmp_path):
+    """The receiver's decode is code * s, rounded, then + z, rounded (two
+    float32 roundings, as the oracle computes it).  A fused multiply-add
+    rounds once and changes some decoded rows, so the decode kernel's machine
+    code must hold no fma at all (the quantiser's fmas are those of the IEEE
+    division sequence, which is correctly rounded)."""
+    out = tmp_path / "fp8.s"
+    cmd = [Bld._hipcc(), *Bld.HIPCC_FLAGS, "--cuda-device-only", "-S",
+           os.path.join(Bld.CSRC, "fp8.hip"), "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    bodies = _kernel_bodies(out.read_text(), "fp8_dequantize_gather_kernel")
+    assert len(bodies) == 1
+    body = "\n".join(bodies[0][1])
+    assert re.search(r"v_mul_f32", body) and re.search(r"v_add_f32", body)
+    assert not re.search(r"v_(pk_)?fmac?_", body)
+    q = _kernel_bodies(out.read_text(), "fp8_quantize_rows_kernel")
+    assert len(q) == 1
+    qb = "\n".join(q[0][1])
+    # every fma there sits between a v_div_scale and its v_div_fixup
+    in_div = False
+    for line in q[0][1]:
+        if "v_div_scale_f32" in line:
+            in_div = True
+        if re.search(r"v_(pk_)?fmac?_", line):
+            assert in_div, line
+        if "v_div_fixup_f32" in line:
+            in_div = False
+    assert "v_div_fixup_f32" in qb

@@ -30,7 +30,7 @@ EXPORTS = ("moe_strerror", "moe_validate", "moe_workspace_bytes", "moe_route", "
            "moe_ffn_gate_up", "moe_ffn_down", "moe_grouped_ffn", "moe_combine", "moe_layer_fwd",
            "moe_packed_weight_bytes", "moe_pack_weights", "moe_ffn_gate_up_packed",
            "moe_ffn_gate_up_packed_gather", "moe_ffn_down_packed", "moe_layer_fwd_packed",
-           "moe_route_stats")
+           "moe_route_stats", "moe_quantize_fp8", "moe_dequantize_fp8")
 
 
 class MoEConfig(ctypes.Structure):
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_gate_up_packed.argtypes = [cfgp, vp, vp, vp, vp, vp]
         L.moe_ffn_gate_up_packed_gather.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
         L.moe_route_stats.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_quantize_fp8.argtypes = [cfgp, vp, vp, vp, vp]
+        L.moe_dequantize_fp8.argtypes = [cfgp, vp, vp, vp, vp, vp]
         L.moe_ffn_down_packed.argtypes = [cfgp, vp, vp, vp, vp, vp]
         L.moe_layer_fwd_packed.argtypes = [cfgp, vp, vp, vp, vp, vp, vp,
                                            ctypes.POINTER(MoELayerBufs), vp, sz, vp]
@@ -244,6 +246,17 @@ def moe_route_stats(cfg, logits, bias, expert_offsets, rank_offsets, hist, rank_
            lib().moe_route_stats(ctypes.byref(cfg), _ptr(logits), _ptr(bias), _ptr(expert_offsets),
                                  _ptr(rank_offsets), _ptr(hist), _ptr(rank_load), _ptr(stats), wp,
                                  wn, _stream(stream)))
+
+
+def moe_quantize_fp8(cfg, x, codes, scale_zero, stream=None):
+    _check("moe_quantize_fp8", lib().moe_quantize_fp8(ctypes.byref(cfg), _ptr(x), _ptr(codes),
+                                                      _ptr(scale_zero), _stream(stream)))
+
+
+def moe_dequantize_fp8(cfg, codes, src_of, scale_zero, x_perm, stream=None):
+    _check("moe_dequantize_fp8",
+           lib().moe_dequantize_fp8(ctypes.byref(cfg), _ptr(codes), _ptr(src_of), _ptr(scale_zero),
+                                    _ptr(x_perm), _stream(stream)))
 
 
 def moe_ffn_down_packed(cfg, h, expert_offsets, packed_down, y_perm, stream=None):

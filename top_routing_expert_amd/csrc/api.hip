@@ -381,6 +381,28 @@ int moe_route_stats(const moe_config* cfg, const float* logits, const float* bia
                                       rank_load, stats, ws, static_cast<hipStream_t>(stream)));
 }
 
+int moe_quantize_fp8(const moe_config* cfg, const void* x, uint8_t* codes, float* scale_zero,
+                     void* stream) {
+  int s = check_core(cfg);
+  if (s != MOE_OK) return s;
+  if (!fp8_row_supported(*cfg)) return MOE_EUNSUPPORTED;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x || !codes || !scale_zero || !aligned16(x) || !aligned16(codes)) return MOE_EINVAL;
+  return status_of(launch_fp8_quantize(*cfg, x, codes, scale_zero, static_cast<hipStream_t>(stream)));
+}
+
+int moe_dequantize_fp8(const moe_config* cfg, const uint8_t* codes, const int32_t* src_of,
+                       const float* scale_zero, void* x_perm, void* stream) {
+  int s = check_core(cfg);
+  if (s != MOE_OK) return s;
+  if (!fp8_row_supported(*cfg)) return MOE_EUNSUPPORTED;
+  if (cfg->T == 0) return MOE_OK;
+  if (!codes || !src_of || !scale_zero || !x_perm || !aligned16(codes) || !aligned16(x_perm))
+    return MOE_EINVAL;
+  return status_of(launch_fp8_dequantize(*cfg, codes, src_of, scale_zero, x_perm,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int moe_ffn_gate_up_packed_gather(const moe_config* cfg, const void* x, const int32_t* src_of,
                                   const int32_t* expert_offsets, const void* packed_gate_up,
                                   void* h, void* stream) {

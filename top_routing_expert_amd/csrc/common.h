@@ -86,6 +86,11 @@ size_t route_stats_ws_bytes(const moe_config& c);
 hipError_t launch_route_stats(const moe_config& c, const float* logits, const float* bias,
                               const int32_t* offs, const int32_t* roffs, int32_t* hist,
                               int32_t* rank_load, float* stats, void* ws, hipStream_t st);
+bool fp8_row_supported(const moe_config& c);
+hipError_t launch_fp8_quantize(const moe_config& c, const void* x, void* codes, float* scale_zero,
+                               hipStream_t st);
+hipError_t launch_fp8_dequantize(const moe_config& c, const void* codes, const int32_t* src_of,
+                                 const float* scale_zero, void* x_perm, hipStream_t st);
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_of,
                           const float* topk_w, void* out, hipStream_t st);
 

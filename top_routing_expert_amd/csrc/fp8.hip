@@ -1,0 +1,179 @@
+// Per-token FP8 compression of the dispatch payload.
+//
+// Pages: [SyncTax] §3.1 -- the expert inputs / outputs that cross the
+// all-to-all are quantised to FP8 per token: every token's vector gets its
+// own min / max and an affine map, so one outlier does not widen the range of
+// every token, and the payload shrinks to one byte per element.
+//
+// quantize: one wave per token row.  The row (d <= 8192 bf16) stays in
+//   registers: wave min / max, then centre z = (max + min) / 2 and scale
+//   s = ((max - min) / 2) / 448 in float32, v = (x - z) / s (0 for a constant
+//   row), clamped to +-448 and rounded to E4M3 (1 sign, 4 exponent bits with
+//   bias 7, 3 mantissa bits), nearest with ties to the even code.
+// dequantize: one wave per expert-ordered row p: the codes of token
+//   src_of[p] / k come back as bf16(code * s + z) (float32 multiply, float32
+//   add, bf16 round to nearest even) -- the receiver's x_perm.
+// Every step is an exactly specified float32 operation, so the codes, scales
+// and decoded rows are bit-exact against a float32 replay.  The default
+// contraction would fuse a multiply and the add after it into one fma (one
+// rounding instead of two): contraction is off in this file, and its float
+// operations are written here, not taken from header helpers compiled with
+// contraction on.
+#include <cmath>
+
+#include "common.h"
+
+#pragma clang fp contract(off)
+
+namespace moe {
+
+__device__ __forceinline__ float f32_add(float a, float b) { return a + b; }
+__device__ __forceinline__ float f32_sub(float a, float b) { return a - b; }
+__device__ __forceinline__ float f32_mul(float a, float b) { return a * b; }
+__device__ __forceinline__ float f32_div(float a, float b) { return a / b; }  // correctly rounded
+
+constexpr int kF8MaxVecsPerLane = 16;  // d <= 64 lanes * 16 vectors * 8 = 8192
+constexpr float kF8Max = 448.0f;       // largest finite E4M3 value
+
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a < 0x1p-6f) {
+    code = (uint32_t)rintf(f32_mul(a, 512.0f));  // subnormal step 2^-9; 8 -> 2^-6
+  } else {
+    int E;
+    const float f = frexpf(a, &E);  // a = f 2^E, f in [0.5, 1)
+    int e = E - 1;
+    const float mant = f32_mul(f, 2.0f);  // [1, 2)
+    int m = (int)rintf(f32_mul(f32_sub(mant, 1.0f), 8.0f));
+    if (m == 8) {
+      ++e;
+      m = 0;
+    }
+    code = (uint32_t)(((e + 7) << 3) | m);
+  }
+  return code | sign;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t e4 = (c >> 3) & 15u, m3 = c & 7u;
+  const float mag = e4 == 0 ? ldexpf((float)m3, -9) : ldexpf((float)(8u + m3), (int)e4 - 10);
+  return (c & 0x80u) ? -mag : mag;
+}
+
+__device__ __forceinline__ float f8_wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float f8_wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__global__ __launch_bounds__(256) void fp8_quantize_rows_kernel(const u32x4* __restrict__ x, int T,
+                                                                int nvec,
+                                                                u32x2* __restrict__ codes,
+                                                                float* __restrict__ scale_zero) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave
+  const u32x4* row = x + (size_t)t * nvec;
+  u32x4 r[kF8MaxVecsPerLane];
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kF8MaxVecsPerLane; ++i) {
+    const int v = lane + 64 * i;
+    if (v < nvec) {
+      r[i] = row[v];
+      const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a = bf16_lo(w[q]), b = bf16_hi(w[q]);
+        lo = fminf(lo, fminf(a, b));
+        hi = fmaxf(hi, fmaxf(a, b));
+      }
+    }
+  }
+  lo = f8_wave_min(lo);
+  hi = f8_wave_max(hi);
+  const float z = f32_mul(f32_add(hi, lo), 0.5f);
+  const float s = f32_div(f32_mul(f32_sub(hi, lo), 0.5f), kF8Max);
+  if (lane == 0) {
+    scale_zero[2 * (size_t)t] = s;
+    scale_zero[2 * (size_t)t + 1] = z;
+  }
+  u32x2* out = codes + (size_t)t * nvec;
+#pragma unroll
+  for (int i = 0; i < kF8MaxVecsPerLane; ++i) {
+    const int v = lane + 64 * i;
+    if (v < nvec) {
+      const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+      uint32_t c[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float xv = (q & 1) ? bf16_hi(w[q >> 1]) : bf16_lo(w[q >> 1]);
+        float y = s > 0.f ? f32_div(f32_sub(xv, z), s) : 0.f;
+        y = fminf(fmaxf(y, -kF8Max), kF8Max);
+        c[q] = e4m3_encode(y);
+      }
+      u32x2 pk;
+      pk.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+      pk.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+      out[v] = pk;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void fp8_dequantize_gather_kernel(
+    const u32x2* __restrict__ codes, const int32_t* __restrict__ src_of,
+    const float* __restrict__ scale_zero, int rows, int k, int T, int nvec,
+    u32x4* __restrict__ x_perm) {
+  const int lane = threadIdx.x & 63;
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (p >= rows) return;  // whole wave
+  const int t = min(max(src_of[p] / k, 0), T - 1);  // a malformed index stays in bounds
+  const float s = scale_zero[2 * (size_t)t], z = scale_zero[2 * (size_t)t + 1];
+  const u32x2* row = codes + (size_t)t * nvec;
+  u32x4* out = x_perm + (size_t)p * nvec;
+  for (int v = lane; v < nvec; v += 64) {
+    const u32x2 c = row[v];
+    float f[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t b = ((q < 4 ? c.x : c.y) >> (8 * (q & 3))) & 0xFFu;
+      f[q] = f32_add(f32_mul(e4m3_decode(b), s), z);
+    }
+    u32x4 o;
+    o.x = pack_bf16x2(f[0], f[1]);
+    o.y = pack_bf16x2(f[2], f[3]);
+    o.z = pack_bf16x2(f[4], f[5]);
+    o.w = pack_bf16x2(f[6], f[7]);
+    out[v] = o;
+  }
+}
+
+bool fp8_row_supported(const moe_config& c) {
+  return c.dtype == MOE_BF16 && c.d % 8 == 0 && c.d / 8 <= 64 * kF8MaxVecsPerLane;
+}
+
+hipError_t launch_fp8_quantize(const moe_config& c, const void* x, void* codes, float* scale_zero,
+                               hipStream_t st) {
+  const int nvec = c.d / 8;
+  fp8_quantize_rows_kernel<<<div_up(c.T, 4), 256, 0, st>>>(
+      static_cast<const u32x4*>(x), c.T, nvec, static_cast<u32x2*>(codes), scale_zero);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_dequantize(const moe_config& c, const void* codes, const int32_t* src_of,
+                                 const float* scale_zero, void* x_perm, hipStream_t st) {
+  const int rows = c.T * c.k, nvec = c.d / 8;
+  fp8_dequantize_gather_kernel<<<div_up(rows, 4), 256, 0, st>>>(
+      static_cast<const u32x2*>(codes), src_of, scale_zero, rows, c.k, c.T, nvec,
+      static_cast<u32x4*>(x_perm));
+  return hipGetLastError();
+}
+
+}  // namespace moe
