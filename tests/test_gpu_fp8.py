@@ -37,7 +37,8 @@ def _quantize(shape, bits):
     return x, codes, sz
 
 
-@pytest.mark.parametrize("T,d", [(1, 64), (7, 320), (257, 4096), (33, 7168), (9, 8192)])
+@pytest.mark.parametrize("T,d", [(1, 64), (7, 320), (5, 1024), (6, 1088), (300, 2048), (257, 4096),
+                                 (33, 7168), (9, 8192)])
 def test_quantize_matches_oracle(T, d):
     log(f"[fp8] quantize T={T} d={d}")
     shape = C.E8_D4096.replace(name="fp8", T=T, d=d, k=1)
@@ -50,7 +51,7 @@ def test_quantize_matches_oracle(T, d):
     assert np.array_equal(got[:, 1].view(np.uint32), z_ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("T,d,E,k", [(300, 256, 8, 2), (1000, 7168, 64, 8)])
+@pytest.mark.parametrize("T,d,E,k", [(300, 256, 8, 2), (77, 1088, 16, 4), (1000, 7168, 64, 8)])
 def test_dequantize_gather_matches_oracle(T, d, E, k):
     log(f"[fp8] dequantize-gather T={T} d={d} E={E} k={k}")
     shape = C.E8_D4096.replace(name="fp8-deq", T=T, d=d, E=E, k=k, ep_ranks=1)

@@ -5,14 +5,19 @@
 // own min / max and an affine map, so one outlier does not widen the range of
 // every token, and the payload shrinks to one byte per element.
 //
-// quantize: one wave per token row.  The row (d <= 8192 bf16) stays in
-//   registers: wave min / max, then centre z = (max + min) / 2 and scale
-//   s = ((max - min) / 2) / 448 in float32, v = (x - z) / s (0 for a constant
-//   row), clamped to +-448 and rounded to E4M3 (1 sign, 4 exponent bits with
-//   bias 7, 3 mantissa bits), nearest with ties to the even code.
-// dequantize: one wave per expert-ordered row p: the codes of token
+// quantize: one row per RT threads (RT = 256 for rows of more than 1024
+//   elements, else one wave), each thread up to 4 vectors of 8 bf16 that stay
+//   in registers: the row's min / max (wave tree, then LDS across the row's
+//   waves), then centre z = (max + min) / 2 and scale s = ((max - min) / 2) /
+//   448 in float32, v = (x - z) / s (0 for a constant row), clamped to +-448
+//   and rounded to E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa
+//   bits), nearest with ties to the even code.  Spreading a row over a whole
+//   block keeps several waves per SIMD busy on the per-element divide and
+//   encode even when there are only a few rows per CU.
+// dequantize: one expert-ordered row p per RT threads: the codes of token
 //   src_of[p] / k come back as bf16(code * s + z) (float32 multiply, float32
-//   add, bf16 round to nearest even) -- the receiver's x_perm.
+//   add, bf16 round to nearest even) -- the receiver's x_perm.  Every thread
+//   issues all of its code loads before it decodes.
 // Every step is an exactly specified float32 operation, so the codes, scales
 // and decoded rows are bit-exact against a float32 replay.  The default
 // contraction would fuse a multiply and the add after it into one fma (one
@@ -32,27 +37,23 @@ __device__ __forceinline__ float f32_sub(float a, float b) { return a - b; }
 __device__ __forceinline__ float f32_mul(float a, float b) { return a * b; }
 __device__ __forceinline__ float f32_div(float a, float b) { return a / b; }  // correctly rounded
 
-constexpr int kF8MaxVecsPerLane = 16;  // d <= 64 lanes * 16 vectors * 8 = 8192
+constexpr int kF8VecsPerThread = 4;  // d <= 256 threads * 4 vectors * 8 = 8192
 constexpr float kF8Max = 448.0f;       // largest finite E4M3 value
 
+// |v| <= 448 -> E4M3 code, nearest with ties to even.  Below 2^-6 the code
+// is the number of 2^-9 steps.  Above, the float32 bit pattern already holds
+// the E4M3 fields: keep its top 3 mantissa bits, round the 20 dropped ones to
+// nearest even (a carry out of the mantissa moves to the next binade by
+// itself) and rebias the exponent from 127 to 7.
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
-  const float a = fabsf(v);
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
   uint32_t code;
-  if (a < 0x1p-6f) {
-    code = (uint32_t)rintf(f32_mul(a, 512.0f));  // subnormal step 2^-9; 8 -> 2^-6
-  } else {
-    int E;
-    const float f = frexpf(a, &E);  // a = f 2^E, f in [0.5, 1)
-    int e = E - 1;
-    const float mant = f32_mul(f, 2.0f);  // [1, 2)
-    int m = (int)rintf(f32_mul(f32_sub(mant, 1.0f), 8.0f));
-    if (m == 8) {
-      ++e;
-      m = 0;
-    }
-    code = (uint32_t)(((e + 7) << 3) | m);
-  }
+  if (a < 0x3C800000u)  // 2^-6
+    code = (uint32_t)rintf(f32_mul(__uint_as_float(a), 512.0f));
+  else
+    code = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
   return code | sign;
 }
 
@@ -73,25 +74,34 @@ __device__ __forceinline__ float f8_wave_max(float v) {
   return v;
 }
 
+// RT threads per row (64 or 256), 256 / RT rows per block.
+template <int RT>
 __global__ __launch_bounds__(256) void fp8_quantize_rows_kernel(const u32x4* __restrict__ x, int T,
                                                                 int nvec,
                                                                 u32x2* __restrict__ codes,
                                                                 float* __restrict__ scale_zero) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // whole wave
-  const u32x4* row = x + (size_t)t * nvec;
-  u32x4 r[kF8MaxVecsPerLane];
+  constexpr int RB = 256 / RT, WPR = RT / 64;
+  __shared__ float s_lo[4], s_hi[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i0 = tid % RT;
+  const int t = blockIdx.x * RB + tid / RT;
+  const bool live = t < T;  // uniform over the row's threads
+  const u32x4* row = x + (size_t)(live ? t : 0) * nvec;
+  u32x4 r[kF8VecsPerThread];
+#pragma unroll
+  for (int i = 0; i < kF8VecsPerThread; ++i) {
+    const int v = i0 + RT * i;
+    if (live && v < nvec) r[i] = row[v];
+  }
   float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < kF8MaxVecsPerLane; ++i) {
-    const int v = lane + 64 * i;
-    if (v < nvec) {
-      r[i] = row[v];
-      const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+  for (int i = 0; i < kF8VecsPerThread; ++i) {
+    const int v = i0 + RT * i;
+    if (live && v < nvec) {
+      const uint32_t wd[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float a = bf16_lo(w[q]), b = bf16_hi(w[q]);
+        const float a = bf16_lo(wd[q]), b = bf16_hi(wd[q]);
         lo = fminf(lo, fminf(a, b));
         hi = fmaxf(hi, fmaxf(a, b));
       }
@@ -99,22 +109,37 @@ __global__ __launch_bounds__(256) void fp8_quantize_rows_kernel(const u32x4* __r
   }
   lo = f8_wave_min(lo);
   hi = f8_wave_max(hi);
+  if constexpr (WPR > 1) {  // RB == 1: the block is one row
+    if (lane == 0) {
+      s_lo[w] = lo;
+      s_hi[w] = hi;
+    }
+    __syncthreads();
+    lo = s_lo[0];
+    hi = s_hi[0];
+#pragma unroll
+    for (int q = 1; q < WPR; ++q) {
+      lo = fminf(lo, s_lo[q]);
+      hi = fmaxf(hi, s_hi[q]);
+    }
+  }
+  if (!live) return;
   const float z = f32_mul(f32_add(hi, lo), 0.5f);
   const float s = f32_div(f32_mul(f32_sub(hi, lo), 0.5f), kF8Max);
-  if (lane == 0) {
+  if (i0 == 0) {
     scale_zero[2 * (size_t)t] = s;
     scale_zero[2 * (size_t)t + 1] = z;
   }
   u32x2* out = codes + (size_t)t * nvec;
 #pragma unroll
-  for (int i = 0; i < kF8MaxVecsPerLane; ++i) {
-    const int v = lane + 64 * i;
+  for (int i = 0; i < kF8VecsPerThread; ++i) {
+    const int v = i0 + RT * i;
     if (v < nvec) {
-      const uint32_t w[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+      const uint32_t wd[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
       uint32_t c[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const float xv = (q & 1) ? bf16_hi(w[q >> 1]) : bf16_lo(w[q >> 1]);
+        const float xv = (q & 1) ? bf16_hi(wd[q >> 1]) : bf16_lo(wd[q >> 1]);
         float y = s > 0.f ? f32_div(f32_sub(xv, z), s) : 0.f;
         y = fminf(fmaxf(y, -kF8Max), kF8Max);
         c[q] = e4m3_encode(y);
@@ -127,52 +152,75 @@ __global__ __launch_bounds__(256) void fp8_quantize_rows_kernel(const u32x4* __r
   }
 }
 
+template <int RT>
 __global__ __launch_bounds__(256) void fp8_dequantize_gather_kernel(
     const u32x2* __restrict__ codes, const int32_t* __restrict__ src_of,
     const float* __restrict__ scale_zero, int rows, int k, int T, int nvec,
     u32x4* __restrict__ x_perm) {
-  const int lane = threadIdx.x & 63;
-  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (p >= rows) return;  // whole wave
+  constexpr int RB = 256 / RT;
+  const int tid = threadIdx.x, i0 = tid % RT;
+  const int p = blockIdx.x * RB + tid / RT;
+  if (p >= rows) return;
   const int t = min(max(src_of[p] / k, 0), T - 1);  // a malformed index stays in bounds
   const float s = scale_zero[2 * (size_t)t], z = scale_zero[2 * (size_t)t + 1];
   const u32x2* row = codes + (size_t)t * nvec;
   u32x4* out = x_perm + (size_t)p * nvec;
-  for (int v = lane; v < nvec; v += 64) {
-    const u32x2 c = row[v];
-    float f[8];
+  u32x2 c[kF8VecsPerThread];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t b = ((q < 4 ? c.x : c.y) >> (8 * (q & 3))) & 0xFFu;
-      f[q] = f32_add(f32_mul(e4m3_decode(b), s), z);
+  for (int i = 0; i < kF8VecsPerThread; ++i) {
+    const int v = i0 + RT * i;
+    if (v < nvec) c[i] = row[v];
+  }
+#pragma unroll
+  for (int i = 0; i < kF8VecsPerThread; ++i) {
+    const int v = i0 + RT * i;
+    if (v < nvec) {
+      float f[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t b = ((q < 4 ? c[i].x : c[i].y) >> (8 * (q & 3))) & 0xFFu;
+        f[q] = f32_add(f32_mul(e4m3_decode(b), s), z);
+      }
+      u32x4 o;
+      o.x = pack_bf16x2(f[0], f[1]);
+      o.y = pack_bf16x2(f[2], f[3]);
+      o.z = pack_bf16x2(f[4], f[5]);
+      o.w = pack_bf16x2(f[6], f[7]);
+      out[v] = o;
     }
-    u32x4 o;
-    o.x = pack_bf16x2(f[0], f[1]);
-    o.y = pack_bf16x2(f[2], f[3]);
-    o.z = pack_bf16x2(f[4], f[5]);
-    o.w = pack_bf16x2(f[6], f[7]);
-    out[v] = o;
   }
 }
 
 bool fp8_row_supported(const moe_config& c) {
-  return c.dtype == MOE_BF16 && c.d % 8 == 0 && c.d / 8 <= 64 * kF8MaxVecsPerLane;
+  return c.dtype == MOE_BF16 && c.d % 8 == 0 && c.d / 8 <= 256 * kF8VecsPerThread;
 }
+
+// Rows of more than 1024 elements get a whole block, shorter ones one wave.
+static bool fp8_wide_rows(int nvec) { return nvec > 64 * kF8VecsPerThread / 2; }
 
 hipError_t launch_fp8_quantize(const moe_config& c, const void* x, void* codes, float* scale_zero,
                                hipStream_t st) {
   const int nvec = c.d / 8;
-  fp8_quantize_rows_kernel<<<div_up(c.T, 4), 256, 0, st>>>(
-      static_cast<const u32x4*>(x), c.T, nvec, static_cast<u32x2*>(codes), scale_zero);
+  const auto* xs = static_cast<const u32x4*>(x);
+  auto* cs = static_cast<u32x2*>(codes);
+  if (fp8_wide_rows(nvec))
+    fp8_quantize_rows_kernel<256><<<c.T, 256, 0, st>>>(xs, c.T, nvec, cs, scale_zero);
+  else
+    fp8_quantize_rows_kernel<64><<<div_up(c.T, 4), 256, 0, st>>>(xs, c.T, nvec, cs, scale_zero);
   return hipGetLastError();
 }
 
 hipError_t launch_fp8_dequantize(const moe_config& c, const void* codes, const int32_t* src_of,
                                  const float* scale_zero, void* x_perm, hipStream_t st) {
   const int rows = c.T * c.k, nvec = c.d / 8;
-  fp8_dequantize_gather_kernel<<<div_up(rows, 4), 256, 0, st>>>(
-      static_cast<const u32x2*>(codes), src_of, scale_zero, rows, c.k, c.T, nvec,
-      static_cast<u32x4*>(x_perm));
+  const auto* cs = static_cast<const u32x2*>(codes);
+  auto* out = static_cast<u32x4*>(x_perm);
+  if (fp8_wide_rows(nvec))
+    fp8_dequantize_gather_kernel<256><<<rows, 256, 0, st>>>(cs, src_of, scale_zero, rows, c.k, c.T,
+                                                           nvec, out);
+  else
+    fp8_dequantize_gather_kernel<64><<<div_up(rows, 4), 256, 0, st>>>(cs, src_of, scale_zero, rows,
+                                                                     c.k, c.T, nvec, out);
   return hipGetLastError();
 }
 
