@@ -1,4 +1,4 @@
-"""CPU oracle of the MoE-layer forward token path.
+"""CPU oracle of the MoE-layer forward token path and of its backward.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or links
 this module: only the tests, the package smoke check and the benchmark's CPU
@@ -27,7 +27,10 @@ fp32 scores, -0 equal to +0; the group score is the max over the group;
 groups and expert-to-rank blocks are contiguous; the order inside an expert's
 segment is ascending token index; no capacity limit (dropless); SwiGLU is
 SiLU(x Wg^T) * (x Wu^T) then W_down; without renormalisation and without
-pre-selection the gate denominator runs over all E experts.
+pre-selection the gate denominator runs over all E experts.  The backward
+holds the forward's selection fixed (it is piecewise constant), so the router
+gets its gradient through the gate weights only; the per-expert bias, added
+to the logits before the softmax, gets sum_t dz[t].
 
 Parity pins: every function here is pinned by `-m "not gpu"` tests against
 closed forms, hand-worked cases, brute force or library routines; none is
@@ -43,7 +46,8 @@ import numpy as np
 __all__ = [
     "widen_bf16", "router_logits", "scores", "select", "gates", "margins", "route",
     "permute", "silu", "expert_ffn", "grouped_ffn", "combine", "layer",
-    "select_bruteforce", "dense_bruteforce",
+    "select_bruteforce", "dense_bruteforce", "combine_backward", "expert_ffn_backward",
+    "grouped_ffn_backward", "scatter_rows_backward", "gates_backward", "layer_backward",
 ]
 
 
@@ -430,6 +434,137 @@ def layer(x, w_router, bias, w_gate, w_up, w_down, *, k, n_group=1, topk_group=1
     out = combine(y, perm["slot_of"], w)
     return dict(logits=z, s=s, topk_idx=idx, topk_w=w, margin=margins(s64, k, n_group, topk_group),
                 x_perm=x_perm, h=h, y_perm=y, out=out, **perm)
+
+
+# ----------------------------------------------------------------------------
+# layer backward: the mirror of the forward on the cached routing
+# ----------------------------------------------------------------------------
+def combine_backward(d_out, y_perm, slot_of, topk_w):
+    """out[t] = sum_j g[t, j] y[p(t, j)]  =>
+    dy[p(t, j)] = g[t, j] d_out[t]  and  dg[t, j] = <d_out[t], y[p(t, j)]>.
+    Returns (dy_perm [A, d], dg [T, k]), float64."""
+    dout = _f64(d_out)
+    g = np.asarray(topk_w, dtype=np.float64)
+    T, k = g.shape
+    y = _f64(y_perm)
+    slots = np.asarray(slot_of).reshape(T, k)
+    dy = np.zeros_like(y)
+    dg = np.zeros((T, k))
+    for j in range(k):
+        dy[slots[:, j]] = g[:, j : j + 1] * dout
+        dg[:, j] = np.sum(dout * y[slots[:, j]], axis=1)
+    return dy, dg
+
+
+def expert_ffn_backward(X, w_gate_e, w_up_e, w_down_e, dY):
+    """Backward of y = (SiLU(a) * u) Wd^T with a = X Wg^T, u = X Wu^T:
+    each product C = A B gives dA = dC B^T and dB = A^T dC ([V4-overlap], PP
+    bubble section: a layer's backward turns dy into dx and dW = x^T dy);
+    SiLU'(a) = sig(a) (1 + a (1 - sig(a))).  Returns
+    (dX, dWg, dWu, dWd, dict of the intermediates a, u, h, dh, da, du)."""
+    X, Wg, Wu, Wd, dY = (_f64(v) for v in (X, w_gate_e, w_up_e, w_down_e, dY))
+    a = X @ Wg.T
+    u = X @ Wu.T
+    sig = 1.0 / (1.0 + np.exp(-a))
+    h = a * sig * u
+    dh = dY @ Wd                      # y = h Wd^T
+    dWd = dY.T @ h
+    da = dh * u * sig * (1.0 + a * (1.0 - sig))
+    du = dh * a * sig
+    dX = da @ Wg + du @ Wu
+    dWg = da.T @ X
+    dWu = du.T @ X
+    return dX, dWg, dWu, dWd, dict(a=a, u=u, h=h, dh=dh, da=da, du=du)
+
+
+def grouped_ffn_backward(x_perm, offsets, w_gate, w_up, w_down, dy_perm):
+    """Every expert's backward on its own row segment; experts without rows
+    get zero weight gradients."""
+    x_perm = _f64(x_perm)
+    E = len(offsets) - 1
+    dx = np.zeros_like(x_perm)
+    dwg = np.zeros(np.shape(w_gate))
+    dwu = np.zeros(np.shape(w_up))
+    dwd = np.zeros(np.shape(w_down))
+    A, f = x_perm.shape[0], np.shape(w_gate)[1]
+    inter = {n: np.zeros((A, f)) for n in ("a", "u", "h", "dh", "da", "du")}
+    dy = _f64(dy_perm)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            dx[r0:r1], dwg[e], dwu[e], dwd[e], it = expert_ffn_backward(
+                x_perm[r0:r1], w_gate[e], w_up[e], w_down[e], dy[r0:r1])
+            for n in inter:
+                inter[n][r0:r1] = it[n]
+    return dx, dwg, dwu, dwd, inter
+
+
+def scatter_rows_backward(dx_perm, src_of, k: int, T: int):
+    """x_perm[p] = x[src_of[p] // k]  =>  dx[t] = sum of dx_perm[p] over the
+    k rows p that copied token t."""
+    dxp = _f64(dx_perm)
+    dx = np.zeros((T, dxp.shape[1]))
+    np.add.at(dx, np.asarray(src_of) // k, dxp)
+    return dx
+
+
+def gates_backward(s, sel, dg, k: int, presel: int = 0, renorm: int = 1):
+    """Backward of `gates` with the selection held fixed (the cached routing).
+    g_j = e_j / D with e_j = exp(s_j - m) and D the sum over the support set S
+    (the k chosen; the P pre-selected; all E).  On S the normalised
+    q_i = e_i / D has dq_i / ds_l = q_i (delta_il - q_l), and g_j = q_j for the
+    k chosen, so ds_l = q_l (dq_l - sum_j g_j dg_j) on S (dq_l = dg_j when l is
+    the j-th chosen expert, else 0) and ds_l = 0 off S.  The shift m cancels.
+    Returns ds [T, E], float64."""
+    s64 = np.asarray(s, dtype=np.float32).astype(np.float64)
+    T, E = s64.shape
+    sel = np.asarray(sel)
+    dg = np.asarray(dg, dtype=np.float64)
+    m = np.take_along_axis(s64, sel[:, :1], axis=1)
+    if renorm:
+        support = sel[:, :k]
+    elif presel:
+        support = sel[:, :presel]
+    else:
+        support = np.tile(np.arange(E), (T, 1))
+    e_sup = np.exp(np.take_along_axis(s64, support, axis=1) - m)
+    q = e_sup / e_sup.sum(axis=1, keepdims=True)
+    dq_full = np.zeros((T, E))
+    np.put_along_axis(dq_full, sel[:, :k], dg, axis=1)
+    q_full = np.zeros((T, E))
+    np.put_along_axis(q_full, support, q, axis=1)
+    g = np.take_along_axis(q_full, sel[:, :k], axis=1)
+    inner = np.sum(g * dg, axis=1, keepdims=True)
+    ds = q_full * (dq_full - inner)
+    return ds
+
+
+def layer_backward(x, w_router, bias, w_gate, w_up, w_down, d_out, *, k, n_group=1,
+                   topk_group=1, presel=0, renorm=1, ep_ranks=1, fwd=None) -> dict:
+    """Gradients of the layer on the routing of its forward pass, which the
+    backward reuses instead of routing again ([SyncTax] §2.4: the backward
+    retraces the forward's routing, kept from the forward as the routing
+    indices).  The selection is piecewise constant, so only the gate weights
+    carry a gradient into the router: s = z + b gives dz = ds and
+    db = sum_t ds[t]; z = x Wr^T gives dx += dz Wr and dWr = dz^T x.
+    Returns dx, dWr, db, dWg, dWu, dWd and the intermediates."""
+    if fwd is None:
+        fwd = layer(x, w_router, bias, w_gate, w_up, w_down, k=k, n_group=n_group,
+                    topk_group=topk_group, presel=presel, renorm=renorm, ep_ranks=ep_ranks)
+    T = np.shape(x)[0]
+    dy_perm, dg = combine_backward(d_out, fwd["y_perm"], fwd["slot_of"], fwd["topk_w"])
+    dx_perm, dwg, dwu, dwd, inter = grouped_ffn_backward(fwd["x_perm"], fwd["offsets"], w_gate,
+                                                         w_up, w_down, dy_perm)
+    dx = scatter_rows_backward(dx_perm, fwd["src_of"], k, T)
+    sel = select(fwd["s"], k, n_group, topk_group, presel)
+    ds = gates_backward(fwd["s"], sel, dg, k, presel, renorm)
+    dz = ds
+    dx_router = dz @ _f64(w_router)
+    dwr = dz.T @ _f64(x)
+    db = dz.sum(axis=0)
+    return dict(dx=dx + dx_router, dx_experts=dx, dx_router=dx_router, dw_router=dwr, d_bias=db,
+                dw_gate=dwg, dw_up=dwu, dw_down=dwd, dy_perm=dy_perm, d_topk_w=dg, dz=dz,
+                dx_perm=dx_perm, **inter)
 
 
 # ----------------------------------------------------------------------------

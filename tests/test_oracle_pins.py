@@ -389,6 +389,84 @@ def pin_widen_bf16():
     assert got.tolist() == want
 
 
+def _fd_problem(rng, m):
+    T, d, f = 10, 6, 5
+    x, wr, b, wg, wu, wd = _small_problem(rng, m["E"], T=T, d=d, f=f, bias=m.get("bias"))
+    return [x, wr, b, wg, wu, wd], rng.standard_normal((T, d))
+
+
+def pin_layer_backward_finite_differences():
+    """Each gradient of layer_backward against a central difference of the
+    (separately pinned) forward along a random direction, in every routing
+    mode; the routing must not change inside the step."""
+    rng = np.random.default_rng(41)
+    eps = 1e-3
+    names = ["dx", "dw_router", "d_bias", "dw_gate", "dw_up", "dw_down"]
+    for m in ROUTING_MODES:
+        params, R = _fd_problem(rng, m)
+        kw = _mode_kw(m)
+        g = om.layer_backward(*params, R, **kw)
+        base = om.layer(*params, **kw)["topk_idx"]
+        for i, name in enumerate(names):
+            if params[i] is None:
+                continue
+            v = rng.standard_normal(np.shape(params[i]))
+            f_at = []
+            for sgn in (1.0, -1.0):
+                pp = list(params)
+                pp[i] = np.asarray(params[i], np.float64) + sgn * eps * v
+                r = om.layer(*pp, **kw)
+                assert np.array_equal(r["topk_idx"], base), (m, name)
+                f_at.append(np.sum(r["out"] * R))
+            fd = (f_at[0] - f_at[1]) / (2 * eps)
+            an = float(np.sum(g[name] * v))
+            assert abs(fd - an) <= 2e-4 * max(1.0, abs(fd)), (m, name, fd, an)
+
+
+def pin_expert_backward_matches_autograd():
+    """One expert's backward against torch autograd of the same MLP (float64)."""
+    rng = np.random.default_rng(42)
+    X = rng.standard_normal((7, 9))
+    wg, wu, wd = rng.standard_normal((5, 9)), rng.standard_normal((5, 9)), rng.standard_normal((9, 5))
+    dY = rng.standard_normal((7, 9))
+    dX, dWg, dWu, dWd, _ = om.expert_ffn_backward(X, wg, wu, wd, dY)
+    t = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (X, wg, wu, wd)]
+    y = torch.nn.functional.silu(t[0] @ t[1].T) * (t[0] @ t[2].T) @ t[3].T
+    y.backward(torch.tensor(dY))
+    for mine, ref in zip((dX, dWg, dWu, dWd), t):
+        assert np.allclose(mine, ref.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def pin_gates_backward_matches_autograd():
+    """Softmax-gate backward against torch autograd of a softmax over the
+    support set, gathered at the chosen experts, in each gate mode."""
+    rng = np.random.default_rng(43)
+    T, E, k = 6, 10, 3
+    s = rng.standard_normal((T, E)).astype(np.float32)
+    dg = rng.standard_normal((T, k))
+    for presel, renorm in ((0, 1), (6, 0), (0, 0), (6, 1)):
+        sel = om.select(s, k, presel=presel)
+        ds = om.gates_backward(s, sel, dg, k, presel, renorm)
+        st = torch.tensor(s.astype(np.float64), requires_grad=True)
+        supp = sel[:, :k] if renorm else (sel[:, :presel] if presel else np.tile(np.arange(E), (T, 1)))
+        sup_t = torch.tensor(supp, dtype=torch.long)
+        q = torch.softmax(torch.gather(st, 1, sup_t), dim=1)
+        qf = torch.zeros(T, E, dtype=torch.float64).scatter(1, sup_t, q)
+        g = torch.gather(qf, 1, torch.tensor(sel[:, :k], dtype=torch.long))
+        g.backward(torch.tensor(dg))
+        assert np.allclose(ds, st.grad.numpy(), rtol=1e-12, atol=1e-14), (presel, renorm)
+        assert np.allclose(ds.sum(axis=1), 0.0, atol=1e-12)  # softmax shift invariance
+
+
+def pin_single_choice_router_has_no_gradient():
+    """k = 1 with renormalisation: the gate is 1 whatever the scores, so the
+    router gets no gradient at all."""
+    rng = np.random.default_rng(44)
+    x, wr, b, wg, wu, wd = _small_problem(rng, 5, T=8, d=6, f=4)
+    g = om.layer_backward(x, wr, b, wg, wu, wd, rng.standard_normal((8, 6)), k=1)
+    assert np.all(g["dz"] == 0) and np.all(g["dw_router"] == 0) and np.all(g["dx_router"] == 0)
+
+
 PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_")}
 
 
@@ -492,6 +570,43 @@ def _quantize_full_range_scale(x_bits):
     return om.fp8_e4m3_encode(np.clip(v, -448, 448)), s, z
 
 
+def _expert_bwd_silu_prime_dropped(X, w_gate_e, w_up_e, w_down_e, dY):
+    X, Wg, Wu, Wd, dY = (np.asarray(v, np.float64) for v in (X, w_gate_e, w_up_e, w_down_e, dY))
+    a, u = X @ Wg.T, X @ Wu.T
+    sig = 1.0 / (1.0 + np.exp(-a))
+    h = a * sig * u
+    dh = dY @ Wd
+    da, du = dh * u * sig, dh * a * sig
+    return (da @ Wg + du @ Wu, da.T @ X, du.T @ X, dY.T @ h,
+            dict(a=a, u=u, h=h, dh=dh, da=da, du=du))
+
+
+def _expert_bwd_branches_swapped(X, w_gate_e, w_up_e, w_down_e, dY):
+    dX, dWg, dWu, dWd, it = _ORIG_EXPERT_BWD(X, w_gate_e, w_up_e, w_down_e, dY)
+    return dX, dWu, dWg, dWd, it
+
+
+def _gates_bwd_sign(s, sel, dg, k, presel=0, renorm=1):
+    return -_ORIG_GATES_BWD(s, sel, dg, k, presel, renorm)
+
+
+def _combine_bwd_no_gate(d_out, y_perm, slot_of, topk_w):
+    dy, dg = _ORIG_COMBINE_BWD(d_out, y_perm, slot_of, np.ones_like(np.asarray(topk_w)))
+    return dy, _ORIG_COMBINE_BWD(d_out, y_perm, slot_of, topk_w)[1]
+
+
+def _scatter_bwd_first_row_only(dx_perm, src_of, k, T):
+    dxp = np.asarray(dx_perm, np.float64)
+    dx = np.zeros((T, dxp.shape[1]))
+    src = np.asarray(src_of)
+    keep = src % k == 0
+    np.add.at(dx, src[keep] // k, dxp[keep])
+    return dx
+
+
+_ORIG_EXPERT_BWD = om.expert_ffn_backward
+_ORIG_GATES_BWD = om.gates_backward
+_ORIG_COMBINE_BWD = om.combine_backward
 _ORIG_FP8_ENCODE = om.fp8_e4m3_encode
 
 MUTANTS = {
@@ -508,6 +623,11 @@ MUTANTS = {
     "stats-histogram-first-choice": ("route_stats", _route_stats_first_choice_only),
     "fp8-round-half-up": ("fp8_e4m3_encode", _fp8_round_half_up),
     "fp8-scale-full-range": ("quantize_rows_fp8", _quantize_full_range_scale),
+    "bwd-silu-derivative-term-dropped": ("expert_ffn_backward", _expert_bwd_silu_prime_dropped),
+    "bwd-gate-up-branches-swapped": ("expert_ffn_backward", _expert_bwd_branches_swapped),
+    "bwd-softmax-sign": ("gates_backward", _gates_bwd_sign),
+    "bwd-combine-without-gate": ("combine_backward", _combine_bwd_no_gate),
+    "bwd-dispatch-first-copy-only": ("scatter_rows_backward", _scatter_bwd_first_row_only),
 }
 
 
