@@ -76,7 +76,9 @@ enum moe_entry {
   MOE_ENTRY_FFN = 3,
   MOE_ENTRY_COMBINE = 4,
   MOE_ENTRY_LAYER = 5,
-  MOE_ENTRY_ROUTE_STATS = 6
+  MOE_ENTRY_ROUTE_STATS = 6,
+  MOE_ENTRY_FFN_BACKWARD = 7,
+  MOE_ENTRY_ROUTE_BACKWARD = 8
 };
 
 /*
@@ -356,6 +358,78 @@ int moe_layer_fwd_packed(const moe_config* cfg, const void* x, const void* w_rou
                          const float* bias, const void* packed_gate_up, const void* packed_down,
                          void* out, const moe_layer_bufs* bufs, void* ws, size_t ws_bytes,
                          void* stream);
+
+/*
+ * ---------------------------------------------------------------- backward
+ * The layer's backward on the routing of its forward pass: the forward's
+ * routing indices (topk_idx, slot_of, src_of, expert_offsets) are reused, not
+ * recomputed ([SyncTax] §2.4: the backward retraces the forward's routing
+ * from the indices the forward kept); each product C = A B gives dA = dC B^T
+ * and dW = A^T dC ([V4-overlap], PP bubble section: dW = x^T dy).  bf16 only
+ * (MOE_EUNSUPPORTED otherwise); fp32 accumulation; every output is written
+ * in full (weight gradients of experts without rows are zero).  All device
+ * pointers, 16-byte aligned; asynchronous on `stream`; errors are reported
+ * before anything is enqueued.  A full step is
+ *   moe_combine_backward -> moe_ffn_backward -> moe_route_backward ->
+ *   moe_unpermute_backward.
+ */
+
+/*
+ * combine backward: out[t] = sum_j g[t,j] y_perm[slot_of[t*k+j]]  =>
+ *   d_y_perm[slot_of[t*k+j]] = bf16(g[t,j] d_out[t])   [T*k, d] bf16 out
+ *   d_topk_w[t*k+j] = <d_out[t], y_perm[slot_of[t*k+j]]>  [T, k] fp32 out
+ * d_out [T, d] bf16, y_perm [T*k, d] bf16 (the forward's), slot_of [T*k],
+ * topk_w [T, k] fp32.
+ */
+int moe_combine_backward(const moe_config* cfg, const void* d_out, const void* y_perm,
+                         const int32_t* slot_of, const float* topk_w, void* d_y_perm,
+                         float* d_topk_w, void* stream);
+
+/*
+ * grouped SwiGLU FFN backward over the expert row segments of x_perm:
+ *   a = x Wg_e^T, u = x Wu_e^T (recomputed: the forward keeps only h),
+ *   h = SiLU(a) u, dh = dy Wd_e, da = dh u SiLU'(a), du = dh SiLU(a),
+ *   d_x_perm = da Wg_e + du Wu_e          [T*k, d] bf16 out
+ *   d_w_gate[e] = da_e^T x_e              [E, f, d] bf16 out
+ *   d_w_up[e]   = du_e^T x_e              [E, f, d] bf16 out
+ *   d_w_down[e] = dy_e^T h_e              [E, d, f] bf16 out
+ * x_perm [T*k, d] bf16 (the forward's dispatched rows), expert_offsets [E+1],
+ * weights as in moe_grouped_ffn, d_y_perm [T*k, d] bf16.
+ * ws: moe_workspace_bytes(MOE_ENTRY_FFN_BACKWARD) = 4 T k f bf16 (a/da,
+ * u/du, h, dh), 256-byte aligned.
+ */
+int moe_ffn_backward(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                     const void* w_gate, const void* w_up, const void* w_down,
+                     const void* d_y_perm, void* d_x_perm, void* d_w_gate, void* d_w_up,
+                     void* d_w_down, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * router backward through the gate softmax, selection held fixed:
+ *   s = logits + bias; the support set S is the k chosen (renorm), else the
+ *   presel pre-selected by (s desc, e asc), else all E; q = softmax of s
+ *   over S; dq_e = d_topk_w[t, j] for e = topk_idx[t, j], else 0;
+ *   d_logits[t, e] = q_e (dq_e - sum_e' q_e' dq_e') on S, 0 off S  [T, E] fp32 out
+ *   d_x_router = dz Wr                     [T, d] bf16 out
+ *   d_w_router = dz^T x                    [E, d] bf16 out
+ *   d_bias[e] = sum_t dz[t, e] (fixed order; NULL skips)   [E] fp32 out
+ * The two products take dz rounded to bf16.  x [T, d] bf16, w_router [E, d]
+ * bf16, logits [T, E] fp32 (moe_route's output), bias [E] fp32 or NULL,
+ * topk_idx [T, k], d_topk_w [T, k] fp32.  Needs E % 8 == 0; pre-selection
+ * without renormalisation together with group-limited routing is
+ * MOE_EUNSUPPORTED.  ws: moe_workspace_bytes(MOE_ENTRY_ROUTE_BACKWARD).
+ */
+int moe_route_backward(const moe_config* cfg, const void* x, const void* w_router,
+                       const float* logits, const float* bias, const int32_t* topk_idx,
+                       const float* d_topk_w, float* d_logits, void* d_x_router,
+                       void* d_w_router, float* d_bias, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/*
+ * dispatch backward: d_x[t] = sum_j d_x_perm[slot_of[t*k+j]] (+ d_x_router[t]
+ * when not NULL), fp32 in j order, then one bf16 rounding.  [T, d] bf16 out.
+ */
+int moe_unpermute_backward(const moe_config* cfg, const void* d_x_perm, const int32_t* slot_of,
+                           const void* d_x_router, void* d_x, void* stream);
 
 #ifdef __cplusplus
 }

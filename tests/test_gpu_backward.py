@@ -1,0 +1,167 @@
+"""Layer backward parity: every output of the four backward entry points
+against the oracle's float64 backward, on the reduced workloads (several
+GEMM tiles, ragged rows per expert), with experts that get no rows, and with
+an empty batch.
+
+The GPU's forward routing must equal the oracle's on these seeds (checked),
+so both sides differentiate the same piecewise-smooth function.
+
+Tolerances, from the arithmetic.  Every backward value passes through at most
+five bf16 roundings (relative 2^-9 each: dy; the recomputed a and u; h or dh;
+da or du; the output) around fp32 accumulation, so its norm-wise relative
+error is at most about 5 * 2^-9 ~ 1e-2 -> TOL_NORM = 1.5e-2, applied
+  * per expert to the weight gradients (a sum over that expert's rows; an
+    expert without rows must be exactly zero),
+  * per row to the row outputs (dy_perm, dx_perm, dx),
+  * to the whole array for the router quantities (d_topk_w, dz, dz Wr,
+    dz^T x, d_bias), where a token's gate
+    gradients cancel against each other (dz = q (dq - sum q dq)).
+Element by element the error of a short sum can reach many times its rms
+(heavy tails, e.g. a 16-row expert's dW entry), so the elementwise check is a
+coarse guard against isolated wrong values: TOL_ELEM = 0.15 of max(|want|,
+rms(want))."""
+import numpy as np
+import pytest
+import torch
+
+from _gpu import alloc, f64, host, log, rel_err, routing_kwargs, run_stages, upload
+from oracle import moe_oracle as om
+from top_routing_expert_amd import binding as B
+from top_routing_expert_amd import configs as C
+from top_routing_expert_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+TOL_NORM = 1.5e-2
+TOL_ELEM = 0.15
+
+
+def _backward(shape, dev, buf, d_out):
+    """combine -> FFN -> router -> dispatch backward through the C ABI."""
+    cfg = B.config(shape)
+    T, d, E, k, f = shape.T, shape.d, shape.E, shape.k, shape.f
+    bf, f32 = torch.bfloat16, torch.float32
+    g = dict(
+        d_y_perm=torch.full((T * k, d), 3.0, dtype=bf, device="cuda"),
+        d_topk_w=torch.full((T, k), 3.0, dtype=f32, device="cuda"),
+        d_x_perm=torch.full((T * k, d), 3.0, dtype=bf, device="cuda"),
+        d_w_gate=torch.full((E, f, d), 3.0, dtype=bf, device="cuda"),
+        d_w_up=torch.full((E, f, d), 3.0, dtype=bf, device="cuda"),
+        d_w_down=torch.full((E, d, f), 3.0, dtype=bf, device="cuda"),
+        d_logits=torch.full((T, E), 3.0, dtype=f32, device="cuda"),
+        d_x_router=torch.full((T, d), 3.0, dtype=bf, device="cuda"),
+        d_w_router=torch.full((E, d), 3.0, dtype=bf, device="cuda"),
+        d_bias=torch.full((E,), 3.0, dtype=f32, device="cuda"),
+        d_x=torch.full((T, d), 3.0, dtype=bf, device="cuda"),
+    )
+    B.moe_combine_backward(cfg, d_out, buf["y_perm"], buf["slot_of"], buf["topk_w"],
+                           g["d_y_perm"], g["d_topk_w"])
+    B.moe_ffn_backward(cfg, buf["x_perm"], buf["expert_offsets"], dev["w_gate"], dev["w_up"],
+                       dev["w_down"], g["d_y_perm"], g["d_x_perm"], g["d_w_gate"], g["d_w_up"],
+                       g["d_w_down"], B.workspace(cfg, "ffn_backward"))
+    B.moe_route_backward(cfg, dev["x"], dev["w_router"], buf["logits"], dev["bias"],
+                         buf["topk_idx"], g["d_topk_w"], g["d_logits"], g["d_x_router"],
+                         g["d_w_router"], g["d_bias"], B.workspace(cfg, "route_backward"))
+    B.moe_unpermute_backward(cfg, g["d_x_perm"], buf["slot_of"], g["d_x_router"], g["d_x"])
+    torch.cuda.synchronize()
+    return g
+
+
+# (GPU output, oracle key, norm-wise grouping: "expert", "row" or "all")
+PAIRS = [("d_topk_w", "d_topk_w", "all"), ("d_y_perm", "dy_perm", "row"),
+         ("d_x_perm", "dx_perm", "row"), ("d_w_gate", "dw_gate", "expert"),
+         ("d_w_up", "dw_up", "expert"), ("d_w_down", "dw_down", "expert"),
+         ("d_logits", "dz", "all"), ("d_x_router", "dx_router", "all"),
+         ("d_w_router", "dw_router", "all"), ("d_bias", "d_bias", "all"), ("d_x", "dx", "row")]
+
+
+def norm_err(got, want, group):
+    """Largest norm-wise relative error over the groups (leading index for
+    "expert" and "row"); a group whose reference is exactly zero must be
+    exactly zero."""
+    got, want = f64(got), np.asarray(want, np.float64)
+    if group == "all":
+        got, want = got.reshape(1, -1), want.reshape(1, -1)
+    else:
+        got, want = got.reshape(got.shape[0], -1), want.reshape(want.shape[0], -1)
+    num = np.sqrt(np.sum((got - want) ** 2, axis=1))
+    den = np.sqrt(np.sum(want * want, axis=1))
+    zero = den == 0
+    assert np.all(num[zero] == 0), "nonzero output where the reference is exactly zero"
+    return float(np.max(num[~zero] / den[~zero])) if np.any(~zero) else 0.0
+
+
+def _check(shape, seed):
+    inp = I.make_inputs(shape, seed=seed)
+    dout_bits = I.make_grad_out(shape, seed)
+    dev, buf = upload(inp), alloc(shape)
+    run_stages(shape, dev, buf)
+    kw = routing_kwargs(shape)
+    ref_fwd = om.layer(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
+                       inp["w_down"], ep_ranks=shape.ep_ranks, **kw)
+    assert np.array_equal(host(buf["topk_idx"]), ref_fwd["topk_idx"])
+    g = _backward(shape, dev, buf, B.to_device(dout_bits))
+    ref = om.layer_backward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
+                            inp["w_down"], om.widen_bf16(dout_bits), fwd=ref_fwd,
+                            ep_ranks=shape.ep_ranks, **kw)
+    bad = {}
+    line = []
+    for gname, rname, group in PAIRS:
+        want = ref[rname]
+        got = host(g[gname])
+        en, ee = norm_err(got, want, group), rel_err(got, want)
+        line.append(f"{gname}={en:.1e}/{ee:.1e}")
+        if not (en <= TOL_NORM and ee <= TOL_ELEM):
+            bad[gname] = (en, ee)
+    log(f"  norm/elem errors {shape.name}: " + " ".join(line))
+    assert not bad, bad
+    return ref_fwd, ref, g
+
+
+@pytest.mark.parametrize("key", ["e8", "e64", "e16", "e256"])
+def test_layer_backward_small_shapes(key):
+    shape = C.SMALL[key]
+    log(f"[backward] {shape.name}")
+    _check(shape, seed=31)
+
+
+def test_backward_experts_without_rows():
+    """E = 64 experts for 20 tokens x 2 choices: most experts get no rows and
+    must get exactly zero weight gradients; dgrad tiles hold 1-3 rows."""
+    shape = C.SMALL["e64"].replace(name="bwd-sparse", T=20, presel=0)
+    log(f"[backward] {shape.name}")
+    fwd, _, g = _check(shape, seed=5)
+    counts = np.diff(fwd["offsets"])
+    empty = np.flatnonzero(counts == 0)
+    assert empty.size > 0
+    for n in ("d_w_gate", "d_w_up", "d_w_down"):
+        assert np.all(host(g[n])[empty] == 0), n
+
+
+def test_backward_single_choice_has_no_router_gradient():
+    shape = C.SMALL["e8"].replace(name="bwd-k1", k=1)
+    log(f"[backward] {shape.name}")
+    _, _, g = _check(shape, seed=7)
+    assert np.all(host(g["d_logits"]) == 0)
+    assert np.all(host(g["d_w_router"]) == 0)
+
+
+def test_backward_empty_batch():
+    shape = C.SMALL["e8"].replace(name="bwd-empty", T=0)
+    log(f"[backward] {shape.name}")
+    cfg = B.config(shape)
+    E, d, f = shape.E, shape.d, shape.f
+    offs = torch.zeros(E + 1, dtype=torch.int32, device="cuda")
+    w = {n: torch.ones(s, dtype=torch.bfloat16, device="cuda")
+         for n, s in (("g", (E, f, d)), ("u", (E, f, d)), ("d", (E, d, f)), ("r", (E, d)))}
+    dwg = torch.full((E, f, d), 3.0, dtype=torch.bfloat16, device="cuda")
+    dwu, dwd = dwg.clone(), torch.full((E, d, f), 3.0, dtype=torch.bfloat16, device="cuda")
+    dwr = torch.full((E, d), 3.0, dtype=torch.bfloat16, device="cuda")
+    db = torch.full((E,), 3.0, dtype=torch.float32, device="cuda")
+    B.moe_ffn_backward(cfg, None, offs, w["g"], w["u"], w["d"], None, None, dwg, dwu, dwd,
+                       B.workspace(cfg, "ffn_backward"))
+    B.moe_route_backward(cfg, None, w["r"], None, None, None, None, None, None, dwr, db,
+                         B.workspace(cfg, "route_backward"))
+    torch.cuda.synchronize()
+    for t in (dwg, dwu, dwd, dwr, db):
+        assert torch.count_nonzero(t).item() == 0

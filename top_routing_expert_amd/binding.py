@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi35
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3
 MOE_F32, MOE_BF16 = 0, 1
-ENTRY = {"route": 1, "permute": 2, "ffn": 3, "combine": 4, "layer": 5, "route_stats": 6}
+ENTRY = {"route": 1, "permute": 2, "ffn": 3, "combine": 4, "layer": 5, "route_stats": 6,
+         "ffn_backward": 7, "route_backward": 8}
 
 CONFIG_FIELDS = ("T", "d", "E", "k", "f", "n_group", "topk_group", "presel", "renorm",
                  "ep_ranks", "dtype")
@@ -30,7 +31,8 @@ EXPORTS = ("moe_strerror", "moe_validate", "moe_workspace_bytes", "moe_route", "
            "moe_ffn_gate_up", "moe_ffn_down", "moe_grouped_ffn", "moe_combine", "moe_layer_fwd",
            "moe_packed_weight_bytes", "moe_pack_weights", "moe_ffn_gate_up_packed",
            "moe_ffn_gate_up_packed_gather", "moe_ffn_down_packed", "moe_layer_fwd_packed",
-           "moe_route_stats", "moe_quantize_fp8", "moe_dequantize_fp8")
+           "moe_route_stats", "moe_quantize_fp8", "moe_dequantize_fp8", "moe_combine_backward",
+           "moe_ffn_backward", "moe_route_backward", "moe_unpermute_backward")
 
 
 class MoEConfig(ctypes.Structure):
@@ -79,6 +81,11 @@ def lib() -> ctypes.CDLL:
         L.moe_quantize_fp8.argtypes = [cfgp, vp, vp, vp, vp]
         L.moe_dequantize_fp8.argtypes = [cfgp, vp, vp, vp, vp, vp]
         L.moe_ffn_down_packed.argtypes = [cfgp, vp, vp, vp, vp, vp]
+        L.moe_combine_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_ffn_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_route_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                         vp]
+        L.moe_unpermute_backward.argtypes = [cfgp, vp, vp, vp, vp, vp]
         L.moe_layer_fwd_packed.argtypes = [cfgp, vp, vp, vp, vp, vp, vp,
                                            ctypes.POINTER(MoELayerBufs), vp, sz, vp]
         for name in EXPORTS[1:]:
@@ -257,6 +264,39 @@ def moe_dequantize_fp8(cfg, codes, src_of, scale_zero, x_perm, stream=None):
     _check("moe_dequantize_fp8",
            lib().moe_dequantize_fp8(ctypes.byref(cfg), _ptr(codes), _ptr(src_of), _ptr(scale_zero),
                                     _ptr(x_perm), _stream(stream)))
+
+
+def moe_combine_backward(cfg, d_out, y_perm, slot_of, topk_w, d_y_perm, d_topk_w, stream=None):
+    _check("moe_combine_backward",
+           lib().moe_combine_backward(ctypes.byref(cfg), _ptr(d_out), _ptr(y_perm), _ptr(slot_of),
+                                      _ptr(topk_w), _ptr(d_y_perm), _ptr(d_topk_w),
+                                      _stream(stream)))
+
+
+def moe_ffn_backward(cfg, x_perm, expert_offsets, w_gate, w_up, w_down, d_y_perm, d_x_perm,
+                     d_w_gate, d_w_up, d_w_down, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check("moe_ffn_backward",
+           lib().moe_ffn_backward(ctypes.byref(cfg), _ptr(x_perm), _ptr(expert_offsets),
+                                  _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(d_y_perm),
+                                  _ptr(d_x_perm), _ptr(d_w_gate), _ptr(d_w_up), _ptr(d_w_down),
+                                  wp, wn, _stream(stream)))
+
+
+def moe_route_backward(cfg, x, w_router, logits, bias, topk_idx, d_topk_w, d_logits, d_x_router,
+                       d_w_router, d_bias, ws=None, stream=None):
+    wp, wn = _ws(ws)
+    _check("moe_route_backward",
+           lib().moe_route_backward(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(logits),
+                                    _ptr(bias), _ptr(topk_idx), _ptr(d_topk_w), _ptr(d_logits),
+                                    _ptr(d_x_router), _ptr(d_w_router), _ptr(d_bias), wp, wn,
+                                    _stream(stream)))
+
+
+def moe_unpermute_backward(cfg, d_x_perm, slot_of, d_x_router, d_x, stream=None):
+    _check("moe_unpermute_backward",
+           lib().moe_unpermute_backward(ctypes.byref(cfg), _ptr(d_x_perm), _ptr(slot_of),
+                                        _ptr(d_x_router), _ptr(d_x), _stream(stream)))
 
 
 def moe_ffn_down_packed(cfg, h, expert_offsets, packed_down, y_perm, stream=None):

@@ -246,6 +246,14 @@ int moe_workspace_bytes(const moe_config* cfg, int entry, size_t* bytes) {
       if ((s = check_routing(cfg)) != MOE_OK) return s;
       *bytes = cfg->T ? align256(route_stats_ws_bytes(*cfg)) : 0;
       return MOE_OK;
+    case MOE_ENTRY_FFN_BACKWARD:
+      if ((s = check_core(cfg)) != MOE_OK) return s;
+      *bytes = align256(ffn_backward_ws_bytes(*cfg));
+      return MOE_OK;
+    case MOE_ENTRY_ROUTE_BACKWARD:
+      if ((s = check_routing(cfg)) != MOE_OK) return s;
+      *bytes = align256(route_backward_ws_bytes(*cfg));
+      return MOE_OK;
     default:
       return MOE_EINVAL;
   }
@@ -445,6 +453,75 @@ int moe_layer_fwd_packed(const moe_config* cfg, const void* x, const void* w_rou
                      return do_ffn_packed(*cfg, act, src, offs, packed_gate_up, packed_down, h, y,
                                           st);
                    });
+}
+
+int moe_combine_backward(const moe_config* cfg, const void* d_out, const void* y_perm,
+                         const int32_t* slot_of, const float* topk_w, void* d_y_perm,
+                         float* d_topk_w, void* stream) {
+  int s = check_core(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (cfg->T == 0) return MOE_OK;
+  if (!d_out || !y_perm || !slot_of || !topk_w || !d_y_perm || !d_topk_w || !aligned16(d_out) ||
+      !aligned16(y_perm) || !aligned16(d_y_perm))
+    return MOE_EINVAL;
+  return status_of(launch_combine_backward(*cfg, d_out, y_perm, slot_of, topk_w, d_y_perm,
+                                           d_topk_w, static_cast<hipStream_t>(stream)));
+}
+
+int moe_ffn_backward(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
+                     const void* w_gate, const void* w_up, const void* w_down,
+                     const void* d_y_perm, void* d_x_perm, void* d_w_gate, void* d_w_up,
+                     void* d_w_down, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_core(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (!expert_offsets || !w_gate || !w_up || !w_down || !d_w_gate || !d_w_up || !d_w_down)
+    return MOE_EINVAL;
+  if (cfg->T > 0 && (!x_perm || !d_y_perm || !d_x_perm)) return MOE_EINVAL;
+  const void* al[] = {x_perm, w_gate, w_up, w_down, d_y_perm, d_x_perm, d_w_gate, d_w_up, d_w_down, ws};
+  for (const void* p : al)
+    if (p && !aligned16(p)) return MOE_EINVAL;
+  if ((s = check_ws(ffn_backward_ws_bytes(*cfg), ws, ws_bytes)) != MOE_OK) return s;
+  return status_of(launch_ffn_backward(*cfg, x_perm, expert_offsets, w_gate, w_up, w_down,
+                                       d_y_perm, d_x_perm, d_w_gate, d_w_up, d_w_down, ws,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int moe_route_backward(const moe_config* cfg, const void* x, const void* w_router,
+                       const float* logits, const float* bias, const int32_t* topk_idx,
+                       const float* d_topk_w, float* d_logits, void* d_x_router,
+                       void* d_w_router, float* d_bias, void* ws, size_t ws_bytes,
+                       void* stream) {
+  int s = check_routing(cfg);
+  if (s != MOE_OK) return s;
+  const moe_config& c = *cfg;
+  if (c.dtype != MOE_BF16 || c.E % 8) return MOE_EUNSUPPORTED;
+  if (!c.renorm && c.presel > 0 && c.n_group > 1 && c.topk_group < c.n_group)
+    return MOE_EUNSUPPORTED;
+  if (!w_router || !d_w_router) return MOE_EINVAL;
+  if (c.T > 0 && (!x || !logits || !topk_idx || !d_topk_w || !d_logits || !d_x_router))
+    return MOE_EINVAL;
+  const void* al[] = {x, w_router, d_x_router, d_w_router, ws};
+  for (const void* p : al)
+    if (p && !aligned16(p)) return MOE_EINVAL;
+  if ((s = check_ws(route_backward_ws_bytes(c), ws, ws_bytes)) != MOE_OK) return s;
+  return status_of(launch_route_backward(c, x, w_router, logits, bias, topk_idx, d_topk_w,
+                                         d_logits, d_x_router, d_w_router, d_bias, ws,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int moe_unpermute_backward(const moe_config* cfg, const void* d_x_perm, const int32_t* slot_of,
+                           const void* d_x_router, void* d_x, void* stream) {
+  int s = check_core(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (cfg->T == 0) return MOE_OK;
+  if (!d_x_perm || !slot_of || !d_x || !aligned16(d_x_perm) || !aligned16(d_x) ||
+      (d_x_router && !aligned16(d_x_router)))
+    return MOE_EINVAL;
+  return status_of(launch_unpermute_backward(*cfg, d_x_perm, slot_of, d_x_router, d_x,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

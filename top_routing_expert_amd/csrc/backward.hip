@@ -1,0 +1,659 @@
+// Layer backward on the cached routing.
+//
+// Pages: [SyncTax] §2.4 (the backward retraces the forward's routing from the
+// routing indices kept by the forward; it is the forward's mirror) and
+// [V4-overlap], PP bubble section (a layer's backward turns dy into dx and the
+// weight gradient dW = x^T dy).  Every product C = A B of the forward gives
+// dA = dC B^T and dB = A^T dC:
+//   combine    out[t] = sum_j g[t,j] y[p(t,j)]:
+//              dy[p(t,j)] = g[t,j] dout[t],  dg[t,j] = <dout[t], y[p(t,j)]>
+//   down       y = h Wd^T:       dh = dy Wd,   dWd_e = dy_e^T h_e
+//   SwiGLU     h = SiLU(a) u:    da = dh u SiLU'(a),  du = dh SiLU(a),
+//              SiLU'(a) = sig(a) (1 + a (1 - sig(a)))
+//   gate/up    a = x Wg^T, u = x Wu^T:  dx = da Wg + du Wu,
+//              dWg_e = da_e^T x_e,  dWu_e = du_e^T x_e
+//   dispatch   x_perm[p] = x[src(p)]:  dx[t] = sum of the k rows of token t
+//   gates      softmax of s = z + b over the support set S (the k chosen, the
+//              P pre-selected, or all E): ds_l = q_l (dq_l - sum_j g_j dg_j)
+//              on S; dz = ds, db = sum_t dz[t];  z = x Wr^T: dx += dz Wr,
+//              dWr = dz^T x.
+//
+// gfx950 design
+//  * One MFMA kernel serves every backward product.  dgrad (dh, dx, the
+//    router's dz Wr) runs over the expert row segments like the forward, with
+//    the expert's weights read in their natural [K, N] layout; wgrad (dW) runs
+//    per expert over its row segment as the reduction.  Operands whose k is
+//    not contiguous in memory (the weights in dgrad, both activations in
+//    wgrad) are transposed on their way into LDS: a thread loads an 8 (k) x 8
+//    block with eight 16-byte loads, transposes it in registers (v_perm) and
+//    writes eight 16-byte LDS rows, so the MFMA fragments are 16-byte LDS
+//    reads on both sides.
+//  * Block tile 128 x 128, four waves 2 x 2 of 64 x 64, 64-wide k stages
+//    double-buffered in LDS (64 KB, two blocks per CU); the next stage's
+//    global loads are in flight while the current stage's MFMAs run.
+//  * Tiles with rows or k past the end read zeros, so no product has a ragged
+//    special case; an expert without rows gets zero weight gradients.
+#include <cmath>
+
+#include "common.h"
+#include "tiles.h"
+
+namespace moe {
+
+constexpr int kGT = 128;      // block tile rows and columns
+constexpr int kGK = 64;       // k per stage
+constexpr int kGPieces = 8;   // 16-byte pieces per LDS row (64 k)
+
+struct GemmPart {
+  const uint16_t* a;
+  const uint16_t* b;
+  long lda, ldb;   // leading dimensions in elements
+  long b_estride;  // dgrad: elements between two experts' weight matrices
+  int K;           // dgrad: k extent of this part
+};
+
+struct GemmArgs {
+  GemmPart part[2];
+  int nparts;
+  uint16_t* c;
+  long ldc, c_estride;
+  const int32_t* offs;
+  int E, rows;
+  int M, N;  // wgrad: the per-expert output is M x N; dgrad: N only
+  int m_tiles, n_tiles, band;
+};
+
+// 8 x 8 bf16 transpose: in[r] holds row r (8 values, 2 per word); out[c]
+// holds column c.  Word w of out[c] is (in[2w][c], in[2w+1][c]).
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      out[c][w] = __builtin_amdgcn_perm(in[2 * w + 1][c >> 1], in[2 * w][c >> 1], sel);
+  }
+}
+
+__device__ __forceinline__ int gpiece(int r, int q) { return r * kGPieces + (q ^ (r & 7)); }
+
+// WGRAD = false: dgrad.  A (M side) = activation rows [row0, row_end) of the
+// tile's expert, k contiguous; B (N side) = the expert's [K, N] weights.
+// WGRAD = true: wgrad.  The reduction runs over the expert's row segment;
+// A = act_a rows (M contiguous), B = act_b rows (N contiguous).
+template <bool WGRAD>
+__global__ __launch_bounds__(256, 2) void grouped_gemm_bwd_kernel(GemmArgs g) {
+  __shared__ u32x4 sA[2][kGT * kGPieces];
+  __shared__ u32x4 sB[2][kGT * kGPieces];
+  __shared__ int s_tile[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  int e, m0, m_lim, n0, k0 = 0, k_lim = 0;
+  if (!WGRAD) {
+    if (wave == 0) place_tile<kGT>(g.offs, g.E, g.rows, g.n_tiles, g.band, lane, s_tile);
+    __syncthreads();
+    e = s_tile[0];
+    if (e < 0) return;  // block-uniform
+    m0 = s_tile[1];
+    m_lim = s_tile[2] - s_tile[1];
+    n0 = s_tile[3] * kGT;
+  } else {
+    const int per_e = g.m_tiles * g.n_tiles;
+    e = blockIdx.x / per_e;
+    const int r = blockIdx.x - e * per_e;
+    m0 = (r / g.n_tiles) * kGT;
+    n0 = (r % g.n_tiles) * kGT;
+    m_lim = min(kGT, g.M - m0);
+    const int o0 = min(max(g.offs[e], 0), g.rows);
+    const int o1 = min(max(g.offs[e + 1], o0), g.rows);
+    k0 = o0;
+    k_lim = o1 - o0;
+  }
+  const int n_lim = min(kGT, g.N - n0);
+
+  // stage list: the parts one after the other (scalars: no indexed copies of
+  // the kernel arguments)
+  const int k0_ext = WGRAD ? k_lim : g.part[0].K;
+  const int k1_ext = g.nparts > 1 ? (WGRAD ? k_lim : g.part[1].K) : 0;
+  const int nst0 = (k0_ext + kGK - 1) / kGK;
+  const int nst1 = (k1_ext + kGK - 1) / kGK;
+  const int S = nst0 + nst1;
+
+  // ---- loader.  Threads 0..127 stage A, 128..255 stage B.  A k-contiguous
+  // operand (dgrad A) is 1024 pieces: thread t takes pieces t + 128 j.  A
+  // transposed operand is 128 blocks of 8 k x 8 m/n: thread t takes block t
+  // (k block t / 16, column block t % 16).
+  const bool is_a = tid < 128;
+  const int lt = tid & 127;
+  const bool kcontig = !WGRAD && is_a;
+  u32x4 stg[8];
+
+  auto load_stage = [&](int s) {
+    const bool p1 = s >= nst0;
+    const int ks = (s - (p1 ? nst0 : 0)) * kGK;  // k offset inside the part
+    const uint16_t* pa = p1 ? g.part[1].a : g.part[0].a;
+    const uint16_t* pb = p1 ? g.part[1].b : g.part[0].b;
+    const long lda = p1 ? g.part[1].lda : g.part[0].lda;
+    const long ldb = p1 ? g.part[1].ldb : g.part[0].ldb;
+    const long bes = p1 ? g.part[1].b_estride : g.part[0].b_estride;
+    const int pk = p1 ? g.part[1].K : g.part[0].K;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    if (kcontig) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int piece = lt + 128 * j, r = piece >> 3, q = piece & 7;
+        const int k = ks + 8 * q;
+        const bool ok = r < m_lim && k < pk;
+        const uint16_t* src = pa + (size_t)(m0 + (ok ? r : 0)) * lda + (ok ? k : 0);
+        stg[j] = ok ? *reinterpret_cast<const u32x4*>(src) : zero;
+      }
+    } else {
+      const int kb = lt >> 4, cb = lt & 15;
+      const int col = 8 * cb;
+      const int klim = WGRAD ? k_lim : pk;
+      const int clim = is_a ? m_lim : n_lim;
+      const uint16_t* base;
+      long ld;
+      if (WGRAD) {
+        base = is_a ? pa + (size_t)k0 * lda + m0 : pb + (size_t)k0 * ldb + n0;
+        ld = is_a ? lda : ldb;
+      } else {
+        base = pb + (size_t)e * bes + n0;
+        ld = ldb;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = ks + 8 * kb + j;
+        const bool ok = k < klim && col < clim;
+        const uint16_t* src = base + (size_t)(ok ? k : 0) * ld + (ok ? col : 0);
+        stg[j] = ok ? *reinterpret_cast<const u32x4*>(src) : zero;
+      }
+    }
+  };
+  auto store_stage = [&](int buf) {
+    u32x4* dst = is_a ? sA[buf] : sB[buf];
+    if (kcontig) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int piece = lt + 128 * j;
+        dst[gpiece(piece >> 3, piece & 7)] = stg[j];
+      }
+    } else {
+      const int kb = lt >> 4, cb = lt & 15;
+      u32x4 tr[8];
+      transpose8x8(stg, tr);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) dst[gpiece(8 * cb + c, kb)] = tr[c];
+    }
+  };
+
+  // ---- fragments: wave (wm, wn) owns rows wm*64.. of A and wn*64.. of B
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lk = lane >> 5;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  if (S > 0) {
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+  }
+  for (int s = 0; s < S; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < S) load_stage(s + 1);
+    const u32x4* a_l = sA[buf];
+    const u32x4* b_l = sB[buf];
+#pragma unroll
+    for (int sl = 0; sl < kGK / 16; ++sl) {
+      const int q = 2 * sl + lk;
+      bf16x8 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[i] = as_bf16x8(a_l[gpiece(wm * 64 + 32 * i + (lane & 31), q)]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[j] = as_bf16x8(b_l[gpiece(wn * 64 + 32 * j + (lane & 31), q)]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    }
+    if (s + 1 < S) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: acc[i][j][4 gq + r] = C[m = wm*64 + 32 i + (lane & 31)]
+  // [n = wn*64 + 32 j + 8 gq + 4 lk + r]: four consecutive n, one 8-byte store.
+  uint16_t* cbase = g.c + (WGRAD ? (size_t)e * g.c_estride : 0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = wm * 64 + 32 * i + (lane & 31);
+    if (m >= m_lim) continue;
+    uint16_t* crow = cbase + (size_t)(m0 + m) * g.ldc + n0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int n = wn * 64 + 32 * j + 8 * gq + 4 * lk;
+        if (n >= n_lim) continue;
+        u32x2 pk;
+        pk.x = pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]);
+        pk.y = pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
+        *reinterpret_cast<u32x2*>(crow + n) = pk;
+      }
+  }
+}
+
+// dgrad: C[rows, N] = A[rows, K] B_e[K, N] (+ the second part), by expert
+// row segments.  Every K, N and leading dimension is a multiple of 8.
+static hipError_t launch_dgrad(const GemmPart* parts, int nparts, const int32_t* offs, int E,
+                               int rows, int N, uint16_t* c, long ldc, hipStream_t st) {
+  GemmArgs g{};
+  for (int p = 0; p < nparts; ++p) g.part[p] = parts[p];
+  g.nparts = nparts;
+  g.c = c;
+  g.ldc = ldc;
+  g.offs = offs;
+  g.E = E;
+  g.rows = rows;
+  g.N = N;
+  g.n_tiles = div_up(N, kGT);
+  g.band = 8;
+  const long total = (long)g.n_tiles * worst_row_tiles(rows, E, kGT);
+  const int blocks = (int)((total + 7) / 8 * 8);
+  grouped_gemm_bwd_kernel<false><<<blocks, 256, 0, st>>>(g);
+  return hipGetLastError();
+}
+
+// wgrad: C_e[M, N] = A_rows^T B_rows over expert e's row segment, for every
+// expert (zeros for an expert without rows).
+static hipError_t launch_wgrad(const uint16_t* a, long lda, const uint16_t* b, long ldb,
+                               const int32_t* offs, int E, int rows, int M, int N, uint16_t* c,
+                               long ldc, long c_estride, hipStream_t st) {
+  GemmArgs g{};
+  g.part[0].a = a;
+  g.part[0].b = b;
+  g.part[0].lda = lda;
+  g.part[0].ldb = ldb;
+  g.nparts = 1;
+  g.c = c;
+  g.ldc = ldc;
+  g.c_estride = c_estride;
+  g.offs = offs;
+  g.E = E;
+  g.rows = rows;
+  g.M = M;
+  g.N = N;
+  g.m_tiles = div_up(M, kGT);
+  g.n_tiles = div_up(N, kGT);
+  const long blocks = (long)E * g.m_tiles * g.n_tiles;
+  grouped_gemm_bwd_kernel<true><<<(int)blocks, 256, 0, st>>>(g);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------- combine backward
+// One wave per token: dy[p(t,j)] = bf16(g dout[t]); dg[t,j] = <dout[t], y[p(t,j)]>
+// (fp32, lane partials then a fixed xor tree).
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__global__ __launch_bounds__(256) void combine_backward_kernel(
+    const u32x4* __restrict__ dout, const u32x4* __restrict__ y, const int32_t* __restrict__ slot_of,
+    const float* __restrict__ topk_w, u32x4* __restrict__ dy, float* __restrict__ dg, int T, int k,
+    int nvec, int A) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave
+  const u32x4* drow = dout + (size_t)t * nvec;
+  for (int j = 0; j < k; ++j) {
+    const int p = min(max(slot_of[(size_t)t * k + j], 0), A - 1);
+    const float w = topk_w[(size_t)t * k + j];
+    const u32x4* yrow = y + (size_t)p * nvec;
+    u32x4* dyrow = dy + (size_t)p * nvec;
+    float dot = 0.f;
+    for (int v = lane; v < nvec; v += 64) {
+      const u32x4 a = drow[v], b = yrow[v];
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a0 = bf16_lo(a[q]), a1 = bf16_hi(a[q]);
+        dot = fmaf(a0, bf16_lo(b[q]), dot);
+        dot = fmaf(a1, bf16_hi(b[q]), dot);
+        o[q] = pack_bf16x2(w * a0, w * a1);
+      }
+      dyrow[v] = o;
+    }
+    dot = wave_sum_f(dot);
+    if (lane == 0) dg[(size_t)t * k + j] = dot;
+  }
+}
+
+// ------------------------------------------------------------- SwiGLU backward
+// Per element: h = SiLU(a) u; da = dh u SiLU'(a); du = dh SiLU(a).  da and du
+// overwrite a and u in place; h goes to its own buffer.
+__global__ __launch_bounds__(256) void swiglu_backward_kernel(const u32x4* __restrict__ dh,
+                                                              u32x4* __restrict__ a_da,
+                                                              u32x4* __restrict__ u_du,
+                                                              u32x4* __restrict__ h, long nvec) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nvec) return;
+  const u32x4 va = a_da[i], vu = u_du[i], vd = dh[i];
+  u32x4 oh, oa, ou;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float r[2][3];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const float a = hh ? bf16_hi(va[q]) : bf16_lo(va[q]);
+      const float u = hh ? bf16_hi(vu[q]) : bf16_lo(vu[q]);
+      const float d = hh ? bf16_hi(vd[q]) : bf16_lo(vd[q]);
+      const float sig = 1.0f / (1.0f + expf(-a));
+      const float silu = a * sig;
+      r[hh][0] = silu * u;
+      r[hh][1] = d * u * sig * (1.0f + a * (1.0f - sig));
+      r[hh][2] = d * silu;
+    }
+    oh[q] = pack_bf16x2(r[0][0], r[1][0]);
+    oa[q] = pack_bf16x2(r[0][1], r[1][1]);
+    ou[q] = pack_bf16x2(r[0][2], r[1][2]);
+  }
+  h[i] = oh;
+  a_da[i] = oa;
+  u_du[i] = ou;
+}
+
+// ------------------------------------------------------------- gates backward
+// One wave per token, EPL experts per lane.  q = softmax of s = z + b over the
+// support set, m = s of the first chosen expert; dq_e = dg_j for the j-th
+// chosen expert; ds_e = q_e (dq_e - sum_e' q_e' dq_e') on the support, 0
+// elsewhere.  The pre-selected set (presel > 0, no renormalisation) is the
+// top presel experts by (s desc, e asc), ranked in LDS.
+template <int EPL>
+__global__ __launch_bounds__(256) void gates_backward_kernel(
+    const float* __restrict__ logits, const float* __restrict__ bias,
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ dg, int T, int E, int k,
+    int presel, int renorm, float* __restrict__ dz, uint16_t* __restrict__ dz_bf16) {
+  extern __shared__ float s_sc[];  // [4 waves][E], for the pre-selection ranks
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + w;
+  const bool live = t < T;  // wave-uniform
+  const bool rank_sel = !renorm && presel > 0;
+  float sc[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    sc[i] = -INFINITY;
+    if (live && e < E) {
+      const float z = logits[(size_t)t * E + e];
+      sc[i] = bias ? z + bias[e] : z;
+      if (rank_sel) s_sc[w * E + e] = sc[i];
+    }
+  }
+  __syncthreads();
+  if (!live) return;
+  const int* idx = topk_idx + (size_t)t * k;
+  const int first = min(max(idx[0], 0), E - 1);
+  const float m = bias ? logits[(size_t)t * E + first] + bias[first] : logits[(size_t)t * E + first];
+  float q[EPL], dq[EPL];
+  float den = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    dq[i] = 0.f;
+    bool chosen = false;
+    for (int j = 0; j < k; ++j)
+      if (idx[j] == e) {
+        chosen = true;
+        dq[i] = dg[(size_t)t * k + j];
+      }
+    bool in = false;
+    if (e < E) {
+      if (renorm) {
+        in = chosen;
+      } else if (presel > 0) {
+        int rank = 0;
+        for (int o = 0; o < E; ++o) {
+          const float so = s_sc[w * E + o];
+          rank += (so > sc[i]) || (so == sc[i] && o < e);
+        }
+        in = rank < presel;
+      } else {
+        in = true;
+      }
+    }
+    q[i] = in ? expf(sc[i] - m) : 0.f;
+    den += q[i];
+  }
+  den = wave_sum_f(den);
+  float inner = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    q[i] = q[i] / den;
+    inner += q[i] * dq[i];
+  }
+  inner = wave_sum_f(inner);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) {
+      const float ds = q[i] * (dq[i] - inner);
+      dz[(size_t)t * E + e] = ds;
+      const __bf16 b = (__bf16)ds;
+      dz_bf16[(size_t)t * E + e] = __builtin_bit_cast(uint16_t, b);
+    }
+  }
+}
+
+// d_bias: column sums of dz in a fixed order: 64-column x 128-row partials,
+// then one thread per column adds the partials in row order.
+constexpr int kBiasRows = 128;
+constexpr int kBiasMaxChunks = 4096;
+static int bias_chunk_rows(int T) { return T > kBiasRows * kBiasMaxChunks ? div_up(T, kBiasMaxChunks) : kBiasRows; }
+__global__ __launch_bounds__(64) void bias_partial_kernel(const float* __restrict__ dz, int T, int E,
+                                                          int chunk_rows, float* __restrict__ part) {
+  const int e = blockIdx.x * 64 + threadIdx.x;
+  const int r0 = blockIdx.y * chunk_rows;
+  if (e >= E) return;
+  float s = 0.f;
+  const int r1 = min(T, r0 + chunk_rows);
+  for (int t = r0; t < r1; ++t) s += dz[(size_t)t * E + e];
+  part[(size_t)blockIdx.y * E + e] = s;
+}
+__global__ __launch_bounds__(256) void bias_final_kernel(const float* __restrict__ part, int chunks,
+                                                         int E, float* __restrict__ db) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= E) return;
+  float s = 0.f;
+  for (int c = 0; c < chunks; ++c) s += part[(size_t)c * E + e];
+  db[e] = s;
+}
+
+// ------------------------------------------------------------- dispatch backward
+// One wave per token: dx[t] = sum_j dx_perm[p(t,j)] (+ dx_router[t]), fp32 in
+// j order, one bf16 rounding.
+__global__ __launch_bounds__(256) void unpermute_sum_kernel(const u32x4* __restrict__ dxp,
+                                                            const int32_t* __restrict__ slot_of,
+                                                            const u32x4* __restrict__ dxr,
+                                                            u32x4* __restrict__ dx, int T, int k,
+                                                            int nvec, int A) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  for (int v = lane; v < nvec; v += 64) {
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int p = min(max(slot_of[(size_t)t * k + j], 0), A - 1);
+      const u32x4 r = dxp[(size_t)p * nvec + v];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_lo(r[q]);
+        acc[2 * q + 1] += bf16_hi(r[q]);
+      }
+    }
+    if (dxr) {
+      const u32x4 r = dxr[(size_t)t * nvec + v];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_lo(r[q]);
+        acc[2 * q + 1] += bf16_hi(r[q]);
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
+    dx[(size_t)t * nvec + v] = o;
+  }
+}
+
+// ------------------------------------------------------------- launchers
+hipError_t launch_combine_backward(const moe_config& c, const void* d_out, const void* y_perm,
+                                   const int32_t* slot_of, const float* topk_w, void* d_y_perm,
+                                   float* d_topk_w, hipStream_t st) {
+  const int nvec = c.d / 8;
+  combine_backward_kernel<<<div_up(c.T, 4), 256, 0, st>>>(
+      static_cast<const u32x4*>(d_out), static_cast<const u32x4*>(y_perm), slot_of, topk_w,
+      static_cast<u32x4*>(d_y_perm), d_topk_w, c.T, c.k, nvec, c.T * c.k);
+  return hipGetLastError();
+}
+
+size_t ffn_backward_ws_bytes(const moe_config& c) {
+  return 4 * (size_t)c.T * c.k * c.f * sizeof(uint16_t);
+}
+
+hipError_t launch_ffn_backward(const moe_config& c, const void* x_perm, const int32_t* offs,
+                               const void* wg, const void* wu, const void* wd, const void* d_y_perm,
+                               void* d_x_perm, void* d_wg, void* d_wu, void* d_wd, void* ws,
+                               hipStream_t st) {
+  const int rows = c.T * c.k, d = c.d, f = c.f, E = c.E;
+  const size_t af = (size_t)rows * f;
+  uint16_t* a = static_cast<uint16_t*>(ws);  // a, then da
+  uint16_t* u = a + af;                       // u, then du
+  uint16_t* h = u + af;
+  uint16_t* dh = h + af;
+  const auto* X = static_cast<const uint16_t*>(x_perm);
+  const auto* dY = static_cast<const uint16_t*>(d_y_perm);
+  const auto* Wg = static_cast<const uint16_t*>(wg);
+  const auto* Wu = static_cast<const uint16_t*>(wu);
+  const auto* Wd = static_cast<const uint16_t*>(wd);
+  hipError_t err;
+  if (rows == 0) {  // no rows: every weight gradient is zero
+    if ((err = launch_wgrad(dY, d, h, f, offs, E, 0, d, f, static_cast<uint16_t*>(d_wd), f,
+                            (long)d * f, st)) != hipSuccess)
+      return err;
+    if ((err = launch_wgrad(a, f, X, d, offs, E, 0, f, d, static_cast<uint16_t*>(d_wg), d,
+                            (long)f * d, st)) != hipSuccess)
+      return err;
+    return launch_wgrad(u, f, X, d, offs, E, 0, f, d, static_cast<uint16_t*>(d_wu), d,
+                        (long)f * d, st);
+  }
+  // recompute the gate and up pre-activations (the forward keeps only h)
+  if ((err = launch_grouped_linear(c, X, offs, Wg, a, f, d, st)) != hipSuccess) return err;
+  if ((err = launch_grouped_linear(c, X, offs, Wu, u, f, d, st)) != hipSuccess) return err;
+  // dh = dy Wd_e   (Wd_e is [d, f])
+  {
+    GemmPart p{dY, Wd, d, f, (long)d * f, d};
+    if ((err = launch_dgrad(&p, 1, offs, E, rows, f, dh, f, st)) != hipSuccess) return err;
+  }
+  // h, da, du
+  {
+    const long nvec = (long)af / 8;
+    swiglu_backward_kernel<<<div_up(nvec, 256), 256, 0, st>>>(
+        reinterpret_cast<const u32x4*>(dh), reinterpret_cast<u32x4*>(a),
+        reinterpret_cast<u32x4*>(u), reinterpret_cast<u32x4*>(h), nvec);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  // dWd_e = dy_e^T h_e   [d, f]
+  if ((err = launch_wgrad(dY, d, h, f, offs, E, rows, d, f, static_cast<uint16_t*>(d_wd), f,
+                          (long)d * f, st)) != hipSuccess)
+    return err;
+  // dx = da Wg_e + du Wu_e   (Wg_e, Wu_e are [f, d])
+  {
+    GemmPart p[2] = {{a, Wg, f, d, (long)f * d, f}, {u, Wu, f, d, (long)f * d, f}};
+    if ((err = launch_dgrad(p, 2, offs, E, rows, d, static_cast<uint16_t*>(d_x_perm), d, st)) !=
+        hipSuccess)
+      return err;
+  }
+  // dWg_e = da_e^T x_e, dWu_e = du_e^T x_e   [f, d]
+  if ((err = launch_wgrad(a, f, X, d, offs, E, rows, f, d, static_cast<uint16_t*>(d_wg), d,
+                          (long)f * d, st)) != hipSuccess)
+    return err;
+  return launch_wgrad(u, f, X, d, offs, E, rows, f, d, static_cast<uint16_t*>(d_wu), d,
+                      (long)f * d, st);
+}
+
+size_t route_backward_ws_bytes(const moe_config& c) {
+  const size_t dzb = ((size_t)c.T * c.E * sizeof(uint16_t) + 255) / 256 * 256;
+  const int T1 = c.T > 0 ? c.T : 1;
+  const size_t part = (size_t)div_up(T1, bias_chunk_rows(T1)) * c.E * sizeof(float);
+  return dzb + 256 + part;
+}
+
+hipError_t launch_route_backward(const moe_config& c, const void* x, const void* w_router,
+                                 const float* logits, const float* bias, const int32_t* topk_idx,
+                                 const float* d_topk_w, float* d_logits, void* d_x_router,
+                                 void* d_w_router, float* d_bias, void* ws, hipStream_t st) {
+  const int T = c.T, E = c.E, d = c.d;
+  char* wsb = static_cast<char*>(ws);
+  uint16_t* dzb = reinterpret_cast<uint16_t*>(wsb);
+  const size_t dzb_bytes = ((size_t)T * E * sizeof(uint16_t) + 255) / 256 * 256;
+  int32_t* offs = reinterpret_cast<int32_t*>(wsb + dzb_bytes);  // {0, T}
+  float* part = reinterpret_cast<float*>(wsb + dzb_bytes + 256);
+  hipError_t err;
+  if (T > 0) {
+    const dim3 grid(div_up(T, 4));
+    const size_t lds = (!c.renorm && c.presel > 0) ? 4 * (size_t)E * sizeof(float) : 0;
+    if (E <= 64)
+      gates_backward_kernel<1><<<grid, 256, lds, st>>>(logits, bias, topk_idx, d_topk_w, T, E, c.k,
+                                                       c.presel, c.renorm, d_logits, dzb);
+    else if (E <= 256)
+      gates_backward_kernel<4><<<grid, 256, lds, st>>>(logits, bias, topk_idx, d_topk_w, T, E, c.k,
+                                                       c.presel, c.renorm, d_logits, dzb);
+    else
+      gates_backward_kernel<16><<<grid, 256, lds, st>>>(logits, bias, topk_idx, d_topk_w, T, E,
+                                                        c.k, c.presel, c.renorm, d_logits, dzb);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if (d_bias) {
+    const int rows_per = bias_chunk_rows(T);
+    const int chunks = div_up(T, rows_per);
+    if (chunks > 0)
+      bias_partial_kernel<<<dim3(div_up(E, 64), chunks), 64, 0, st>>>(d_logits, T, E, rows_per,
+                                                                      part);
+    bias_final_kernel<<<div_up(E, 256), 256, 0, st>>>(part, chunks, E, d_bias);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  if ((err = launch_fill_i32(offs, 1, 0, st)) != hipSuccess) return err;
+  if ((err = launch_fill_i32(offs + 1, 1, T, st)) != hipSuccess) return err;
+  // dx_router = dz Wr   (Wr is [E, d]: the [K, N] weights of one group)
+  {
+    GemmPart p{dzb, static_cast<const uint16_t*>(w_router), E, d, 0, E};
+    if ((err = launch_dgrad(&p, 1, offs, 1, T, d, static_cast<uint16_t*>(d_x_router), d, st)) !=
+        hipSuccess)
+      return err;
+  }
+  // dWr = dz^T x   [E, d]
+  return launch_wgrad(dzb, E, static_cast<const uint16_t*>(x), d, offs, 1, T, E, d,
+                      static_cast<uint16_t*>(d_w_router), d, 0, st);
+}
+
+hipError_t launch_unpermute_backward(const moe_config& c, const void* d_x_perm,
+                                     const int32_t* slot_of, const void* d_x_router, void* d_x,
+                                     hipStream_t st) {
+  const int nvec = c.d / 8;
+  unpermute_sum_kernel<<<div_up(c.T, 4), 256, 0, st>>>(
+      static_cast<const u32x4*>(d_x_perm), slot_of, static_cast<const u32x4*>(d_x_router),
+      static_cast<u32x4*>(d_x), c.T, c.k, nvec, c.T * c.k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

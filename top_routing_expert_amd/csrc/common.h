@@ -96,4 +96,24 @@ hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t
 
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
 
+// Layer backward (backward.hip); bf16 only.
+hipError_t launch_grouped_linear(const moe_config& c, const uint16_t* act, const int32_t* offs,
+                                 const uint16_t* w, uint16_t* out, int N, int K, hipStream_t st);
+hipError_t launch_combine_backward(const moe_config& c, const void* d_out, const void* y_perm,
+                                   const int32_t* slot_of, const float* topk_w, void* d_y_perm,
+                                   float* d_topk_w, hipStream_t st);
+size_t ffn_backward_ws_bytes(const moe_config& c);
+hipError_t launch_ffn_backward(const moe_config& c, const void* x_perm, const int32_t* offs,
+                               const void* wg, const void* wu, const void* wd, const void* d_y_perm,
+                               void* d_x_perm, void* d_wg, void* d_wu, void* d_wd, void* ws,
+                               hipStream_t st);
+size_t route_backward_ws_bytes(const moe_config& c);
+hipError_t launch_route_backward(const moe_config& c, const void* x, const void* w_router,
+                                 const float* logits, const float* bias, const int32_t* topk_idx,
+                                 const float* d_topk_w, float* d_logits, void* d_x_router,
+                                 void* d_w_router, float* d_bias, void* ws, hipStream_t st);
+hipError_t launch_unpermute_backward(const moe_config& c, const void* d_x_perm,
+                                     const int32_t* slot_of, const void* d_x_router, void* d_x,
+                                     hipStream_t st);
+
 }  // namespace moe

@@ -406,6 +406,15 @@ hipError_t launch_ffn_gate_up(const moe_config& c, const void* x_perm, const int
   return hipGetLastError();
 }
 
+// out[rows, N] = act[rows, K] W_e^T by expert row segments, W_e [N, K] (bf16).
+hipError_t launch_grouped_linear(const moe_config& c, const uint16_t* act, const int32_t* offs,
+                                 const uint16_t* w, uint16_t* out, int N, int K, hipStream_t st) {
+  const long rows = (long)c.T * c.k;
+  const GemmPlan p = plan_gemm(rows, c.E, N, false);
+  launch_gemm<false>(p, act, offs, w, nullptr, out, c.E, N, K, (int)rows, st);
+  return hipGetLastError();
+}
+
 hipError_t launch_ffn_down(const moe_config& c, const void* h, const int32_t* offs, const void* wd,
                            void* y, hipStream_t st) {
   const long rows = (long)c.T * c.k;

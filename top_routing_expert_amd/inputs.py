@@ -22,7 +22,7 @@ import numpy as np
 
 from .configs import MoEShape
 
-TID_X, TID_ROUTER, TID_BIAS, TID_GATE, TID_UP, TID_DOWN = range(6)
+TID_X, TID_ROUTER, TID_BIAS, TID_GATE, TID_UP, TID_DOWN, TID_DOUT = range(7)
 X_BLOCK_ROWS = 1024
 
 
@@ -90,6 +90,12 @@ def make_expert_weight(shape: MoEShape, seed: int, tid: int, pool=None) -> np.nd
 
     _run(pool, one, range(shape.E))
     return out
+
+
+def make_grad_out(shape: MoEShape, seed: int) -> np.ndarray:
+    """The gradient arriving at the layer's output for a backward step: [T, d]
+    standard normal (bf16 bits for bf16 shapes)."""
+    return _normal_block(seed, TID_DOUT, 0, (shape.T, shape.d), 1.0, shape.dtype == "bf16")
 
 
 def make_router(shape: MoEShape, seed: int) -> np.ndarray:
