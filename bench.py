@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--diagnostics", action="store_true",
                     help="also time the routing diagnostics (moe_route_stats) after the dispatch; "
                          "reported as its own phase and included in the step")
+    ap.add_argument("--backward", action="store_true",
+                    help="time forward + backward (combine, grouped FFN, router and dispatch "
+                         "backward on the forward's routing) instead of the forward alone")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     a = ap.parse_args()
@@ -108,6 +111,20 @@ def algorithmic(shape, counts, gather=False):
         "fp8_quantize": dict(bytes=T * d * s + T * d + 8 * T, flops=0),
         # codes of each row's token (and its scale) in, src_of in, the bf16 row out
         "fp8_dequantize": dict(bytes=A * d + 8 * A + 4 * A + A * d * s, flops=0),
+        # d_out and y_perm in, dy_perm out, indices and gates
+        "combine_bwd": dict(bytes=T * d * s + 2 * A * d * s + 12 * A, flops=4 * A * d),
+        # weights read by the recompute (Wg, Wu), dh (Wd) and dx (Wg, Wu); the three
+        # weight gradients written; x_perm and dy read twice each; a, u, h, dh written,
+        # then a, u, dh read and h, da, du written by the SwiGLU step, h, da, du read
+        # twice each by the products.  16 A d f flops: recompute 4, dh 2, dWd 2, dx 4,
+        # dWg + dWu 4.
+        "ffn_bwd": dict(bytes=5 * e_nz * f * d * s + 3 * E * f * d * s + 5 * A * d * s
+                        + 13 * A * f * s + 8 * (E + 1), flops=16 * A * d * f),
+        # logits, bias, indices and gate gradients in; dz out (fp32 + bf16); x, Wr in;
+        # dz Wr and dz^T x out
+        "route_bwd": dict(bytes=T * E * 4 * 2 + T * E * 2 + 8 * A + T * d * s * 2
+                          + 2 * E * d * s, flops=4 * T * E * d),
+        "unpermute_bwd": dict(bytes=A * d * s + 2 * T * d * s + 4 * A, flops=A * d),
     }
 
 
@@ -191,6 +208,11 @@ def main():
         a.ffn = "rowmajor"  # packed images are bf16 only
     if a.ffn != "packed":
         a.dispatch = "copy"  # the gather is a packed-FFN kernel
+    if a.backward:
+        if shape.dtype != "bf16":
+            print("--backward needs a bf16 workload", file=sys.stderr)
+            sys.exit(2)
+        a.dispatch = "copy"  # the FFN backward reads the dispatched rows
     gather = a.dispatch == "gather"
     fp8 = a.dispatch == "fp8"
     log(f"workload {shape.name}: generating inputs")
@@ -223,7 +245,8 @@ def main():
         log("packing expert weights")
         pgu, pd = B.pack_weights(cfg, dev["w_gate"], dev["w_up"], dev["w_down"], stream=stream)
         torch.cuda.synchronize()
-        dev["w_gate"] = dev["w_up"] = dev["w_down"] = None
+        if not a.backward:  # the backward reads the weights in their own layout
+            dev["w_gate"] = dev["w_up"] = dev["w_down"] = None
         if a.dispatch == "gather":
             gate_up = lambda: B.moe_ffn_gate_up_packed_gather(cfg, dev["x"], buf["src"],
                                                                buf["offs"], pgu, buf["h"], stream)
@@ -269,6 +292,34 @@ def main():
                                                          buf["stats"], ws_s, stream)
         phases_run = phases_run[:2] + ("route_stats",) + phases_run[2:]
 
+    if a.backward:
+        grad = dict(
+            dout=B.to_device(I.make_grad_out(shape, C.CONFIGS.index(shape) + 1)),
+            dy=torch.empty((A, d), dtype=dt, device="cuda"),
+            dw=torch.empty((T, k), dtype=torch.float32, device="cuda"),
+            dxp=torch.empty((A, d), dtype=dt, device="cuda"),
+            dwg=torch.empty((E, f, d), dtype=dt, device="cuda"),
+            dwu=torch.empty((E, f, d), dtype=dt, device="cuda"),
+            dwd=torch.empty((E, d, f), dtype=dt, device="cuda"),
+            dz=torch.empty((T, E), dtype=torch.float32, device="cuda"),
+            dxr=torch.empty((T, d), dtype=dt, device="cuda"),
+            dwr=torch.empty((E, d), dtype=dt, device="cuda"),
+            db=torch.empty(E, dtype=torch.float32, device="cuda") if dev["bias"] is not None else None,
+            dx=torch.empty((T, d), dtype=dt, device="cuda"),
+        )
+        ws_fb, ws_rb = B.workspace(cfg, "ffn_backward"), B.workspace(cfg, "route_backward")
+        calls["combine_bwd"] = lambda: B.moe_combine_backward(
+            cfg, grad["dout"], buf["y"], buf["slot"], buf["w"], grad["dy"], grad["dw"], stream)
+        calls["ffn_bwd"] = lambda: B.moe_ffn_backward(
+            cfg, buf["xp"], buf["offs"], dev["w_gate"], dev["w_up"], dev["w_down"], grad["dy"],
+            grad["dxp"], grad["dwg"], grad["dwu"], grad["dwd"], ws_fb, stream)
+        calls["route_bwd"] = lambda: B.moe_route_backward(
+            cfg, dev["x"], dev["w_router"], buf["logits"], dev["bias"], buf["idx"], grad["dw"],
+            grad["dz"], grad["dxr"], grad["dwr"], grad["db"], ws_rb, stream)
+        calls["unpermute_bwd"] = lambda: B.moe_unpermute_backward(
+            cfg, grad["dxp"], buf["slot"], grad["dxr"], grad["dx"], stream)
+        phases_run = phases_run + ("combine_bwd", "ffn_bwd", "route_bwd", "unpermute_bwd")
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
@@ -309,7 +360,8 @@ def main():
         log(f"cpu baseline: oracle on {a.cpu_tokens} tokens")
         cpu = cpu_baseline(shape, inp, a.cpu_tokens)
     res = {
-        "metric": "MoE-layer fwd tokens/s @1 GPU; % bf16 MFMA peak (FFN), % HBM BW (route/permute)",
+        "metric": ("MoE-layer fwd+bwd tokens/s @1 GPU (training step)" if a.backward else
+                   "MoE-layer fwd tokens/s @1 GPU; % bf16 MFMA peak (FFN), % HBM BW (route/permute)"),
         "value": T * a.steps / elapsed,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -324,7 +376,8 @@ def main():
         "config": {"workload": shape.name, "T": T, "d": d, "E": E, "k": k, "f": f,
                    "n_group": shape.n_group, "topk_group": shape.topk_group,
                    "presel": shape.presel, "renorm": shape.renorm, "ep_ranks": R,
-                   "ffn_weights": a.ffn, "dispatch": a.dispatch, "parallelism": "single GPU"},
+                   "ffn_weights": a.ffn, "dispatch": a.dispatch, "backward": a.backward,
+                   "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "phases": {p: {kk: (round(v, 5) if isinstance(v, float) else v) for kk, v in ph.items()}
