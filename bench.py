@@ -247,7 +247,12 @@ def main():
         torch.cuda.synchronize()
         if not a.backward:  # the backward reads the weights in their own layout
             dev["w_gate"] = dev["w_up"] = dev["w_down"] = None
-        if a.dispatch == "gather":
+        if a.backward:  # training forward: also keep the pre-activations a and u
+            buf["a"] = torch.empty((A, f), dtype=dt, device="cuda")
+            buf["u"] = torch.empty((A, f), dtype=dt, device="cuda")
+            gate_up = lambda: B.moe_ffn_gate_up_packed_train(cfg, buf["xp"], None, buf["offs"], pgu,
+                                                              buf["h"], buf["a"], buf["u"], stream)
+        elif a.dispatch == "gather":
             gate_up = lambda: B.moe_ffn_gate_up_packed_gather(cfg, dev["x"], buf["src"],
                                                                buf["offs"], pgu, buf["h"], stream)
         else:
@@ -312,7 +317,8 @@ def main():
             cfg, grad["dout"], buf["y"], buf["slot"], buf["w"], grad["dy"], grad["dw"], stream)
         calls["ffn_bwd"] = lambda: B.moe_ffn_backward(
             cfg, buf["xp"], buf["offs"], dev["w_gate"], dev["w_up"], dev["w_down"], grad["dy"],
-            grad["dxp"], grad["dwg"], grad["dwu"], grad["dwd"], ws_fb, stream)
+            grad["dxp"], grad["dwg"], grad["dwu"], grad["dwd"], ws_fb, stream, a=buf.get("a"),
+            u=buf.get("u"))
         calls["route_bwd"] = lambda: B.moe_route_backward(
             cfg, dev["x"], dev["w_router"], buf["logits"], dev["bias"], buf["idx"], grad["dw"],
             grad["dz"], grad["dxr"], grad["dwr"], grad["db"], ws_rb, stream)
@@ -346,6 +352,11 @@ def main():
                                   for s in range(a.steps)])) for i, p in enumerate(phases_run)}
     ms_per_step = elapsed * 1e3 / a.steps
     work = algorithmic(shape, counts, gather)
+    if a.backward and a.ffn == "packed":  # the saved pre-activations, written by the forward
+        work["ffn_gate_up"]["bytes"] += 2 * A * f * (2 if shape.dtype == "bf16" else 4)
+        # and read by the backward instead of the recompute (no weight re-read, 4 A d f fewer flops)
+        work["ffn_bwd"]["bytes"] -= 2 * int((counts > 0).sum()) * f * d * 2
+        work["ffn_bwd"]["flops"] -= 4 * A * d * f
     phases = {p: dict(ms=phase_ms[p], **roofline_of(work[p], phase_ms[p])) for p in phases_run}
     dom = phases[DOMINANT]
     traffic = measured_traffic(a.ffn, shape.name, a.dispatch)

@@ -399,9 +399,20 @@ int moe_combine_backward(const moe_config* cfg, const void* d_out, const void* y
  * u/du, h, dh), 256-byte aligned.
  */
 int moe_ffn_backward(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
-                     const void* w_gate, const void* w_up, const void* w_down,
-                     const void* d_y_perm, void* d_x_perm, void* d_w_gate, void* d_w_up,
-                     void* d_w_down, void* ws, size_t ws_bytes, void* stream);
+                     const void* w_gate, const void* w_up, const void* w_down, const void* a,
+                     const void* u, const void* d_y_perm, void* d_x_perm, void* d_w_gate,
+                     void* d_w_up, void* d_w_down, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Training forward of the first FFN GEMM: moe_ffn_gate_up_packed (src_of ==
+ * NULL: act is x_perm) or moe_ffn_gate_up_packed_gather (src_of != NULL: act
+ * is the token-order x), which also writes the pre-activations a = x Wg^T and
+ * u = x Wu^T ([T*k, f] bf16 each, rounded once from the same fp32 sums as h)
+ * for moe_ffn_backward, so the backward does not recompute them.
+ */
+int moe_ffn_gate_up_packed_train(const moe_config* cfg, const void* act, const int32_t* src_of,
+                                 const int32_t* expert_offsets, const void* packed_gate_up,
+                                 void* h, void* a, void* u, void* stream);
 
 /*
  * router backward through the gate softmax, selection held fixed:

@@ -36,7 +36,7 @@ TOL_NORM = 1.5e-2
 TOL_ELEM = 0.15
 
 
-def _backward(shape, dev, buf, d_out):
+def _backward(shape, dev, buf, d_out, a=None, u=None):
     """combine -> FFN -> router -> dispatch backward through the C ABI."""
     cfg = B.config(shape)
     T, d, E, k, f = shape.T, shape.d, shape.E, shape.k, shape.f
@@ -58,7 +58,7 @@ def _backward(shape, dev, buf, d_out):
                            g["d_y_perm"], g["d_topk_w"])
     B.moe_ffn_backward(cfg, buf["x_perm"], buf["expert_offsets"], dev["w_gate"], dev["w_up"],
                        dev["w_down"], g["d_y_perm"], g["d_x_perm"], g["d_w_gate"], g["d_w_up"],
-                       g["d_w_down"], B.workspace(cfg, "ffn_backward"))
+                       g["d_w_down"], B.workspace(cfg, "ffn_backward"), a=a, u=u)
     B.moe_route_backward(cfg, dev["x"], dev["w_router"], buf["logits"], dev["bias"],
                          buf["topk_idx"], g["d_topk_w"], g["d_logits"], g["d_x_router"],
                          g["d_w_router"], g["d_bias"], B.workspace(cfg, "route_backward"))
@@ -165,3 +165,50 @@ def test_backward_empty_batch():
     torch.cuda.synchronize()
     for t in (dwg, dwu, dwd, dwr, db):
         assert torch.count_nonzero(t).item() == 0
+
+
+@pytest.mark.parametrize("key,gather", [("e8", True), ("e16", False), ("e256", True)])
+def test_backward_on_saved_preactivations(key, gather):
+    """Training forward: the packed first GEMM also writes a = x Wg^T and
+    u = x Wu^T (h bit for bit as the inference kernel's); the backward then
+    takes them instead of recomputing, to the same bounds."""
+    shape = C.SMALL[key]
+    log(f"[backward] saved a/u {shape.name} gather={gather}")
+    inp = I.make_inputs(shape, seed=31)
+    dout_bits = I.make_grad_out(shape, 31)
+    dev, buf = upload(inp), alloc(shape)
+    cfg = B.config(shape)
+    B.moe_route(cfg, dev["x"], dev["w_router"], dev["bias"], buf["logits"], buf["topk_idx"],
+                buf["topk_w"], B.workspace(cfg, "route"))
+    B.moe_permute(cfg, dev["x"], buf["topk_idx"], buf["expert_offsets"], buf["rank_offsets"],
+                  buf["slot_of"], buf["src_of"], buf["x_perm"], B.workspace(cfg, "permute"))
+    pgu, pd = B.pack_weights(cfg, dev["w_gate"], dev["w_up"], dev["w_down"])
+    A, f = shape.T * shape.k, shape.f
+    a = torch.full((A, f), 5.0, dtype=torch.bfloat16, device="cuda")
+    u = torch.full((A, f), 5.0, dtype=torch.bfloat16, device="cuda")
+    act, src = (dev["x"], buf["src_of"]) if gather else (buf["x_perm"], None)
+    B.moe_ffn_gate_up_packed_train(cfg, act, src, buf["expert_offsets"], pgu, buf["h"], a, u)
+    h_inf = torch.empty_like(buf["h"])
+    B.moe_ffn_gate_up_packed(cfg, buf["x_perm"], buf["expert_offsets"], pgu, h_inf)
+    B.moe_ffn_down_packed(cfg, buf["h"], buf["expert_offsets"], pd, buf["y_perm"])
+    B.moe_combine(cfg, buf["y_perm"], buf["slot_of"], buf["topk_w"], buf["out"])
+    torch.cuda.synchronize()
+    assert torch.equal(buf["h"].view(torch.int16), h_inf.view(torch.int16))
+    kw = routing_kwargs(shape)
+    ref_fwd = om.layer(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
+                       inp["w_down"], ep_ranks=shape.ep_ranks, **kw)
+    assert np.array_equal(host(buf["topk_idx"]), ref_fwd["topk_idx"])
+    ref = om.layer_backward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
+                            inp["w_down"], om.widen_bf16(dout_bits), fwd=ref_fwd,
+                            ep_ranks=shape.ep_ranks, **kw)
+    # a and u: one bf16 rounding of an fp32 sum of bf16 products
+    assert norm_err(host(a), ref["a"], "row") <= 2 ** -8
+    assert norm_err(host(u), ref["u"], "row") <= 2 ** -8
+    g = _backward(shape, dev, buf, B.to_device(dout_bits), a=a, u=u)
+    bad = {}
+    for gname, rname, group in PAIRS:
+        got = host(g[gname])
+        en, ee = norm_err(got, ref[rname], group), rel_err(got, ref[rname])
+        if not (en <= TOL_NORM and ee <= TOL_ELEM):
+            bad[gname] = (en, ee)
+    assert not bad, bad

@@ -32,7 +32,8 @@ EXPORTS = ("moe_strerror", "moe_validate", "moe_workspace_bytes", "moe_route", "
            "moe_packed_weight_bytes", "moe_pack_weights", "moe_ffn_gate_up_packed",
            "moe_ffn_gate_up_packed_gather", "moe_ffn_down_packed", "moe_layer_fwd_packed",
            "moe_route_stats", "moe_quantize_fp8", "moe_dequantize_fp8", "moe_combine_backward",
-           "moe_ffn_backward", "moe_route_backward", "moe_unpermute_backward")
+           "moe_ffn_backward", "moe_route_backward", "moe_unpermute_backward",
+           "moe_ffn_gate_up_packed_train")
 
 
 class MoEConfig(ctypes.Structure):
@@ -82,7 +83,9 @@ def lib() -> ctypes.CDLL:
         L.moe_dequantize_fp8.argtypes = [cfgp, vp, vp, vp, vp, vp]
         L.moe_ffn_down_packed.argtypes = [cfgp, vp, vp, vp, vp, vp]
         L.moe_combine_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp]
-        L.moe_ffn_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_ffn_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                       sz, vp]
+        L.moe_ffn_gate_up_packed_train.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_route_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                          vp]
         L.moe_unpermute_backward.argtypes = [cfgp, vp, vp, vp, vp, vp]
@@ -273,12 +276,21 @@ def moe_combine_backward(cfg, d_out, y_perm, slot_of, topk_w, d_y_perm, d_topk_w
                                       _stream(stream)))
 
 
+def moe_ffn_gate_up_packed_train(cfg, act, src_of, expert_offsets, packed_gate_up, h, a, u,
+                                 stream=None):
+    _check("moe_ffn_gate_up_packed_train",
+           lib().moe_ffn_gate_up_packed_train(ctypes.byref(cfg), _ptr(act), _ptr(src_of),
+                                              _ptr(expert_offsets), _ptr(packed_gate_up), _ptr(h),
+                                              _ptr(a), _ptr(u), _stream(stream)))
+
+
 def moe_ffn_backward(cfg, x_perm, expert_offsets, w_gate, w_up, w_down, d_y_perm, d_x_perm,
-                     d_w_gate, d_w_up, d_w_down, ws=None, stream=None):
+                     d_w_gate, d_w_up, d_w_down, ws=None, stream=None, a=None, u=None):
     wp, wn = _ws(ws)
     _check("moe_ffn_backward",
            lib().moe_ffn_backward(ctypes.byref(cfg), _ptr(x_perm), _ptr(expert_offsets),
-                                  _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(d_y_perm),
+                                  _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(a), _ptr(u),
+                                  _ptr(d_y_perm),
                                   _ptr(d_x_perm), _ptr(d_w_gate), _ptr(d_w_up), _ptr(d_w_down),
                                   wp, wn, _stream(stream)))
 

@@ -423,6 +423,20 @@ int moe_ffn_gate_up_packed_gather(const moe_config* cfg, const void* x, const in
                        static_cast<hipStream_t>(stream));
 }
 
+int moe_ffn_gate_up_packed_train(const moe_config* cfg, const void* act, const int32_t* src_of,
+                                 const int32_t* expert_offsets, const void* packed_gate_up,
+                                 void* h, void* a, void* u, void* stream) {
+  int s = check_packed(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->T == 0) return MOE_OK;
+  if (!act || !expert_offsets || !packed_gate_up || !h || !a || !u || !aligned16(act) ||
+      !aligned16(packed_gate_up) || !aligned16(h) || !aligned16(a) || !aligned16(u))
+    return MOE_EINVAL;
+  return status_of(launch_ffn_gate_up_packed_save(*cfg, act, src_of, expert_offsets,
+                                                  packed_gate_up, h, a, u,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 int moe_ffn_down_packed(const moe_config* cfg, const void* h, const int32_t* expert_offsets,
                         const void* packed_down, void* y_perm, void* stream) {
   int s = check_packed(cfg);
@@ -470,20 +484,22 @@ int moe_combine_backward(const moe_config* cfg, const void* d_out, const void* y
 }
 
 int moe_ffn_backward(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
-                     const void* w_gate, const void* w_up, const void* w_down,
-                     const void* d_y_perm, void* d_x_perm, void* d_w_gate, void* d_w_up,
-                     void* d_w_down, void* ws, size_t ws_bytes, void* stream) {
+                     const void* w_gate, const void* w_up, const void* w_down, const void* a,
+                     const void* u, const void* d_y_perm, void* d_x_perm, void* d_w_gate,
+                     void* d_w_up, void* d_w_down, void* ws, size_t ws_bytes, void* stream) {
   int s = check_core(cfg);
   if (s != MOE_OK) return s;
   if (cfg->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
   if (!expert_offsets || !w_gate || !w_up || !w_down || !d_w_gate || !d_w_up || !d_w_down)
     return MOE_EINVAL;
   if (cfg->T > 0 && (!x_perm || !d_y_perm || !d_x_perm)) return MOE_EINVAL;
-  const void* al[] = {x_perm, w_gate, w_up, w_down, d_y_perm, d_x_perm, d_w_gate, d_w_up, d_w_down, ws};
+  if (!a != !u) return MOE_EINVAL;
+  const void* al[] = {x_perm, w_gate, w_up, w_down, a, u, d_y_perm, d_x_perm, d_w_gate, d_w_up,
+                      d_w_down, ws};
   for (const void* p : al)
     if (p && !aligned16(p)) return MOE_EINVAL;
   if ((s = check_ws(ffn_backward_ws_bytes(*cfg), ws, ws_bytes)) != MOE_OK) return s;
-  return status_of(launch_ffn_backward(*cfg, x_perm, expert_offsets, w_gate, w_up, w_down,
+  return status_of(launch_ffn_backward(*cfg, x_perm, expert_offsets, w_gate, w_up, w_down, a, u,
                                        d_y_perm, d_x_perm, d_w_gate, d_w_up, d_w_down, ws,
                                        static_cast<hipStream_t>(stream)));
 }

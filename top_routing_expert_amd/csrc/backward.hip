@@ -75,7 +75,13 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
   }
 }
 
-__device__ __forceinline__ int gpiece(int r, int q) { return r * kGPieces + (q ^ (r & 7)); }
+// LDS row r (128 bytes, 8 pieces of 16 bytes): logical piece q sits at
+// q ^ (r & 7) ^ ((r >> 3) & 7).  The fragment reads (32 consecutive rows, one
+// piece) and the transposed stores (rows 8 apart, one piece) then both spread
+// over all eight piece slots.
+__device__ __forceinline__ int gpiece(int r, int q) {
+  return r * kGPieces + (q ^ (r & 7) ^ ((r >> 3) & 7));
+}
 
 // WGRAD = false: dgrad.  A (M side) = activation rows [row0, row_end) of the
 // tile's expert, k contiguous; B (N side) = the expert's [K, N] weights.
@@ -338,14 +344,15 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
 
 // ------------------------------------------------------------- SwiGLU backward
 // Per element: h = SiLU(a) u; da = dh u SiLU'(a); du = dh SiLU(a).  da and du
-// overwrite a and u in place; h goes to its own buffer.
+// may overwrite a and u (same element, read before written).
 __global__ __launch_bounds__(256) void swiglu_backward_kernel(const u32x4* __restrict__ dh,
-                                                              u32x4* __restrict__ a_da,
-                                                              u32x4* __restrict__ u_du,
+                                                              const u32x4* a_in,
+                                                              const u32x4* u_in, u32x4* da_out,
+                                                              u32x4* du_out,
                                                               u32x4* __restrict__ h, long nvec) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= nvec) return;
-  const u32x4 va = a_da[i], vu = u_du[i], vd = dh[i];
+  const u32x4 va = a_in[i], vu = u_in[i], vd = dh[i];
   u32x4 oh, oa, ou;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -366,8 +373,8 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(const u32x4* __res
     ou[q] = pack_bf16x2(r[0][2], r[1][2]);
   }
   h[i] = oh;
-  a_da[i] = oa;
-  u_du[i] = ou;
+  da_out[i] = oa;
+  du_out[i] = ou;
 }
 
 // ------------------------------------------------------------- gates backward
@@ -531,9 +538,9 @@ size_t ffn_backward_ws_bytes(const moe_config& c) {
 }
 
 hipError_t launch_ffn_backward(const moe_config& c, const void* x_perm, const int32_t* offs,
-                               const void* wg, const void* wu, const void* wd, const void* d_y_perm,
-                               void* d_x_perm, void* d_wg, void* d_wu, void* d_wd, void* ws,
-                               hipStream_t st) {
+                               const void* wg, const void* wu, const void* wd, const void* a_in,
+                               const void* u_in, const void* d_y_perm, void* d_x_perm,
+                               void* d_wg, void* d_wu, void* d_wd, void* ws, hipStream_t st) {
   const int rows = c.T * c.k, d = c.d, f = c.f, E = c.E;
   const size_t af = (size_t)rows * f;
   uint16_t* a = static_cast<uint16_t*>(ws);  // a, then da
@@ -556,9 +563,16 @@ hipError_t launch_ffn_backward(const moe_config& c, const void* x_perm, const in
     return launch_wgrad(u, f, X, d, offs, E, 0, f, d, static_cast<uint16_t*>(d_wu), d,
                         (long)f * d, st);
   }
-  // recompute the gate and up pre-activations (the forward keeps only h)
-  if ((err = launch_grouped_linear(c, X, offs, Wg, a, f, d, st)) != hipSuccess) return err;
-  if ((err = launch_grouped_linear(c, X, offs, Wu, u, f, d, st)) != hipSuccess) return err;
+  // the gate and up pre-activations: the training forward's, else recomputed
+  // (the inference forward keeps only h)
+  const uint16_t* a_src = static_cast<const uint16_t*>(a_in);
+  const uint16_t* u_src = static_cast<const uint16_t*>(u_in);
+  if (!a_src) {
+    if ((err = launch_grouped_linear(c, X, offs, Wg, a, f, d, st)) != hipSuccess) return err;
+    if ((err = launch_grouped_linear(c, X, offs, Wu, u, f, d, st)) != hipSuccess) return err;
+    a_src = a;
+    u_src = u;
+  }
   // dh = dy Wd_e   (Wd_e is [d, f])
   {
     GemmPart p{dY, Wd, d, f, (long)d * f, d};
@@ -568,7 +582,8 @@ hipError_t launch_ffn_backward(const moe_config& c, const void* x_perm, const in
   {
     const long nvec = (long)af / 8;
     swiglu_backward_kernel<<<div_up(nvec, 256), 256, 0, st>>>(
-        reinterpret_cast<const u32x4*>(dh), reinterpret_cast<u32x4*>(a),
+        reinterpret_cast<const u32x4*>(dh), reinterpret_cast<const u32x4*>(a_src),
+        reinterpret_cast<const u32x4*>(u_src), reinterpret_cast<u32x4*>(a),
         reinterpret_cast<u32x4*>(u), reinterpret_cast<u32x4*>(h), nvec);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }

@@ -79,6 +79,12 @@ hipError_t launch_ffn_gate_up_packed(const moe_config& c, const void* x_perm, co
 hipError_t launch_ffn_gate_up_packed_gather(const moe_config& c, const void* x,
                                             const int32_t* src_of, const int32_t* offs,
                                             const void* pgu, void* h, hipStream_t st);
+// gate/up with the pre-activations a = x Wg^T and u = x Wu^T also written
+// (bf16, [rows, f]); src_of != NULL gathers the rows from token order.
+hipError_t launch_ffn_gate_up_packed_save(const moe_config& c, const void* act,
+                                          const int32_t* src_of, const int32_t* offs,
+                                          const void* pgu, void* h, void* a, void* u,
+                                          hipStream_t st);
 hipError_t launch_ffn_down_packed(const moe_config& c, const void* h, const int32_t* offs,
                                   const void* packed_down, void* y, hipStream_t st);
 
@@ -104,9 +110,9 @@ hipError_t launch_combine_backward(const moe_config& c, const void* d_out, const
                                    float* d_topk_w, hipStream_t st);
 size_t ffn_backward_ws_bytes(const moe_config& c);
 hipError_t launch_ffn_backward(const moe_config& c, const void* x_perm, const int32_t* offs,
-                               const void* wg, const void* wu, const void* wd, const void* d_y_perm,
-                               void* d_x_perm, void* d_wg, void* d_wu, void* d_wd, void* ws,
-                               hipStream_t st);
+                               const void* wg, const void* wu, const void* wd, const void* a_in,
+                               const void* u_in, const void* d_y_perm, void* d_x_perm,
+                               void* d_wg, void* d_wu, void* d_wd, void* ws, hipStream_t st);
 size_t route_backward_ws_bytes(const moe_config& c);
 hipError_t launch_route_backward(const moe_config& c, const void* x, const void* w_router,
                                  const float* logits, const float* bias, const int32_t* topk_idx,

@@ -268,11 +268,13 @@ struct JnSel {
 // GATHER: the activation rows are gathered from token order: tile row p reads
 // act row src_of[p] / gk (clamped into [0, gtokens)), so the permuted copy of
 // the activations is never written.
-template <bool GATED, int JMAX, int WF, bool GATHER>
+// SAVE (gated only): also write the pre-activations a and u next to h.
+template <bool GATED, int JMAX, int WF, bool GATHER, bool SAVE = false>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offs,
     const u32x4* __restrict__ wp, uint16_t* __restrict__ out, int E, int N, int K, int rows,
-    int slabs, int band, bool sized, const int32_t* __restrict__ src_of, int gk, int gtokens) {
+    int slabs, int band, bool sized, const int32_t* __restrict__ src_of, int gk, int gtokens,
+    uint16_t* __restrict__ save_a, uint16_t* __restrict__ save_u) {
   constexpr int TM = 32 * JMAX;
   constexpr int TN = GATED ? 128 : 256;       // output features per slab
   constexpr int HB = TM * 128;                // bytes of one 64-wide k half-stage
@@ -561,6 +563,16 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
             pk.x = pack_bf16x2(hv[0], hv[1]);
             pk.y = pack_bf16x2(hv[2], hv[3]);
             *reinterpret_cast<u32x2*>(orow + n) = pk;
+            if (SAVE) {  // training forward: the pre-activations for the backward
+              const size_t o = (size_t)p * N + n;
+              u32x2 pa, pu;
+              pa.x = pack_bf16x2(acc[ii][jj][4 * g], acc[ii][jj][4 * g + 1]);
+              pa.y = pack_bf16x2(acc[ii][jj][4 * g + 2], acc[ii][jj][4 * g + 3]);
+              pu.x = pack_bf16x2(acc[ii][jj][4 * g + 8], acc[ii][jj][4 * g + 9]);
+              pu.y = pack_bf16x2(acc[ii][jj][4 * g + 10], acc[ii][jj][4 * g + 11]);
+              *reinterpret_cast<u32x2*>(save_a + o) = pa;
+              *reinterpret_cast<u32x2*>(save_u + o) = pu;
+            }
           }
         } else {
 #pragma unroll
@@ -641,10 +653,10 @@ static int device_cus() {
 // the E=8/16 and E=64/256 workloads).
 constexpr int kSizedMaxExperts = 16;
 
-template <bool GATED, int JMAX, int WF, bool GATHER>
+template <bool GATED, int JMAX, int WF, bool GATHER, bool SAVE>
 static hipError_t launch_packed_t(const moe_config& c, const void* act, const int32_t* offs,
                                   const void* wp, void* out, const int32_t* src_of,
-                                  hipStream_t st) {
+                                  void* save_a, void* save_u, hipStream_t st) {
   const long rows = (long)c.T * c.k;
   const int N = GATED ? c.f : c.d, K = GATED ? c.d : c.f;
   const PackGeom g = pack_geom(N, K, GATED);
@@ -652,10 +664,11 @@ static hipError_t launch_packed_t(const moe_config& c, const void* act, const in
   const long worst = (long)g.slabs * (WF == 2 ? 1 : 2) * worst_row_tiles(rows, c.E, 32 * JMAX);
   const long cap = ((long)device_cus() + 7) / 8 * 8;
   const int blocks = (int)std::min(cap, (worst + 7) / 8 * 8);
-  grouped_gemm_packed_kernel<GATED, JMAX, WF, GATHER><<<blocks, 256, 0, st>>>(
+  grouped_gemm_packed_kernel<GATED, JMAX, WF, GATHER, SAVE><<<blocks, 256, 0, st>>>(
       static_cast<const uint16_t*>(act), offs, static_cast<const u32x4*>(wp),
       static_cast<uint16_t*>(out), c.E, N, K, (int)rows, g.slabs, 8,
-      /*sized=*/c.E <= kSizedMaxExperts, src_of, c.k, c.T);
+      /*sized=*/c.E <= kSizedMaxExperts, src_of, c.k, c.T, static_cast<uint16_t*>(save_a),
+      static_cast<uint16_t*>(save_u));
   return hipGetLastError();
 }
 
@@ -664,16 +677,18 @@ static hipError_t launch_packed_t(const moe_config& c, const void* act, const in
 // few experts with some hundred rows each: then half-slab tiles of up to 320
 // rows (WF = 1, JMAX = 10), which double the tile count and cover an expert of
 // up to 320 rows with one tile.
-template <bool GATED, bool GATHER>
+template <bool GATED, bool GATHER, bool SAVE = false>
 static hipError_t launch_packed(const moe_config& c, const void* act, const int32_t* offs,
                                 const void* wp, void* out, const int32_t* src_of,
-                                hipStream_t st) {
+                                hipStream_t st, void* save_a = nullptr, void* save_u = nullptr) {
   const long rows = (long)c.T * c.k;
   const PackGeom g = pack_geom(GATED ? c.f : c.d, GATED ? c.d : c.f, GATED);
   const long typical = (long)g.slabs * std::max<long>(c.E, (rows + 255) / 256);
   if (typical < 2L * device_cus())
-    return launch_packed_t<GATED, 10, 1, GATHER>(c, act, offs, wp, out, src_of, st);
-  return launch_packed_t<GATED, 8, 2, GATHER>(c, act, offs, wp, out, src_of, st);
+    return launch_packed_t<GATED, 10, 1, GATHER, SAVE>(c, act, offs, wp, out, src_of, save_a,
+                                                       save_u, st);
+  return launch_packed_t<GATED, 8, 2, GATHER, SAVE>(c, act, offs, wp, out, src_of, save_a, save_u,
+                                                    st);
 }
 
 hipError_t launch_ffn_gate_up_packed(const moe_config& c, const void* x_perm, const int32_t* offs,
@@ -685,6 +700,14 @@ hipError_t launch_ffn_gate_up_packed_gather(const moe_config& c, const void* x,
                                             const int32_t* src_of, const int32_t* offs,
                                             const void* pgu, void* h, hipStream_t st) {
   return launch_packed<true, true>(c, x, offs, pgu, h, src_of, st);
+}
+
+hipError_t launch_ffn_gate_up_packed_save(const moe_config& c, const void* act,
+                                          const int32_t* src_of, const int32_t* offs,
+                                          const void* pgu, void* h, void* a, void* u,
+                                          hipStream_t st) {
+  if (src_of) return launch_packed<true, true, true>(c, act, offs, pgu, h, src_of, st, a, u);
+  return launch_packed<true, false, true>(c, act, offs, pgu, h, nullptr, st, a, u);
 }
 
 hipError_t launch_ffn_down_packed(const moe_config& c, const void* h, const int32_t* offs,
