@@ -28,9 +28,12 @@
 //    block with eight 16-byte loads, transposes it in registers (v_perm) and
 //    writes eight 16-byte LDS rows, so the MFMA fragments are 16-byte LDS
 //    reads on both sides.
-//  * Block tile 128 x 128, four waves 2 x 2 of 64 x 64, 64-wide k stages
-//    double-buffered in LDS (64 KB, two blocks per CU); the next stage's
-//    global loads are in flight while the current stage's MFMAs run.
+//  * Block tiles of 128 x 128 (four waves of 64 x 64, two blocks per CU); the
+//    wgrad also has 256 x 256 (eight waves of 128 x 64, 128 KB of LDS, one
+//    block per CU) where there are enough of them to fill the chip: its
+//    operands are re-read from L2 once per tile, so that halves the traffic.
+//    64-wide k stages double-buffered in LDS; the global loads run two stages
+//    ahead (128) or one (256: a second staging set would not fit).
 //  * Tiles with rows or k past the end read zeros, so no product has a ragged
 //    special case; an expert without rows gets zero weight gradients.
 #include <cmath>
@@ -40,7 +43,6 @@
 
 namespace moe {
 
-constexpr int kGT = 128;      // block tile rows and columns
 constexpr int kGK = 64;       // k per stage
 constexpr int kGPieces = 8;   // 16-byte pieces per LDS row (64 k)
 
@@ -87,8 +89,18 @@ __device__ __forceinline__ int gpiece(int r, int q) {
 // tile's expert, k contiguous; B (N side) = the expert's [K, N] weights.
 // WGRAD = true: wgrad.  The reduction runs over the expert's row segment;
 // A = act_a rows (M contiguous), B = act_b rows (N contiguous).
-template <bool WGRAD>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_bwd_kernel(GemmArgs g) {
+// BT: block tile (rows and columns), 128 with four waves of 64 x 64 (two
+// blocks per CU) or 256 with eight waves of 128 x 64 (one block per CU, half
+// the operand bytes per flop).  Half of the threads stage A, half stage B:
+// BT threads each.
+template <bool WGRAD, int BT>
+__global__ __launch_bounds__(BT / 2 * 4, BT == 128 ? 2 : 1) void grouped_gemm_bwd_kernel(
+    GemmArgs g) {
+  constexpr int kGT = BT;
+  constexpr int NTH = 2 * BT;         // threads
+  constexpr int WN = NTH / 64 / 2;    // waves along N (2 or 4); two along M
+  constexpr int FM = BT / 64;         // 32-row fragments per wave along M
+  constexpr int CB = BT / 8;          // 8-column blocks per row of a transposed stage
   __shared__ u32x4 sA[2][kGT * kGPieces];
   __shared__ u32x4 sB[2][kGT * kGPieces];
   __shared__ int s_tile[4];
@@ -126,67 +138,80 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_bwd_kernel(GemmArgs g) {
   const int nst1 = (k1_ext + kGK - 1) / kGK;
   const int S = nst0 + nst1;
 
-  // ---- loader.  Threads 0..127 stage A, 128..255 stage B.  A k-contiguous
-  // operand (dgrad A) is 1024 pieces: thread t takes pieces t + 128 j.  A
-  // transposed operand is 128 blocks of 8 k x 8 m/n: thread t takes block t
-  // (k block t / 16, column block t % 16).
-  const bool is_a = tid < 128;
-  const int lt = tid & 127;
+  // ---- loader.  Waves 0..NW/2-1 stage A, the others B (BT threads each).  A
+  // k-contiguous operand (dgrad A) is 8 BT pieces: thread t takes pieces
+  // t + BT j (row t/8 + (BT/8) j, piece t % 8).  A transposed operand is BT
+  // blocks of 8 k x 8 m/n: thread t takes block t (k block t / CB, column
+  // block t % CB), load j reading k row 8 (t / CB) + j.
+  // Rows and columns past the tile's end only feed outputs that are never
+  // stored, so inside the buffer they are simply read; k past the end of a
+  // part must read zeros (both operands).  A stage is "plain" when its k is
+  // whole and the tile's rows / columns end inside the buffer: then load j is
+  // one per-thread offset plus j times a block-uniform stride (scalar base
+  // per load).  Otherwise (a part's ragged last stage, the buffer's last
+  // tiles) every load is clamped and masked.  The parts of one product share
+  // lda, ldb and the expert stride (checked by the launcher).
+  const bool is_a = wave < NTH / 128;  // wave-uniform, so the bases stay scalar
+  const int lt = tid % BT;
   const bool kcontig = !WGRAD && is_a;
-  u32x4 stg[8];
+  const long lda = g.part[0].lda, ldb = g.part[0].ldb, bes = g.part[0].b_estride;
+  const long ld = (kcontig || (WGRAD && is_a)) ? lda : ldb;
+  const int kb = lt / CB, cb = lt % CB;
+  // per-thread byte offset of load 0 and the uniform byte stride between loads
+  const uint32_t voff = kcontig ? (uint32_t)(((long)(lt >> 3) * lda + 8 * (lt & 7)) * 2)
+                                : (uint32_t)(((long)(8 * kb) * ld + 8 * cb) * 2);
+  const long jstride = kcontig ? (long)(BT / 8) * lda * 2 : ld * 2;
+  // the tile's rows / columns end inside the buffer
+  const bool inside = kcontig ? m0 + BT <= g.rows
+                              : (is_a ? m0 + BT <= g.M : n0 + BT <= g.N);
+  const int clim = is_a ? m_lim : n_lim;  // transposed operands: a multiple of 8
+  u32x4 stgA[8], stgB[8];  // two stages of staging registers: loads run two stages ahead
 
-  auto load_stage = [&](int s) {
+  auto load_stage = [&](int s, u32x4 (&stg)[8]) {
     const bool p1 = s >= nst0;
     const int ks = (s - (p1 ? nst0 : 0)) * kGK;  // k offset inside the part
     const uint16_t* pa = p1 ? g.part[1].a : g.part[0].a;
     const uint16_t* pb = p1 ? g.part[1].b : g.part[0].b;
-    const long lda = p1 ? g.part[1].lda : g.part[0].lda;
-    const long ldb = p1 ? g.part[1].ldb : g.part[0].ldb;
-    const long bes = p1 ? g.part[1].b_estride : g.part[0].b_estride;
-    const int pk = p1 ? g.part[1].K : g.part[0].K;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    if (kcontig) {
+    const int klim = WGRAD ? k_lim : (p1 ? g.part[1].K : g.part[0].K);
+    const uint16_t* base;
+    if (kcontig)
+      base = pa + (size_t)m0 * lda + ks;
+    else if (WGRAD)
+      base = (is_a ? pa + m0 : pb + n0) + (size_t)(k0 + ks) * ld;
+    else
+      base = pb + (size_t)e * bes + n0 + (size_t)ks * ldb;
+    const char* cbase = reinterpret_cast<const char*>(base);
+    if (inside && ks + kGK <= klim) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int piece = lt + 128 * j, r = piece >> 3, q = piece & 7;
-        const int k = ks + 8 * q;
-        const bool ok = r < m_lim && k < pk;
-        const uint16_t* src = pa + (size_t)(m0 + (ok ? r : 0)) * lda + (ok ? k : 0);
-        stg[j] = ok ? *reinterpret_cast<const u32x4*>(src) : zero;
-      }
+      for (int j = 0; j < 8; ++j)
+        stg[j] = *reinterpret_cast<const u32x4*>(cbase + j * jstride + voff);
     } else {
-      const int kb = lt >> 4, cb = lt & 15;
-      const int col = 8 * cb;
-      const int klim = WGRAD ? k_lim : pk;
-      const int clim = is_a ? m_lim : n_lim;
-      const uint16_t* base;
-      long ld;
-      if (WGRAD) {
-        base = is_a ? pa + (size_t)k0 * lda + m0 : pb + (size_t)k0 * ldb + n0;
-        ld = is_a ? lda : ldb;
-      } else {
-        base = pb + (size_t)e * bes + n0;
-        ld = ldb;
-      }
+      const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int k = ks + 8 * kb + j;
-        const bool ok = k < klim && col < clim;
-        const uint16_t* src = base + (size_t)(ok ? k : 0) * ld + (ok ? col : 0);
-        stg[j] = ok ? *reinterpret_cast<const u32x4*>(src) : zero;
+        long o;
+        int k;
+        if (kcontig) {
+          const int r = min((lt >> 3) + (BT / 8) * j, m_lim - 1);
+          k = ks + 8 * (lt & 7);
+          o = ((long)r * lda + 8 * (lt & 7)) * 2;
+        } else {
+          k = ks + 8 * kb + j;
+          o = ((long)(8 * kb + j) * ld + min(8 * cb, clim - 8)) * 2;
+        }
+        stg[j] = k < klim ? *reinterpret_cast<const u32x4*>(cbase + o) : zero;
       }
     }
   };
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&](int buf, const u32x4 (&stg)[8]) {
     u32x4* dst = is_a ? sA[buf] : sB[buf];
     if (kcontig) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int piece = lt + 128 * j;
+        const int piece = lt + BT * j;
         dst[gpiece(piece >> 3, piece & 7)] = stg[j];
       }
     } else {
-      const int kb = lt >> 4, cb = lt & 15;
       u32x4 tr[8];
       transpose8x8(stg, tr);
 #pragma unroll
@@ -194,51 +219,75 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_bwd_kernel(GemmArgs g) {
     }
   };
 
-  // ---- fragments: wave (wm, wn) owns rows wm*64.. of A and wn*64.. of B
-  const int wm = wave >> 1, wn = wave & 1;
+  // ---- fragments: wave (wm, wn) owns rows wm*BT/2.. of A and wn*64.. of B
+  const int wm = wave / WN, wn = wave % WN;
   const int lk = lane >> 5;
-  f32x16 acc[2][2];
+  f32x16 acc[FM][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  if (S > 0) {
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-  }
-  for (int s = 0; s < S; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < S) load_stage(s + 1);
+  auto compute = [&](int buf) {
     const u32x4* a_l = sA[buf];
     const u32x4* b_l = sB[buf];
 #pragma unroll
     for (int sl = 0; sl < kGK / 16; ++sl) {
       const int q = 2 * sl + lk;
-      bf16x8 fa[2], fb[2];
+      bf16x8 fa[FM], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = as_bf16x8(a_l[gpiece(wm * 64 + 32 * i + (lane & 31), q)]);
+      for (int i = 0; i < FM; ++i)
+        fa[i] = as_bf16x8(a_l[gpiece(wm * (BT / 2) + 32 * i + (lane & 31), q)]);
 #pragma unroll
       for (int j = 0; j < 2; ++j) fb[j] = as_bf16x8(b_l[gpiece(wn * 64 + 32 * j + (lane & 31), q)]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
-    if (s + 1 < S) store_stage(buf ^ 1);
+  };
+  // Step s: `nxt` holds stage s + 1 (its loads in flight), `cur` is free
+  // (its stage is in LDS).  Stage s + 2 is loaded into `cur`, stage s
+  // computed from LDS, stage s + 1 written to the other LDS buffer (the wait
+  // for its loads leaves stage s + 2's in flight), then one barrier.
+  auto step = [&](int s, u32x4 (&cur)[8], u32x4 (&nxt)[8]) {
+    if (s + 2 < S) load_stage(s + 2, cur);
+    compute(s & 1);
+    if (s + 1 < S) store_stage((s + 1) & 1, nxt);
+    __syncthreads();
+  };
+  // One stage ahead only for the 256-wide tile: a second staging set would
+  // not fit its register budget (it spills).
+  auto step1 = [&](int s) {
+    if (s + 1 < S) load_stage(s + 1, stgA);
+    compute(s & 1);
+    if (s + 1 < S) store_stage((s + 1) & 1, stgA);
+    __syncthreads();
+  };
+  if (S > 0) {
+    load_stage(0, stgA);
+    if (BT == 128 && S > 1) load_stage(1, stgB);
+    store_stage(0, stgA);
     __syncthreads();
   }
+  if (BT == 128) {
+    for (int s = 0; s < S; s += 2) {
+      step(s, stgA, stgB);
+      if (s + 1 < S) step(s + 1, stgB, stgA);
+    }
+  } else {
+    for (int s = 0; s < S; ++s) step1(s);
+  }
 
-  // ---- epilogue: acc[i][j][4 gq + r] = C[m = wm*64 + 32 i + (lane & 31)]
+  // ---- epilogue: acc[i][j][4 gq + r] = C[m = wm*BT/2 + 32 i + (lane & 31)]
   // [n = wn*64 + 32 j + 8 gq + 4 lk + r]: four consecutive n, one 8-byte store.
   uint16_t* cbase = g.c + (WGRAD ? (size_t)e * g.c_estride : 0);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = wm * 64 + 32 * i + (lane & 31);
+  for (int i = 0; i < FM; ++i) {
+    const int m = wm * (BT / 2) + 32 * i + (lane & 31);
     if (m >= m_lim) continue;
     uint16_t* crow = cbase + (size_t)(m0 + m) * g.ldc + n0;
 #pragma unroll
@@ -257,8 +306,14 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_bwd_kernel(GemmArgs g) {
 
 // dgrad: C[rows, N] = A[rows, K] B_e[K, N] (+ the second part), by expert
 // row segments.  Every K, N and leading dimension is a multiple of 8.
+// wgrad: 256-wide tiles when they still give every CU a tile, else 128-wide.
+constexpr int kCUs = 256;
+
 static hipError_t launch_dgrad(const GemmPart* parts, int nparts, const int32_t* offs, int E,
                                int rows, int N, uint16_t* c, long ldc, hipStream_t st) {
+  if (nparts == 2 && (parts[1].lda != parts[0].lda || parts[1].ldb != parts[0].ldb ||
+                      parts[1].b_estride != parts[0].b_estride))
+    return hipErrorInvalidValue;  // the kernel reads these from the first part
   GemmArgs g{};
   for (int p = 0; p < nparts; ++p) g.part[p] = parts[p];
   g.nparts = nparts;
@@ -268,11 +323,12 @@ static hipError_t launch_dgrad(const GemmPart* parts, int nparts, const int32_t*
   g.E = E;
   g.rows = rows;
   g.N = N;
-  g.n_tiles = div_up(N, kGT);
   g.band = 8;
-  const long total = (long)g.n_tiles * worst_row_tiles(rows, E, kGT);
-  const int blocks = (int)((total + 7) / 8 * 8);
-  grouped_gemm_bwd_kernel<false><<<blocks, 256, 0, st>>>(g);
+  // 128-wide tiles: the 256-wide dgrad tile measured no faster (and does not
+  // fit its registers without spilling)
+  g.n_tiles = div_up(N, 128);
+  const long total = (long)g.n_tiles * worst_row_tiles(rows, E, 128);
+  grouped_gemm_bwd_kernel<false, 128><<<(int)((total + 7) / 8 * 8), 256, 0, st>>>(g);
   return hipGetLastError();
 }
 
@@ -295,10 +351,17 @@ static hipError_t launch_wgrad(const uint16_t* a, long lda, const uint16_t* b, l
   g.rows = rows;
   g.M = M;
   g.N = N;
-  g.m_tiles = div_up(M, kGT);
-  g.n_tiles = div_up(N, kGT);
-  const long blocks = (long)E * g.m_tiles * g.n_tiles;
-  grouped_gemm_bwd_kernel<true><<<(int)blocks, 256, 0, st>>>(g);
+  if ((long)E * div_up(M, 256) * div_up(N, 256) >= kCUs) {
+    g.m_tiles = div_up(M, 256);
+    g.n_tiles = div_up(N, 256);
+    const long blocks = (long)E * g.m_tiles * g.n_tiles;
+    grouped_gemm_bwd_kernel<true, 256><<<(int)blocks, 512, 0, st>>>(g);
+  } else {
+    g.m_tiles = div_up(M, 128);
+    g.n_tiles = div_up(N, 128);
+    const long blocks = (long)E * g.m_tiles * g.n_tiles;
+    grouped_gemm_bwd_kernel<true, 128><<<(int)blocks, 256, 0, st>>>(g);
+  }
   return hipGetLastError();
 }
 
