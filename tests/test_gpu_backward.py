@@ -212,3 +212,93 @@ def test_backward_on_saved_preactivations(key, gather):
         if not (en <= TOL_NORM and ee <= TOL_ELEM):
             bad[gname] = (en, ee)
     assert not bad, bad
+
+
+def test_backward_full_size_sampled():
+    """T1024-d4096-E8-top2-f11008 in the benchmark's configuration (training
+    forward with the packed weights, saved pre-activations): two experts'
+    whole row segments (every dx_perm row and the full dWg, dWu, dWd of each)
+    and a sample of tokens (d_topk_w, dz, dz Wr, dx) against the oracle, on the
+    GPU's routing (itself checked against the oracle's decision on the same
+    fp32 logits)."""
+    shape = C.CONFIGS[1]
+    log(f"[backward] full {shape.name}: inputs")
+    inp = I.make_inputs(shape, seed=2)
+    dout_bits = I.make_grad_out(shape, 2)
+    dev, buf = upload(inp), alloc(shape)
+    cfg = B.config(shape)
+    T, d, E, k, f = shape.T, shape.d, shape.E, shape.k, shape.f
+    log("  forward")
+    B.moe_route(cfg, dev["x"], dev["w_router"], dev["bias"], buf["logits"], buf["topk_idx"],
+                buf["topk_w"], B.workspace(cfg, "route"))
+    B.moe_permute(cfg, dev["x"], buf["topk_idx"], buf["expert_offsets"], buf["rank_offsets"],
+                  buf["slot_of"], buf["src_of"], buf["x_perm"], B.workspace(cfg, "permute"))
+    pgu, pd = B.pack_weights(cfg, dev["w_gate"], dev["w_up"], dev["w_down"])
+    a = torch.empty((T * k, f), dtype=torch.bfloat16, device="cuda")
+    u = torch.empty_like(a)
+    B.moe_ffn_gate_up_packed_train(cfg, buf["x_perm"], None, buf["expert_offsets"], pgu,
+                                   buf["h"], a, u)
+    B.moe_ffn_down_packed(cfg, buf["h"], buf["expert_offsets"], pd, buf["y_perm"])
+    B.moe_combine(cfg, buf["y_perm"], buf["slot_of"], buf["topk_w"], buf["out"])
+    del pgu, pd
+    log("  backward")
+    g = _backward(shape, dev, buf, B.to_device(dout_bits), a=a, u=u)
+    del a, u
+    idx, w = host(buf["topk_idx"]), host(buf["topk_w"]).astype(np.float64)
+    logits = host(buf["logits"])
+    offs, src, slot = host(buf["expert_offsets"]), host(buf["src_of"]), host(buf["slot_of"])
+    kw = routing_kwargs(shape)
+    o_idx, o_w, s = om.route(logits, inp["bias"], **kw)
+    assert np.array_equal(idx, o_idx)
+    dout = om.widen_bf16(dout_bits)
+    errs = {}
+
+    def check(name, got, want, group):
+        en, ee = norm_err(got, want, group), rel_err(got, want)
+        errs[name] = (en, ee)
+        return en <= TOL_NORM and ee <= TOL_ELEM
+
+    ok = True
+    counts = np.diff(offs)
+    for e in (int(np.argmax(counts)), int(np.argmin(counts))):
+        r0, r1 = int(offs[e]), int(offs[e + 1])
+        if r1 == r0:
+            continue
+        log(f"  oracle expert {e}: {r1 - r0} rows")
+        t_p, j_p = src[r0:r1] // k, src[r0:r1] % k
+        dY = dout[t_p] * w[t_p, j_p][:, None]
+        dX, dWg, dWu, dWd, _ = om.expert_ffn_backward(inp["x"][t_p], inp["w_gate"][e],
+                                                      inp["w_up"][e], inp["w_down"][e], dY)
+        ok &= check(f"d_y_perm[e{e}]", host(g["d_y_perm"])[r0:r1], dY, "row")
+        ok &= check(f"d_x_perm[e{e}]", host(g["d_x_perm"])[r0:r1], dX, "row")
+        ok &= check(f"d_w_gate[e{e}]", host(g["d_w_gate"])[e], dWg, "all")
+        ok &= check(f"d_w_up[e{e}]", host(g["d_w_up"])[e], dWu, "all")
+        ok &= check(f"d_w_down[e{e}]", host(g["d_w_down"])[e], dWd, "all")
+    # sampled tokens, one expert row at a time
+    rng = np.random.default_rng(3)
+    tokens = np.sort(rng.choice(T, size=12, replace=False))
+    log(f"  oracle tokens {tokens.tolist()}")
+    dg = np.zeros((tokens.size, k))
+    dx = np.zeros((tokens.size, d))
+    need = {}
+    for r, t in enumerate(tokens):
+        for j in range(k):
+            need.setdefault(int(idx[t, j]), []).append((r, int(t), j))
+    for e, items in need.items():  # the sampled rows of one expert at a time
+        ts = np.array([t for _, t, _ in items])
+        gw = np.array([w[t, j] for _, t, j in items])[:, None]
+        wg_e, wu_e, wd_e = inp["w_gate"][e], inp["w_up"][e], inp["w_down"][e]
+        y, _ = om.expert_ffn(inp["x"][ts], wg_e, wu_e, wd_e)
+        dXr, _, _, _, _ = om.expert_ffn_backward(inp["x"][ts], wg_e, wu_e, wd_e, dout[ts] * gw)
+        for n, (r, t, j) in enumerate(items):
+            dg[r, j] = float(np.dot(dout[t], y[n]))
+            dx[r] += dXr[n]
+    sel = om.select(s[tokens], k, shape.n_group, shape.topk_group, shape.presel)
+    dz = om.gates_backward(s[tokens], sel, dg, k, shape.presel, shape.renorm)
+    dxr = dz @ om.widen_bf16(inp["w_router"])
+    ok &= check("d_topk_w[sample]", host(g["d_topk_w"])[tokens], dg, "all")
+    ok &= check("d_logits[sample]", host(g["d_logits"])[tokens], dz, "all")
+    ok &= check("d_x_router[sample]", host(g["d_x_router"])[tokens], dxr, "all")
+    ok &= check("d_x[sample]", host(g["d_x"])[tokens], dx + dxr, "row")
+    log("  norm/elem errors: " + " ".join(f"{n}={a:.1e}/{b:.1e}" for n, (a, b) in errs.items()))
+    assert ok, {n: v for n, v in errs.items() if not (v[0] <= TOL_NORM and v[1] <= TOL_ELEM)}
