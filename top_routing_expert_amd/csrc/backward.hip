@@ -33,7 +33,7 @@
 //    block per CU) where there are enough of them to fill the chip: its
 //    operands are re-read from L2 once per tile, so that halves the traffic.
 //    64-wide k stages double-buffered in LDS; the global loads run two stages
-//    ahead (128) or one (256: a second staging set would not fit).
+//    ahead (dgrad) or one (wgrad: a second staging set would not fit).
 //  * Tiles with rows or k past the end read zeros, so no product has a ragged
 //    special case; an expert without rows gets zero weight gradients.
 #include <cmath>
@@ -249,37 +249,57 @@ __global__ __launch_bounds__(BT / 2 * 4, BT == 128 ? 2 : 1) void grouped_gemm_bw
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
   };
-  // Step s: `nxt` holds stage s + 1 (its loads in flight), `cur` is free
-  // (its stage is in LDS).  Stage s + 2 is loaded into `cur`, stage s
-  // computed from LDS, stage s + 1 written to the other LDS buffer (the wait
-  // for its loads leaves stage s + 2's in flight), then one barrier.
-  auto step = [&](int s, u32x4 (&cur)[8], u32x4 (&nxt)[8]) {
-    if (s + 2 < S) load_stage(s + 2, cur);
-    compute(s & 1);
-    if (s + 1 < S) store_stage((s + 1) & 1, nxt);
-    __syncthreads();
-  };
-  // One stage ahead only for the 256-wide tile: a second staging set would
-  // not fit its register budget (it spills).
+  // One stage ahead for the wgrad and the 256-wide tile: a second staging set
+  // would not fit their register budget (they spill).
+  constexpr bool kDeep = !WGRAD && BT == 128;
   auto step1 = [&](int s) {
     if (s + 1 < S) load_stage(s + 1, stgA);
     compute(s & 1);
     if (s + 1 < S) store_stage((s + 1) & 1, stgA);
     __syncthreads();
   };
-  if (S > 0) {
+  if (!kDeep) {
+    if (S > 0) {
+      load_stage(0, stgA);
+      store_stage(0, stgA);
+      __syncthreads();
+    }
+    for (int s = 0; s < S; ++s) step1(s);
+  } else if (S > 0) {
+    // Two stages ahead with fixed roles, so that no staging register is ever
+    // copied (a copy would wait for the loads in flight).  At the top of each
+    // iteration stage s is in LDS buffer s & 1, stgB holds stage s + 1 (loads
+    // in flight) and stgA is free.  Step s loads stage s + 2 into stgA and
+    // writes stgB to the other buffer; step s + 1 loads stage s + 3 into stgB
+    // and writes stgA.  Each step ends with one barrier.
     load_stage(0, stgA);
-    if (BT == 128 && S > 1) load_stage(1, stgB);
+    if (S > 1) load_stage(1, stgB);
     store_stage(0, stgA);
     __syncthreads();
-  }
-  if (BT == 128) {
-    for (int s = 0; s < S; s += 2) {
-      step(s, stgA, stgB);
-      if (s + 1 < S) step(s + 1, stgB, stgA);
+    int s = 0;
+    for (; s + 3 < S; s += 2) {
+      load_stage(s + 2, stgA);
+      compute(s & 1);
+      store_stage((s + 1) & 1, stgB);
+      __syncthreads();
+      load_stage(s + 3, stgB);
+      compute((s + 1) & 1);
+      store_stage(s & 1, stgA);
+      __syncthreads();
     }
-  } else {
-    for (int s = 0; s < S; ++s) step1(s);
+    // the last one to three steps, same roles
+    if (s + 2 < S) load_stage(s + 2, stgA);
+    compute(s & 1);
+    if (s + 1 < S) {
+      store_stage((s + 1) & 1, stgB);
+      __syncthreads();
+      compute((s + 1) & 1);
+      if (s + 2 < S) {
+        store_stage(s & 1, stgA);
+        __syncthreads();
+        compute(s & 1);
+      }
+    }
   }
 
   // ---- epilogue: acc[i][j][4 gq + r] = C[m = wm*BT/2 + 32 i + (lane & 31)]
