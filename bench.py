@@ -326,11 +326,18 @@ def main():
             cfg, grad["dxp"], buf["slot"], grad["dxr"], grad["dx"], stream)
         phases_run = phases_run + ("combine_bwd", "ffn_bwd", "route_bwd", "unpermute_bwd")
 
-    def step(ev=None):
+    def step(ev=None, dom_ev=None):
+        """One pass of the path.  ev: an event after every phase (the phase
+        breakdown); dom_ev: one pair around the dominant kernel only (the
+        timed steps: six markers per step cost ~3 % of the T1024 step)."""
         if ev is not None:
             ev[0].record(stream)
         for i, p in enumerate(phases_run):
+            if dom_ev is not None and p == DOMINANT:
+                dom_ev[0].record(stream)
             calls[p]()
+            if dom_ev is not None and p == DOMINANT:
+                dom_ev[1].record(stream)
             if ev is not None:
                 ev[i + 1].record(stream)
 
@@ -339,17 +346,24 @@ def main():
         step()
     torch.cuda.synchronize()
     counts = np.diff(B.to_host_bits(buf["offs"]).astype(np.int64))
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases_run) + 1)]
-              for _ in range(a.steps)]
+    dom_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(a.steps)]
     log(f"timing {a.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(a.steps):
-        step(events[s])
+        step(dom_ev=dom_events[s])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    dom_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in dom_events]))
+    # phase breakdown: the same steps again, untimed, with an event after every phase
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases_run) + 1)]
+              for _ in range(a.steps)]
+    for s in range(a.steps):
+        step(ev=events[s])
+    torch.cuda.synchronize()
     phase_ms = {p: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
                                   for s in range(a.steps)])) for i, p in enumerate(phases_run)}
+    phase_ms[DOMINANT] = dom_ms  # the dominant kernel as timed inside the timed region
     ms_per_step = elapsed * 1e3 / a.steps
     work = algorithmic(shape, counts, gather)
     if a.backward and a.ffn == "packed":  # the saved pre-activations, written by the forward
@@ -362,7 +376,9 @@ def main():
     traffic = measured_traffic(a.ffn, shape.name, a.dispatch)
     roofline = {"bound": dom["bound"], "achieved": round(dom["achieved"], 3),
                 "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4),
-                "traffic": traffic, "kernel": FFN_KERNELS[a.ffn][2],
+                "traffic": traffic,
+                "kernel": FFN_KERNELS[a.ffn][2].replace(
+                    ")", "_gather)" if gather else ("_train)" if a.backward and a.ffn == "packed" else ")")),
                 "algorithmic_bytes": work[DOMINANT]["bytes"],
                 "algorithmic_flops": work[DOMINANT]["flops"],
                 "avg_launch_ms": round(dom["ms"], 5)}
