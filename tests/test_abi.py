@@ -141,3 +141,49 @@ def test_workspace_sizes():
     assert B.workspace_bytes(B.config(C.E8_D4096, T=0), "permute") == 0
     with pytest.raises(B.MoEError):
         B.workspace_bytes(B.config(C.E8_D4096, k=0), "layer")
+
+
+def test_backward_entries_reject_before_launch():
+    """Every backward entry point checks its arguments on the host and
+    returns before anything reaches a GPU (so these run without one)."""
+    L = B.lib()
+    fake = 1 << 40  # 16-byte aligned, never dereferenced
+    cfg = B.config(C.E8_D4096)
+    f32 = B.config(C.TINY_F32)
+    bf = ctypes.byref
+    # combine backward
+    assert L.moe_combine_backward(bf(f32), fake, fake, fake, fake, fake, fake,
+                                  None) == B.MOE_EUNSUPPORTED
+    assert L.moe_combine_backward(bf(cfg), None, fake, fake, fake, fake, fake,
+                                  None) == B.MOE_EINVAL
+    assert L.moe_combine_backward(bf(cfg), fake + 2, fake, fake, fake, fake, fake,
+                                  None) == B.MOE_EINVAL  # misaligned rows
+    # FFN backward
+    need = B.workspace_bytes(cfg, "ffn_backward")
+    A, f = C.E8_D4096.T * C.E8_D4096.k, C.E8_D4096.f
+    assert need >= 4 * A * f * 2
+    args = [fake, fake, fake, fake, fake]  # x_perm, offsets, w_gate, w_up, w_down
+    outs = [fake, fake, fake, fake, fake]  # d_y_perm, d_x_perm, d_w_gate, d_w_up, d_w_down
+    assert L.moe_ffn_backward(bf(f32), *args, None, None, *outs, fake, 1 << 34,
+                              None) == B.MOE_EUNSUPPORTED
+    assert L.moe_ffn_backward(bf(cfg), *args, fake, None, *outs, fake, need,
+                              None) == B.MOE_EINVAL  # a without u
+    assert L.moe_ffn_backward(bf(cfg), *args, None, None, *outs, fake, need - 1,
+                              None) == B.MOE_EINVAL  # workspace too small
+    assert L.moe_ffn_backward(bf(cfg), *args, None, None, *outs, fake + 16, need,
+                              None) == B.MOE_EINVAL  # workspace not 256-byte aligned
+    # router backward
+    rneed = B.workspace_bytes(cfg, "route_backward")
+    assert rneed > 0
+    rargs = [fake] * 6 + [fake, fake, fake, None]  # ... d_logits, d_x_router, d_w_router, d_bias
+    assert L.moe_route_backward(bf(B.config(C.E8_D4096, E=12)), *rargs, fake, 1 << 34,
+                                None) == B.MOE_EUNSUPPORTED  # E % 8 != 0
+    grouped_presel = B.config(C.E8_D4096, E=16, presel=4, renorm=0, n_group=4, topk_group=2)
+    assert L.moe_validate(bf(grouped_presel)) == B.MOE_OK
+    assert L.moe_route_backward(bf(grouped_presel), *rargs, fake, 1 << 34,
+                                None) == B.MOE_EUNSUPPORTED
+    assert L.moe_route_backward(bf(cfg), *rargs, fake, rneed - 1, None) == B.MOE_EINVAL
+    # dispatch backward and the training forward
+    assert L.moe_unpermute_backward(bf(cfg), fake, fake, fake + 4, fake, None) == B.MOE_EINVAL
+    assert L.moe_ffn_gate_up_packed_train(bf(cfg), fake, None, fake, fake, fake, None, fake,
+                                          None) == B.MOE_EINVAL  # a missing
