@@ -324,6 +324,230 @@ __global__ __launch_bounds__(BT / 2 * 4, BT == 128 ? 2 : 1) void grouped_gemm_bw
   }
 }
 
+// ---------------------------------------------------------------- wgrad, LDS-DMA
+// C_e[M, N] = sum over the expert's rows r of A[r, m] B[r, n].  Both operands
+// have k (the row index) as their slow index, so they go to LDS as they are
+// laid out in memory -- by the gfx950 LDS-DMA load, no staging registers --
+// and the MFMA fragments are read transposed with ds_read_b64_tr_b16: within
+// each 16-lane group, lane c receives element c % 4 of the 8-byte pieces
+// addressed by lanes 4 q + c / 4 (q = 0..3), so when lane 4 q + j addresses
+// k-row k0 + q, columns c0 + 4 j .. + 3, lane c gets column c0 + c at the four
+// k-rows k0 .. k0 + 3.  Two such reads give an MFMA lane its 8 consecutive k.
+// 128 x 128 tiles, four waves of 64 x 64, 32-row k stages in a ring of four
+// (64 KB, two blocks per CU), explicit waits.  k-rows past the expert's end are
+// copied from a page of zeros; columns past M or N are clamped inside the
+// row (they only feed outputs that are never stored).
+typedef __attribute__((address_space(3))) void bw_lds_t;
+typedef short bw_v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __attribute__((aligned(16))) const uint32_t kBwZeroPage[4] = {0u, 0u, 0u, 0u};
+
+__device__ __forceinline__ uint32_t bw_lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const bw_lds_t*)p;
+}
+// 16 bytes per lane, global -> LDS; lane L writes LDS bytes [lds + 16 L, + 16).
+__device__ __forceinline__ void bw_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void bw_wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+constexpr int kWK = 32;                      // k-rows per stage
+constexpr int kWRing = 4;                    // stages in the LDS ring
+constexpr int kWDpw = 4;                     // DMA instructions (1 KB) per wave per stage
+
+// byte offset of 16-byte column piece p of k-row r in one operand's stage
+// (2 WT bytes per k-row; pieces XOR-swizzled with (r & 3) << 2 so that a
+// transposed read's four k-rows land on different banks)
+template <int WT>
+__device__ __forceinline__ uint32_t wg_piece(int r, int p) {
+  return (uint32_t)(r * (2 * WT) + ((p ^ ((r & 3) << 2)) << 4));
+}
+
+// WT = 128: four waves of 64 x 64, 64 KB ring, two blocks per CU, the next
+// stage's fragments read while the current one's MFMAs run.  WT = 256: eight
+// waves of 128 x 64, 128 KB ring, one block per CU, half the operand bytes
+// per flop; one fragment set (two would not fit its registers).
+template <int WT>
+__global__ __launch_bounds__(WT * 2, WT == 128 ? 2 : 1) void wgrad_dma_kernel(
+    const uint16_t* __restrict__ a, long lda, const uint16_t* __restrict__ b, long ldb,
+    const int32_t* __restrict__ offs, int E, int rows, int M, int N, int m_tiles, int n_tiles,
+    uint16_t* __restrict__ c, long ldc, long c_estride) {
+  constexpr int NW = WT / 32;                  // waves (4 or 8)
+  constexpr int WN = NW / 2;                   // waves along N; two along M
+  constexpr int FM = WT / 64;                  // 32-column A fragments per wave
+  constexpr int OPB = kWK * WT * 2;            // one operand's stage
+  constexpr int STB = 2 * OPB;                 // one stage
+  constexpr int CPO = OPB / 1024;              // 1 KB chunks per operand
+  constexpr int RPC = 1024 / (2 * WT);         // k-rows per chunk
+  constexpr bool kPrefetch = WT == 128;
+  static_assert(2 * CPO == NW * kWDpw, "chunks per stage");
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kWRing * STB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int per_e = m_tiles * n_tiles;
+  const int e = blockIdx.x / per_e;
+  const int rr = blockIdx.x - e * per_e;
+  const int m0 = (rr / n_tiles) * WT, n0 = (rr % n_tiles) * WT;
+  const int m_lim = min(WT, M - m0), n_lim = min(WT, N - n0);
+  const int k0 = min(max(offs[e], 0), rows);
+  const int k_lim = min(max(offs[e + 1], k0), rows) - k0;
+  const int nk = (k_lim + kWK - 1) / kWK;
+
+  // ---- DMA: stage chunk q (1 KB) = operand q / CPO, k-rows RPC (q % CPO) ..;
+  // wave w issues chunks w + NW i.  Lane L lands at k-row RPC (q % CPO) +
+  // L / (WT / 8), physical piece L % (WT / 8), so it fetches logical piece
+  // (L % (WT / 8)) ^ ((row & 3) << 2).
+  int drow[kWDpw];
+  const uint16_t* dcol[kWDpw];
+  long dld[kWDpw];
+#pragma unroll
+  for (int i = 0; i < kWDpw; ++i) {
+    const int q = wave + NW * i;
+    const bool is_a = q < CPO;
+    const int r = RPC * (q % CPO) + lane / (WT / 8);
+    const int p = (lane % (WT / 8)) ^ ((r & 3) << 2);
+    const int lim = is_a ? m_lim : n_lim;  // a multiple of 8
+    const int col = min(8 * p, lim - 8);
+    drow[i] = r;
+    dcol[i] = is_a ? a + (size_t)k0 * lda + m0 + col : b + (size_t)k0 * ldb + n0 + col;
+    dld[i] = is_a ? lda : ldb;
+  }
+  const uint32_t lds0 = bw_lds_addr(ring);
+  auto issue = [&](int kt) {
+    const uint32_t sbase = lds0 + (uint32_t)(kt % kWRing) * STB;
+#pragma unroll
+    for (int i = 0; i < kWDpw; ++i) {
+      const int k = kt * kWK + drow[i];
+      const void* src = k < k_lim ? (const void*)(dcol[i] + (size_t)k * dld[i])
+                                  : (const void*)kBwZeroPage;
+      bw_dma16(src, sbase + (uint32_t)(wave + NW * i) * 1024u);
+    }
+  };
+
+  // ---- fragments: wave (wm, wn) owns A columns wm*WT/2.. and B columns wn*64..
+  const int wm = wave / WN, wn = wave % WN;
+  const int g = lane >> 4;
+  const int tr_col = 16 * (g & 1) + 4 * (lane & 3);  // column of the addressed piece
+  const int tr_row = 8 * (g >> 1) + ((lane >> 2) & 3);
+  struct Frags {
+    bf16x8 a[2][FM];  // [k slab][fragment]
+    bf16x8 b[2][2];
+  };
+  auto read_frag = [&](uint32_t opbase, int col0, int s2) -> bf16x8 {
+    const int col = col0 + tr_col;
+    bw_v4i16 h[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int r = 16 * s2 + tr_row + 4 * hh;
+      const uint32_t addr = opbase + wg_piece<WT>(r, col >> 3) + (uint32_t)((col & 7) * 2);
+      h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) bw_v4i16*)(size_t)addr);
+    }
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
+  auto load_frags = [&](int kt, Frags& F) {
+    const uint32_t sb = lds0 + (uint32_t)(kt % kWRing) * STB;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) F.a[s2][i] = read_frag(sb, wm * (WT / 2) + 32 * i, s2);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) F.b[s2][j] = read_frag(sb + OPB, wn * 64 + 32 * j, s2);
+    }
+  };
+  f32x16 acc[FM][2];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  auto mfma_stage = [&](const Frags& F) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.b[s2][j], F.a[s2][i], acc[i][j],
+                                                              0, 0, 0);
+  };
+  // Stage j lives in ring slot j % 4.  With prefetch, stage kt's fragments are
+  // read during step kt - 1; without, at the start of step kt.  End of step
+  // kt: wait for this wave's copies of stage kt + 2 (kt + 1 without
+  // prefetch), barrier (that stage visible; slot kt % 4 no longer read),
+  // refill slot kt % 4 with stage kt + 4.
+  constexpr int AHEAD = kPrefetch ? 2 : 1;
+  if (nk > 0) {
+#pragma unroll
+    for (int i = 0; i < kWRing; ++i)
+      if (i < nk) issue(i);
+    {  // stages 0 .. AHEAD - 1 visible, the later ones may still fly
+      const int later = min(nk - 1, kWRing - 1) - (AHEAD - 1);
+      if (later <= 0) bw_wait_vm_barrier<0>();
+      else if (later == 1) bw_wait_vm_barrier<kWDpw>();
+      else if (later == 2) bw_wait_vm_barrier<2 * kWDpw>();
+      else bw_wait_vm_barrier<3 * kWDpw>();
+    }
+    auto finish = [&](int kt) {
+      const int j = kt + AHEAD;  // the stage that must be visible next
+      const int later = j < nk ? min(nk - 1, kt + kWRing - 1) - j : 0;
+      if (later <= 0) bw_wait_vm_barrier<0>();
+      else if (later == 1) bw_wait_vm_barrier<kWDpw>();
+      else bw_wait_vm_barrier<2 * kWDpw>();
+      if (kt + kWRing < nk) issue(kt + kWRing);
+    };
+    if constexpr (kPrefetch) {
+      Frags F0, F1;
+      load_frags(0, F0);
+      auto step = [&](int kt, Frags& cur, Frags& nxt) {
+        load_frags(min(kt + 1, nk - 1), nxt);  // the last step re-reads the final stage
+        mfma_stage(cur);
+        finish(kt);
+      };
+      for (int kt = 0; kt < nk; kt += 2) {
+        step(kt, F0, F1);
+        if (kt + 1 < nk) step(kt + 1, F1, F0);
+      }
+    } else {
+      for (int kt = 0; kt < nk; ++kt) {
+        Frags F;
+        load_frags(kt, F);
+        mfma_stage(F);
+        finish(kt);
+      }
+    }
+  }
+
+  // ---- epilogue: acc[i][j][4 gq + r] = C[m = wm*WT/2 + 32 i + (lane & 31)]
+  // [n = wn*64 + 32 j + 8 gq + 4 (lane >> 5) + r]
+  uint16_t* cbase = c + (size_t)e * c_estride;
+  const int lk = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int m = wm * (WT / 2) + 32 * i + (lane & 31);
+    if (m >= m_lim) continue;
+    uint16_t* crow = cbase + (size_t)(m0 + m) * ldc + n0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int n = wn * 64 + 32 * j + 8 * gq + 4 * lk;
+        if (n >= n_lim) continue;
+        u32x2 pk;
+        pk.x = pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]);
+        pk.y = pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
+        *reinterpret_cast<u32x2*>(crow + n) = pk;
+      }
+  }
+}
+
 // dgrad: C[rows, N] = A[rows, K] B_e[K, N] (+ the second part), by expert
 // row segments.  Every K, N and leading dimension is a multiple of 8.
 // wgrad: 256-wide tiles when they still give every CU a tile, else 128-wide.
@@ -357,30 +581,17 @@ static hipError_t launch_dgrad(const GemmPart* parts, int nparts, const int32_t*
 static hipError_t launch_wgrad(const uint16_t* a, long lda, const uint16_t* b, long ldb,
                                const int32_t* offs, int E, int rows, int M, int N, uint16_t* c,
                                long ldc, long c_estride, hipStream_t st) {
-  GemmArgs g{};
-  g.part[0].a = a;
-  g.part[0].b = b;
-  g.part[0].lda = lda;
-  g.part[0].ldb = ldb;
-  g.nparts = 1;
-  g.c = c;
-  g.ldc = ldc;
-  g.c_estride = c_estride;
-  g.offs = offs;
-  g.E = E;
-  g.rows = rows;
-  g.M = M;
-  g.N = N;
-  if ((long)E * div_up(M, 256) * div_up(N, 256) >= kCUs) {
-    g.m_tiles = div_up(M, 256);
-    g.n_tiles = div_up(N, 256);
-    const long blocks = (long)E * g.m_tiles * g.n_tiles;
-    grouped_gemm_bwd_kernel<true, 256><<<(int)blocks, 512, 0, st>>>(g);
+  // 256-wide tiles for long reductions (measured: faster from ~2048 rows per
+  // expert, slower at ~256, where the 128-wide tile's two blocks per CU hide
+  // each tile's start and end) when they still give every CU one
+  if (rows >= 1024L * E && (long)E * div_up(M, 256) * div_up(N, 256) >= kCUs) {
+    const int mt = div_up(M, 256), nt = div_up(N, 256);
+    wgrad_dma_kernel<256><<<(int)((long)E * mt * nt), 512, 0, st>>>(
+        a, lda, b, ldb, offs, E, rows, M, N, mt, nt, c, ldc, c_estride);
   } else {
-    g.m_tiles = div_up(M, 128);
-    g.n_tiles = div_up(N, 128);
-    const long blocks = (long)E * g.m_tiles * g.n_tiles;
-    grouped_gemm_bwd_kernel<true, 128><<<(int)blocks, 256, 0, st>>>(g);
+    const int mt = div_up(M, 128), nt = div_up(N, 128);
+    wgrad_dma_kernel<128><<<(int)((long)E * mt * nt), 256, 0, st>>>(
+        a, lda, b, ldb, offs, E, rows, M, N, mt, nt, c, ldc, c_estride);
   }
   return hipGetLastError();
 }
