@@ -235,8 +235,8 @@ def test_fp8_decode_rounds_twice(tmp_path):
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc not available")
 def test_backward_kernels_keep_everything_in_registers(tmp_path):
-    """The backward GEMM holds up to 256 registers per lane; a spill would put
-    scratch traffic into its main loop."""
+    """The backward GEMMs hold up to 256 registers per lane; a spill would put
+    scratch traffic into their main loops."""
     out = tmp_path / "backward.s"
     cmd = [Bld._hipcc(), *Bld.HIPCC_FLAGS, "--cuda-device-only", "-S",
            os.path.join(Bld.CSRC, "backward.hip"), "-o", str(out)]
@@ -244,5 +244,6 @@ def test_backward_kernels_keep_everything_in_registers(tmp_path):
     assert r.returncode == 0, r.stderr[-2000:]
     meta = out.read_text().split("amdhsa.kernels", 1)[1]
     kernels = re.findall(r"\.name:\s+(\S+)[\s\S]*?\.private_segment_fixed_size:\s+(\d+)", meta)
-    assert any("grouped_gemm_bwd" in n for n, _ in kernels)
+    assert any("dgrad_dma_kernel" in n for n, _ in kernels)
+    assert any("wgrad_dma_kernel" in n for n, _ in kernels)
     assert [n for n, ps in kernels if int(ps)] == []

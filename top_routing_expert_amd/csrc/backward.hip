@@ -19,23 +19,22 @@
 //              dWr = dz^T x.
 //
 // gfx950 design
-//  * One MFMA kernel serves every backward product.  dgrad (dh, dx, the
-//    router's dz Wr) runs over the expert row segments like the forward, with
-//    the expert's weights read in their natural [K, N] layout; wgrad (dW) runs
-//    per expert over its row segment as the reduction.  Operands whose k is
-//    not contiguous in memory (the weights in dgrad, both activations in
-//    wgrad) are transposed on their way into LDS: a thread loads an 8 (k) x 8
-//    block with eight 16-byte loads, transposes it in registers (v_perm) and
-//    writes eight 16-byte LDS rows, so the MFMA fragments are 16-byte LDS
-//    reads on both sides.
-//  * Block tiles of 128 x 128 (four waves of 64 x 64, two blocks per CU); the
-//    wgrad also has 256 x 256 (eight waves of 128 x 64, 128 KB of LDS, one
-//    block per CU) where there are enough of them to fill the chip: its
-//    operands are re-read from L2 once per tile, so that halves the traffic.
-//    64-wide k stages double-buffered in LDS; the global loads run two stages
-//    ahead (dgrad) or one (wgrad: a second staging set would not fit).
-//  * Tiles with rows or k past the end read zeros, so no product has a ragged
-//    special case; an expert without rows gets zero weight gradients.
+//  * Two MFMA kernels serve every backward product.  dgrad (dh, dx, the
+//    router's dz Wr) runs over the expert row segments with the forward's
+//    device tile table; wgrad (dW) runs per expert with the expert's row
+//    segment as the reduction (zeros for an expert without rows).
+//  * Both stream their operands into LDS with the gfx950 LDS-DMA load (no
+//    staging registers) through a ring of four 32-k stages with explicit
+//    waits.  Operands whose k is contiguous (dgrad's activation rows) sit in
+//    LDS as 64-byte rows and are read as 16-byte fragments; operands whose k
+//    is the slow index (dgrad's weights, both wgrad operands) are copied as
+//    they lie and read transposed with ds_read_b64_tr_b16.
+//  * 128 x 128 tiles (four waves of 64 x 64, two blocks per CU); the wgrad
+//    also has 256 x 256 (eight waves, one block per CU, half the L2 traffic)
+//    for long reductions.
+//  * Rows and columns past a tile's end are clamped onto data inside the
+//    buffers (they only feed outputs that are never stored); k past the end
+//    of a part or an expert's segment is read from a page of zeros.
 #include <cmath>
 
 #include "common.h"
@@ -43,286 +42,24 @@
 
 namespace moe {
 
-constexpr int kGK = 64;       // k per stage
-constexpr int kGPieces = 8;   // 16-byte pieces per LDS row (64 k)
-
 struct GemmPart {
   const uint16_t* a;
   const uint16_t* b;
   long lda, ldb;   // leading dimensions in elements
-  long b_estride;  // dgrad: elements between two experts' weight matrices
-  int K;           // dgrad: k extent of this part
+  long b_estride;  // elements between two experts' weight matrices
+  int K;           // k extent of this part
 };
 
-struct GemmArgs {
+struct GemmArgs {  // dgrad
   GemmPart part[2];
   int nparts;
   uint16_t* c;
-  long ldc, c_estride;
+  long ldc;
   const int32_t* offs;
   int E, rows;
-  int M, N;  // wgrad: the per-expert output is M x N; dgrad: N only
-  int m_tiles, n_tiles, band;
+  int N;
+  int n_tiles, band;
 };
-
-// 8 x 8 bf16 transpose: in[r] holds row r (8 values, 2 per word); out[c]
-// holds column c.  Word w of out[c] is (in[2w][c], in[2w+1][c]).
-__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
-#pragma unroll
-    for (int w = 0; w < 4; ++w)
-      out[c][w] = __builtin_amdgcn_perm(in[2 * w + 1][c >> 1], in[2 * w][c >> 1], sel);
-  }
-}
-
-// LDS row r (128 bytes, 8 pieces of 16 bytes): logical piece q sits at
-// q ^ (r & 7) ^ ((r >> 3) & 7).  The fragment reads (32 consecutive rows, one
-// piece) and the transposed stores (rows 8 apart, one piece) then both spread
-// over all eight piece slots.
-__device__ __forceinline__ int gpiece(int r, int q) {
-  return r * kGPieces + (q ^ (r & 7) ^ ((r >> 3) & 7));
-}
-
-// WGRAD = false: dgrad.  A (M side) = activation rows [row0, row_end) of the
-// tile's expert, k contiguous; B (N side) = the expert's [K, N] weights.
-// WGRAD = true: wgrad.  The reduction runs over the expert's row segment;
-// A = act_a rows (M contiguous), B = act_b rows (N contiguous).
-// BT: block tile (rows and columns), 128 with four waves of 64 x 64 (two
-// blocks per CU) or 256 with eight waves of 128 x 64 (one block per CU, half
-// the operand bytes per flop).  Half of the threads stage A, half stage B:
-// BT threads each.
-template <bool WGRAD, int BT>
-__global__ __launch_bounds__(BT / 2 * 4, BT == 128 ? 2 : 1) void grouped_gemm_bwd_kernel(
-    GemmArgs g) {
-  constexpr int kGT = BT;
-  constexpr int NTH = 2 * BT;         // threads
-  constexpr int WN = NTH / 64 / 2;    // waves along N (2 or 4); two along M
-  constexpr int FM = BT / 64;         // 32-row fragments per wave along M
-  constexpr int CB = BT / 8;          // 8-column blocks per row of a transposed stage
-  __shared__ u32x4 sA[2][kGT * kGPieces];
-  __shared__ u32x4 sB[2][kGT * kGPieces];
-  __shared__ int s_tile[4];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  int e, m0, m_lim, n0, k0 = 0, k_lim = 0;
-  if (!WGRAD) {
-    if (wave == 0) place_tile<kGT>(g.offs, g.E, g.rows, g.n_tiles, g.band, lane, s_tile);
-    __syncthreads();
-    e = s_tile[0];
-    if (e < 0) return;  // block-uniform
-    m0 = s_tile[1];
-    m_lim = s_tile[2] - s_tile[1];
-    n0 = s_tile[3] * kGT;
-  } else {
-    const int per_e = g.m_tiles * g.n_tiles;
-    e = blockIdx.x / per_e;
-    const int r = blockIdx.x - e * per_e;
-    m0 = (r / g.n_tiles) * kGT;
-    n0 = (r % g.n_tiles) * kGT;
-    m_lim = min(kGT, g.M - m0);
-    const int o0 = min(max(g.offs[e], 0), g.rows);
-    const int o1 = min(max(g.offs[e + 1], o0), g.rows);
-    k0 = o0;
-    k_lim = o1 - o0;
-  }
-  const int n_lim = min(kGT, g.N - n0);
-
-  // stage list: the parts one after the other (scalars: no indexed copies of
-  // the kernel arguments)
-  const int k0_ext = WGRAD ? k_lim : g.part[0].K;
-  const int k1_ext = g.nparts > 1 ? (WGRAD ? k_lim : g.part[1].K) : 0;
-  const int nst0 = (k0_ext + kGK - 1) / kGK;
-  const int nst1 = (k1_ext + kGK - 1) / kGK;
-  const int S = nst0 + nst1;
-
-  // ---- loader.  Waves 0..NW/2-1 stage A, the others B (BT threads each).  A
-  // k-contiguous operand (dgrad A) is 8 BT pieces: thread t takes pieces
-  // t + BT j (row t/8 + (BT/8) j, piece t % 8).  A transposed operand is BT
-  // blocks of 8 k x 8 m/n: thread t takes block t (k block t / CB, column
-  // block t % CB), load j reading k row 8 (t / CB) + j.
-  // Rows and columns past the tile's end only feed outputs that are never
-  // stored, so inside the buffer they are simply read; k past the end of a
-  // part must read zeros (both operands).  A stage is "plain" when its k is
-  // whole and the tile's rows / columns end inside the buffer: then load j is
-  // one per-thread offset plus j times a block-uniform stride (scalar base
-  // per load).  Otherwise (a part's ragged last stage, the buffer's last
-  // tiles) every load is clamped and masked.  The parts of one product share
-  // lda, ldb and the expert stride (checked by the launcher).
-  const bool is_a = wave < NTH / 128;  // wave-uniform, so the bases stay scalar
-  const int lt = tid % BT;
-  const bool kcontig = !WGRAD && is_a;
-  const long lda = g.part[0].lda, ldb = g.part[0].ldb, bes = g.part[0].b_estride;
-  const long ld = (kcontig || (WGRAD && is_a)) ? lda : ldb;
-  const int kb = lt / CB, cb = lt % CB;
-  // per-thread byte offset of load 0 and the uniform byte stride between loads
-  const uint32_t voff = kcontig ? (uint32_t)(((long)(lt >> 3) * lda + 8 * (lt & 7)) * 2)
-                                : (uint32_t)(((long)(8 * kb) * ld + 8 * cb) * 2);
-  const long jstride = kcontig ? (long)(BT / 8) * lda * 2 : ld * 2;
-  // the tile's rows / columns end inside the buffer
-  const bool inside = kcontig ? m0 + BT <= g.rows
-                              : (is_a ? m0 + BT <= g.M : n0 + BT <= g.N);
-  const int clim = is_a ? m_lim : n_lim;  // transposed operands: a multiple of 8
-  u32x4 stgA[8], stgB[8];  // two stages of staging registers: loads run two stages ahead
-
-  auto load_stage = [&](int s, u32x4 (&stg)[8]) {
-    const bool p1 = s >= nst0;
-    const int ks = (s - (p1 ? nst0 : 0)) * kGK;  // k offset inside the part
-    const uint16_t* pa = p1 ? g.part[1].a : g.part[0].a;
-    const uint16_t* pb = p1 ? g.part[1].b : g.part[0].b;
-    const int klim = WGRAD ? k_lim : (p1 ? g.part[1].K : g.part[0].K);
-    const uint16_t* base;
-    if (kcontig)
-      base = pa + (size_t)m0 * lda + ks;
-    else if (WGRAD)
-      base = (is_a ? pa + m0 : pb + n0) + (size_t)(k0 + ks) * ld;
-    else
-      base = pb + (size_t)e * bes + n0 + (size_t)ks * ldb;
-    const char* cbase = reinterpret_cast<const char*>(base);
-    if (inside && ks + kGK <= klim) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        stg[j] = *reinterpret_cast<const u32x4*>(cbase + j * jstride + voff);
-    } else {
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        long o;
-        int k;
-        if (kcontig) {
-          const int r = min((lt >> 3) + (BT / 8) * j, m_lim - 1);
-          k = ks + 8 * (lt & 7);
-          o = ((long)r * lda + 8 * (lt & 7)) * 2;
-        } else {
-          k = ks + 8 * kb + j;
-          o = ((long)(8 * kb + j) * ld + min(8 * cb, clim - 8)) * 2;
-        }
-        stg[j] = k < klim ? *reinterpret_cast<const u32x4*>(cbase + o) : zero;
-      }
-    }
-  };
-  auto store_stage = [&](int buf, const u32x4 (&stg)[8]) {
-    u32x4* dst = is_a ? sA[buf] : sB[buf];
-    if (kcontig) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int piece = lt + BT * j;
-        dst[gpiece(piece >> 3, piece & 7)] = stg[j];
-      }
-    } else {
-      u32x4 tr[8];
-      transpose8x8(stg, tr);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) dst[gpiece(8 * cb + c, kb)] = tr[c];
-    }
-  };
-
-  // ---- fragments: wave (wm, wn) owns rows wm*BT/2.. of A and wn*64.. of B
-  const int wm = wave / WN, wn = wave % WN;
-  const int lk = lane >> 5;
-  f32x16 acc[FM][2];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  auto compute = [&](int buf) {
-    const u32x4* a_l = sA[buf];
-    const u32x4* b_l = sB[buf];
-#pragma unroll
-    for (int sl = 0; sl < kGK / 16; ++sl) {
-      const int q = 2 * sl + lk;
-      bf16x8 fa[FM], fb[2];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        fa[i] = as_bf16x8(a_l[gpiece(wm * (BT / 2) + 32 * i + (lane & 31), q)]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = as_bf16x8(b_l[gpiece(wn * 64 + 32 * j + (lane & 31), q)]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-    }
-  };
-  // One stage ahead for the wgrad and the 256-wide tile: a second staging set
-  // would not fit their register budget (they spill).
-  constexpr bool kDeep = !WGRAD && BT == 128;
-  auto step1 = [&](int s) {
-    if (s + 1 < S) load_stage(s + 1, stgA);
-    compute(s & 1);
-    if (s + 1 < S) store_stage((s + 1) & 1, stgA);
-    __syncthreads();
-  };
-  if (!kDeep) {
-    if (S > 0) {
-      load_stage(0, stgA);
-      store_stage(0, stgA);
-      __syncthreads();
-    }
-    for (int s = 0; s < S; ++s) step1(s);
-  } else if (S > 0) {
-    // Two stages ahead with fixed roles, so that no staging register is ever
-    // copied (a copy would wait for the loads in flight).  At the top of each
-    // iteration stage s is in LDS buffer s & 1, stgB holds stage s + 1 (loads
-    // in flight) and stgA is free.  Step s loads stage s + 2 into stgA and
-    // writes stgB to the other buffer; step s + 1 loads stage s + 3 into stgB
-    // and writes stgA.  Each step ends with one barrier.
-    load_stage(0, stgA);
-    if (S > 1) load_stage(1, stgB);
-    store_stage(0, stgA);
-    __syncthreads();
-    int s = 0;
-    for (; s + 3 < S; s += 2) {
-      load_stage(s + 2, stgA);
-      compute(s & 1);
-      store_stage((s + 1) & 1, stgB);
-      __syncthreads();
-      load_stage(s + 3, stgB);
-      compute((s + 1) & 1);
-      store_stage(s & 1, stgA);
-      __syncthreads();
-    }
-    // the last one to three steps, same roles
-    if (s + 2 < S) load_stage(s + 2, stgA);
-    compute(s & 1);
-    if (s + 1 < S) {
-      store_stage((s + 1) & 1, stgB);
-      __syncthreads();
-      compute((s + 1) & 1);
-      if (s + 2 < S) {
-        store_stage(s & 1, stgA);
-        __syncthreads();
-        compute(s & 1);
-      }
-    }
-  }
-
-  // ---- epilogue: acc[i][j][4 gq + r] = C[m = wm*BT/2 + 32 i + (lane & 31)]
-  // [n = wn*64 + 32 j + 8 gq + 4 lk + r]: four consecutive n, one 8-byte store.
-  uint16_t* cbase = g.c + (WGRAD ? (size_t)e * g.c_estride : 0);
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int m = wm * (BT / 2) + 32 * i + (lane & 31);
-    if (m >= m_lim) continue;
-    uint16_t* crow = cbase + (size_t)(m0 + m) * g.ldc + n0;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int n = wn * 64 + 32 * j + 8 * gq + 4 * lk;
-        if (n >= n_lim) continue;
-        u32x2 pk;
-        pk.x = pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]);
-        pk.y = pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
-        *reinterpret_cast<u32x2*>(crow + n) = pk;
-      }
-  }
-}
 
 // ---------------------------------------------------------------- wgrad, LDS-DMA
 // C_e[M, N] = sum over the expert's rows r of A[r, m] B[r, n].  Both operands
@@ -548,6 +285,181 @@ __global__ __launch_bounds__(WT * 2, WT == 128 ? 2 : 1) void wgrad_dma_kernel(
   }
 }
 
+// ---------------------------------------------------------------- dgrad, LDS-DMA
+// C[rows, N] = A[rows, K] B_e[K, N] (+ a second part with the same leading
+// dimensions) over the expert row segments.  A (k contiguous) is copied to LDS
+// in 64-byte rows of 32 k (16-byte pieces XOR-swizzled with (row >> 2) & 3)
+// and read as 16-byte fragments; B (the expert's weights, n contiguous) is
+// copied as it lies and read transposed (ds_read_b64_tr_b16), as in the
+// wgrad.  128 x 128 tiles placed by the device tile table, four waves of
+// 64 x 64, 32-k stages in a ring of four, explicit waits, rows past the
+// tile's end clamped onto its last row, k past a part's end read from the
+// zero page.
+__global__ __launch_bounds__(256, 2) void dgrad_dma_kernel(GemmArgs g) {
+  constexpr int WT = 128;
+  constexpr int OPB = kWK * WT * 2;  // one operand's stage: 8 KB
+  constexpr int STB = 2 * OPB;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kWRing * STB];
+  __shared__ int s_tile[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wave == 0) place_tile<WT>(g.offs, g.E, g.rows, g.n_tiles, g.band, lane, s_tile);
+  __syncthreads();
+  const int e = s_tile[0];
+  if (e < 0) return;  // block-uniform
+  const int m0 = s_tile[1], m_lim = s_tile[2] - s_tile[1], n0 = s_tile[3] * WT;
+  const int n_lim = min(WT, g.N - n0);
+  const int K0 = g.part[0].K, K1 = g.nparts > 1 ? g.part[1].K : 0;
+  const int nst0 = (K0 + kWK - 1) / kWK;
+  const int nk = nst0 + (K1 + kWK - 1) / kWK;
+  const long lda = g.part[0].lda, ldb = g.part[0].ldb, bes = g.part[0].b_estride;
+
+  // ---- DMA: chunks 0..7 = A (16 rows of 64 bytes each), 8..15 = B (4 k-rows
+  // of 256 bytes each); wave w issues chunks w + 4 i.
+  uint32_t doff[kWDpw];  // element offset of this lane's piece inside the part's stage
+  int dk[kWDpw];         // k of this lane's piece inside the stage
+#pragma unroll
+  for (int i = 0; i < kWDpw; ++i) {
+    const int q = wave + 4 * i;
+    if (q < 8) {  // A: row 16 q + L / 4, physical piece L % 4
+      const int r = 16 * q + (lane >> 2);
+      const int lp = (lane & 3) ^ ((lane >> 4) & 3);
+      dk[i] = 8 * lp;
+      doff[i] = (uint32_t)((long)min(r, m_lim - 1) * lda + 8 * lp);
+    } else {  // B: k-row 4 (q - 8) + L / 16, physical piece L % 16
+      const int r = 4 * (q - 8) + (lane >> 4);
+      const int p = (lane & 15) ^ ((r & 3) << 2);
+      dk[i] = r;
+      doff[i] = (uint32_t)((long)r * ldb + min(8 * p, n_lim - 8));
+    }
+  }
+  const uint32_t lds0 = bw_lds_addr(ring);
+  auto issue = [&](int kt) {
+    const bool p1 = kt >= nst0;
+    const int ks = (kt - (p1 ? nst0 : 0)) * kWK;
+    const int klim = p1 ? K1 : K0;
+    const uint16_t* abase = (p1 ? g.part[1].a : g.part[0].a) + (size_t)m0 * lda + ks;
+    const uint16_t* bbase = (p1 ? g.part[1].b : g.part[0].b) + (size_t)e * bes + n0 +
+                            (size_t)ks * ldb;
+    const uint32_t sbase = lds0 + (uint32_t)(kt % kWRing) * STB;
+#pragma unroll
+    for (int i = 0; i < kWDpw; ++i) {
+      const int q = wave + 4 * i;
+      const uint16_t* base = q < 8 ? abase : bbase;
+      const void* src = ks + dk[i] < klim ? (const void*)(base + doff[i])
+                                          : (const void*)kBwZeroPage;
+      bw_dma16(src, sbase + (uint32_t)q * 1024u);
+    }
+  };
+
+  // ---- fragments
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lk = lane >> 5;
+  const int gq4 = lane >> 4;
+  const int tr_col = 16 * (gq4 & 1) + 4 * (lane & 3);
+  const int tr_row = 8 * (gq4 >> 1) + ((lane >> 2) & 3);
+  struct Frags {
+    bf16x8 a[2][2];
+    bf16x8 b[2][2];
+  };
+  auto load_frags = [&](int kt, Frags& F) {
+    const uint32_t sb = lds0 + (uint32_t)(kt % kWRing) * STB;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int qa = 2 * s2 + lk;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + 32 * i + (lane & 31);
+        const uint32_t off = (sb - lds0) + (uint32_t)((r * 4 + (qa ^ ((r >> 2) & 3))) * 16);
+        F.a[s2][i] = *reinterpret_cast<const bf16x8*>(ring + off);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = wn * 64 + 32 * j + tr_col;
+        bw_v4i16 h[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int r = 16 * s2 + tr_row + 4 * hh;
+          const uint32_t addr = sb + OPB + wg_piece<WT>(r, col >> 3) + (uint32_t)((col & 7) * 2);
+          h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) bw_v4i16*)(size_t)addr);
+        }
+        typedef short v8i16 __attribute__((ext_vector_type(8)));
+        const v8i16 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+        F.b[s2][j] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  auto mfma_stage = [&](const Frags& F) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.b[s2][j], F.a[s2][i], acc[i][j],
+                                                              0, 0, 0);
+  };
+  // same ring discipline as the wgrad with prefetch: stage kt's fragments are
+  // read during step kt - 1; the end of step kt makes stage kt + 2 visible and
+  // refills slot kt % 4 with stage kt + 4
+  if (nk > 0) {
+#pragma unroll
+    for (int i = 0; i < kWRing; ++i)
+      if (i < nk) issue(i);
+    {
+      const int later = min(nk - 1, kWRing - 1) - 1;
+      if (later <= 0) bw_wait_vm_barrier<0>();
+      else if (later == 1) bw_wait_vm_barrier<kWDpw>();
+      else bw_wait_vm_barrier<2 * kWDpw>();
+    }
+    auto finish = [&](int kt) {
+      const int j = kt + 2;
+      const int later = j < nk ? min(nk - 1, kt + kWRing - 1) - j : 0;
+      if (later <= 0) bw_wait_vm_barrier<0>();
+      else bw_wait_vm_barrier<kWDpw>();
+      if (kt + kWRing < nk) issue(kt + kWRing);
+    };
+    Frags F0, F1;
+    load_frags(0, F0);
+    auto step = [&](int kt, Frags& cur, Frags& nxt) {
+      load_frags(min(kt + 1, nk - 1), nxt);
+      mfma_stage(cur);
+      finish(kt);
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(kt, F0, F1);
+      if (kt + 1 < nk) step(kt + 1, F1, F0);
+    }
+  }
+
+  // ---- epilogue: C[row m0 + m][n0 + n]
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = wm * 64 + 32 * i + (lane & 31);
+    if (m >= m_lim) continue;
+    uint16_t* crow = g.c + (size_t)(m0 + m) * g.ldc + n0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int n = wn * 64 + 32 * j + 8 * gq + 4 * lk;
+        if (n >= n_lim) continue;
+        u32x2 pk;
+        pk.x = pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]);
+        pk.y = pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
+        *reinterpret_cast<u32x2*>(crow + n) = pk;
+      }
+  }
+}
+
 // dgrad: C[rows, N] = A[rows, K] B_e[K, N] (+ the second part), by expert
 // row segments.  Every K, N and leading dimension is a multiple of 8.
 // wgrad: 256-wide tiles when they still give every CU a tile, else 128-wide.
@@ -572,7 +484,7 @@ static hipError_t launch_dgrad(const GemmPart* parts, int nparts, const int32_t*
   // fit its registers without spilling)
   g.n_tiles = div_up(N, 128);
   const long total = (long)g.n_tiles * worst_row_tiles(rows, E, 128);
-  grouped_gemm_bwd_kernel<false, 128><<<(int)((total + 7) / 8 * 8), 256, 0, st>>>(g);
+  dgrad_dma_kernel<<<(int)((total + 7) / 8 * 8), 256, 0, st>>>(g);
   return hipGetLastError();
 }
 
