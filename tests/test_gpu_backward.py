@@ -302,3 +302,14 @@ def test_backward_full_size_sampled():
     ok &= check("d_x[sample]", host(g["d_x"])[tokens], dx + dxr, "row")
     log("  norm/elem errors: " + " ".join(f"{n}={a:.1e}/{b:.1e}" for n, (a, b) in errs.items()))
     assert ok, {n: v for n, v in errs.items() if not (v[0] <= TOL_NORM and v[1] <= TOL_ELEM)}
+
+
+def test_backward_long_reductions_take_the_wide_wgrad_tiles():
+    """8 experts x ~1024 rows each: the weight gradients take the 256-wide
+    wgrad tiles (long reductions; 8 x 8 x 4 = 256 tiles), which the reduced
+    workloads above never reach."""
+    shape = C.E8_D4096.replace(name="bwd-long-k", T=4096, d=2048, E=8, k=2, f=1024)
+    assert shape.T * shape.k >= 1024 * shape.E
+    assert shape.E * (shape.d // 256) * (shape.f // 256) >= 256
+    log(f"[backward] {shape.name}")
+    _check(shape, seed=11)
