@@ -238,6 +238,15 @@ def test_backward_full_size_sampled():
     u = torch.empty_like(a)
     B.moe_ffn_gate_up_packed_train(cfg, buf["x_perm"], None, buf["expert_offsets"], pgu,
                                    buf["h"], a, u)
+    # the same GEMM with the dispatch gather fused in (the whole-slab tile
+    # shape with both the gather and the saved pre-activations): bit for bit
+    h2, a2, u2 = torch.empty_like(buf["h"]), torch.empty_like(a), torch.empty_like(a)
+    B.moe_ffn_gate_up_packed_train(cfg, dev["x"], buf["src_of"], buf["expert_offsets"], pgu,
+                                   h2, a2, u2)
+    torch.cuda.synchronize()
+    for p_, q_ in ((buf["h"], h2), (a, a2), (u, u2)):
+        assert torch.equal(p_.view(torch.int16), q_.view(torch.int16))
+    del h2, a2, u2
     B.moe_ffn_down_packed(cfg, buf["h"], buf["expert_offsets"], pd, buf["y_perm"])
     B.moe_combine(cfg, buf["y_perm"], buf["slot_of"], buf["topk_w"], buf["out"])
     del pgu, pd

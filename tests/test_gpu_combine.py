@@ -13,7 +13,8 @@ from top_routing_expert_amd import inputs as I
 pytestmark = pytest.mark.gpu
 
 CASES = [(1, 64, 8, 2, "bf16"), (1000, 256, 64, 2, "bf16"), (333, 512, 256, 8, "bf16"),
-         (77, 128, 1024, 16, "bf16"), (256, 64, 8, 2, "f32"), (129, 68, 8, 3, "f32")]
+         (77, 128, 1024, 16, "bf16"), (130, 320, 12, 3, "bf16"), (500, 192, 16, 4, "bf16"),
+         (256, 64, 8, 2, "f32"), (129, 68, 8, 3, "f32")]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[str(c) for c in CASES])
