@@ -38,6 +38,22 @@ def _check_route(shape, inp, buf, rows_for_bound=None):
     return z, idx
 
 
+# expert counts whose gate GEMM takes the 32-, 128- and 256-wide expert blocks
+# (the workloads only reach the E <= 16, 64 and 256 shapes), with ragged T and E
+GEMM_SHAPES = [dict(E=24, k=2, T=333, d=320), dict(E=100, k=5, T=257, d=256, presel=20),
+               dict(E=1024, k=16, T=130, d=128, n_group=64, topk_group=16, presel=32)]
+
+
+@pytest.mark.parametrize("over", GEMM_SHAPES, ids=[str(o) for o in GEMM_SHAPES])
+def test_route_gemm_expert_blocks(over):
+    shape = C.E8_D4096.replace(name="route-blocks", ep_ranks=1, renorm=1, **over)
+    log(f"[route] gate GEMM blocks {over}")
+    inp = I.make_inputs(shape, seed=23, with_experts=False)
+    dev, buf = upload(inp), alloc(shape)
+    _route(shape, dev, buf)
+    _check_route(shape, inp, buf)
+
+
 @pytest.mark.parametrize("key", list(C.SMALL), ids=list(C.SMALL))
 def test_route_small_shapes(key):
     shape = C.SMALL[key]
