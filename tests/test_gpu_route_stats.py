@@ -55,6 +55,14 @@ def test_route_stats_small_shapes(key):
     _check(*_stats(shape, 101))
 
 
+def test_route_stats_many_experts():
+    """1024 experts (16 scores per lane), pre-selection and groups."""
+    shape = C.SMALL["e64"].replace(name="stats-e1024", T=300, E=1024, k=16, presel=32, renorm=0,
+                                   n_group=64, topk_group=16, ep_ranks=16, d=128)
+    log(f"[route-stats] {shape.name}")
+    _check(*_stats(shape, 103))
+
+
 @pytest.mark.parametrize("shape", C.CONFIGS, ids=lambda s: s.name)
 def test_route_stats_full_size(shape):
     log(f"[route-stats] {shape.name}")
