@@ -458,6 +458,26 @@ def pin_gates_backward_matches_autograd():
         assert np.allclose(ds.sum(axis=1), 0.0, atol=1e-12)  # softmax shift invariance
 
 
+def pin_gates_backward_two_choice_closed_form():
+    """Top-2 with renormalisation: g1 = sigmoid(s1 - s2), g2 = 1 - g1, so
+    ds1 = g1 g2 (dg1 - dg2) = -ds2 and every other expert gets nothing."""
+    rng = np.random.default_rng(45)
+    T, E = 9, 7
+    s = rng.standard_normal((T, E)).astype(np.float32)
+    dg = rng.standard_normal((T, 2))
+    sel = om.select(s, 2)
+    ds = om.gates_backward(s, sel, dg, 2, 0, 1)
+    s64 = s.astype(np.float64)
+    for t in range(T):
+        e1, e2 = int(sel[t, 0]), int(sel[t, 1])
+        g1 = 1.0 / (1.0 + math.exp(-(s64[t, e1] - s64[t, e2])))
+        want = g1 * (1.0 - g1) * (dg[t, 0] - dg[t, 1])
+        assert math.isclose(ds[t, e1], want, rel_tol=1e-12, abs_tol=1e-15)
+        assert math.isclose(ds[t, e2], -want, rel_tol=1e-12, abs_tol=1e-15)
+        others = [e for e in range(E) if e not in (e1, e2)]
+        assert np.all(ds[t, others] == 0)
+
+
 def pin_single_choice_router_has_no_gradient():
     """k = 1 with renormalisation: the gate is 1 whatever the scores, so the
     router gets no gradient at all."""
