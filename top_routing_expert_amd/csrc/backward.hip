@@ -36,6 +36,7 @@
 //    buffers (they only feed outputs that are never stored); k past the end
 //    of a part or an expert's segment is read from a page of zeros.
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "tiles.h"
@@ -104,49 +105,57 @@ __device__ __forceinline__ uint32_t wg_piece(int r, int p) {
   return (uint32_t)(r * (2 * WT) + ((p ^ ((r & 3) << 2)) << 4));
 }
 
-// WT = 128: four waves of 64 x 64, 64 KB ring, two blocks per CU, the next
-// stage's fragments read while the current one's MFMAs run.  WT = 256: eight
+// <TM, TN>: tile of TM rows of C (A columns) by TN columns (B columns).
+// 128 x 128: four waves of 64 x 64, 64 KB ring, two blocks per CU, the next
+// stage's fragments read while the current one's MFMAs run.  256 x 256: eight
 // waves of 128 x 64, 128 KB ring, one block per CU, half the operand bytes
-// per flop; one fragment set (two would not fit its registers).
-template <int WT>
-__global__ __launch_bounds__(WT * 2, WT == 128 ? 2 : 1) void wgrad_dma_kernel(
+// per flop.  256 x 128: four waves of 128 x 64, a ring of three (72 KB), two
+// blocks per CU, a quarter fewer operand bytes per flop.  The larger wave
+// tiles keep one fragment set (two would not fit their registers).
+template <int TM, int TN>
+__global__ __launch_bounds__(TN == 256 ? 512 : 256, TN == 256 ? 1 : 2) void wgrad_dma_kernel(
     const uint16_t* __restrict__ a, long lda, const uint16_t* __restrict__ b, long ldb,
     const int32_t* __restrict__ offs, int E, int rows, int M, int N, int m_tiles, int n_tiles,
     uint16_t* __restrict__ c, long ldc, long c_estride) {
-  constexpr int NW = WT / 32;                  // waves (4 or 8)
+  constexpr int NW = TN == 256 ? 8 : 4;        // waves
   constexpr int WN = NW / 2;                   // waves along N; two along M
-  constexpr int FM = WT / 64;                  // 32-column A fragments per wave
-  constexpr int OPB = kWK * WT * 2;            // one operand's stage
-  constexpr int STB = 2 * OPB;                 // one stage
-  constexpr int CPO = OPB / 1024;              // 1 KB chunks per operand
-  constexpr int RPC = 1024 / (2 * WT);         // k-rows per chunk
-  constexpr bool kPrefetch = WT == 128;
-  static_assert(2 * CPO == NW * kWDpw, "chunks per stage");
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[kWRing * STB];
+  constexpr int FM = TM / 64;                  // 32-column A fragments per wave
+  constexpr int RING = TM == 256 && TN == 128 ? 3 : kWRing;
+  constexpr int OPA = kWK * TM * 2;            // A's stage
+  constexpr int OPB = kWK * TN * 2;            // B's stage
+  constexpr int STB = OPA + OPB;               // one stage
+  constexpr int CA = OPA / 1024;               // 1 KB chunks of A
+  constexpr int RPCA = 1024 / (2 * TM), RPCB = 1024 / (2 * TN);  // k-rows per chunk
+  constexpr int DPW = (STB / 1024) / NW;       // DMA instructions per wave per stage
+  constexpr bool kPrefetch = TM == 128;
+  static_assert((STB / 1024) % NW == 0, "chunks per stage");
+  static_assert(WN * 64 == TN, "wave columns");
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[RING * STB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int per_e = m_tiles * n_tiles;
   const int e = blockIdx.x / per_e;
   const int rr = blockIdx.x - e * per_e;
-  const int m0 = (rr / n_tiles) * WT, n0 = (rr % n_tiles) * WT;
-  const int m_lim = min(WT, M - m0), n_lim = min(WT, N - n0);
+  const int m0 = (rr / n_tiles) * TM, n0 = (rr % n_tiles) * TN;
+  const int m_lim = min(TM, M - m0), n_lim = min(TN, N - n0);
   const int k0 = min(max(offs[e], 0), rows);
   const int k_lim = min(max(offs[e + 1], k0), rows) - k0;
   const int nk = (k_lim + kWK - 1) / kWK;
 
-  // ---- DMA: stage chunk q (1 KB) = operand q / CPO, k-rows RPC (q % CPO) ..;
-  // wave w issues chunks w + NW i.  Lane L lands at k-row RPC (q % CPO) +
-  // L / (WT / 8), physical piece L % (WT / 8), so it fetches logical piece
-  // (L % (WT / 8)) ^ ((row & 3) << 2).
-  int drow[kWDpw];
-  const uint16_t* dcol[kWDpw];
-  long dld[kWDpw];
+  // ---- DMA: stage chunk q (1 KB): A chunks first (RPCA k-rows each), then B
+  // (RPCB each); wave w issues chunks w + NW i.  Lane L lands at k-row
+  // RPC (chunk) + L / (width / 8), physical piece L % (width / 8), so it
+  // fetches logical piece (L % (width / 8)) ^ ((row & 3) << 2).
+  int drow[DPW];
+  const uint16_t* dcol[DPW];
+  long dld[DPW];
 #pragma unroll
-  for (int i = 0; i < kWDpw; ++i) {
+  for (int i = 0; i < DPW; ++i) {
     const int q = wave + NW * i;
-    const bool is_a = q < CPO;
-    const int r = RPC * (q % CPO) + lane / (WT / 8);
-    const int p = (lane % (WT / 8)) ^ ((r & 3) << 2);
+    const bool is_a = q < CA;
+    const int width = is_a ? TM : TN;
+    const int r = is_a ? RPCA * q + lane / (TM / 8) : RPCB * (q - CA) + lane / (TN / 8);
+    const int p = (lane % (width / 8)) ^ ((r & 3) << 2);
     const int lim = is_a ? m_lim : n_lim;  // a multiple of 8
     const int col = min(8 * p, lim - 8);
     drow[i] = r;
@@ -155,9 +164,9 @@ __global__ __launch_bounds__(WT * 2, WT == 128 ? 2 : 1) void wgrad_dma_kernel(
   }
   const uint32_t lds0 = bw_lds_addr(ring);
   auto issue = [&](int kt) {
-    const uint32_t sbase = lds0 + (uint32_t)(kt % kWRing) * STB;
+    const uint32_t sbase = lds0 + (uint32_t)(kt % RING) * STB;
 #pragma unroll
-    for (int i = 0; i < kWDpw; ++i) {
+    for (int i = 0; i < DPW; ++i) {
       const int k = kt * kWK + drow[i];
       const void* src = k < k_lim ? (const void*)(dcol[i] + (size_t)k * dld[i])
                                   : (const void*)kBwZeroPage;
@@ -165,7 +174,7 @@ __global__ __launch_bounds__(WT * 2, WT == 128 ? 2 : 1) void wgrad_dma_kernel(
     }
   };
 
-  // ---- fragments: wave (wm, wn) owns A columns wm*WT/2.. and B columns wn*64..
+  // ---- fragments: wave (wm, wn) owns A columns wm*TM/2.. and B columns wn*64..
   const int wm = wave / WN, wn = wave % WN;
   const int g = lane >> 4;
   const int tr_col = 16 * (g & 1) + 4 * (lane & 3);  // column of the addressed piece
@@ -174,13 +183,14 @@ __global__ __launch_bounds__(WT * 2, WT == 128 ? 2 : 1) void wgrad_dma_kernel(
     bf16x8 a[2][FM];  // [k slab][fragment]
     bf16x8 b[2][2];
   };
-  auto read_frag = [&](uint32_t opbase, int col0, int s2) -> bf16x8 {
+  auto read_frag = [&](uint32_t opbase, int col0, int s2, auto width_c) -> bf16x8 {
+    constexpr int W = decltype(width_c)::value;
     const int col = col0 + tr_col;
     bw_v4i16 h[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int r = 16 * s2 + tr_row + 4 * hh;
-      const uint32_t addr = opbase + wg_piece<WT>(r, col >> 3) + (uint32_t)((col & 7) * 2);
+      const uint32_t addr = opbase + wg_piece<W>(r, col >> 3) + (uint32_t)((col & 7) * 2);
       h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) bw_v4i16*)(size_t)addr);
     }
@@ -189,13 +199,15 @@ __global__ __launch_bounds__(WT * 2, WT == 128 ? 2 : 1) void wgrad_dma_kernel(
     return __builtin_bit_cast(bf16x8, v);
   };
   auto load_frags = [&](int kt, Frags& F) {
-    const uint32_t sb = lds0 + (uint32_t)(kt % kWRing) * STB;
+    const uint32_t sb = lds0 + (uint32_t)(kt % RING) * STB;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) F.a[s2][i] = read_frag(sb, wm * (WT / 2) + 32 * i, s2);
+      for (int i = 0; i < FM; ++i)
+        F.a[s2][i] = read_frag(sb, wm * (TM / 2) + 32 * i, s2, std::integral_constant<int, TM>());
 #pragma unroll
-      for (int j = 0; j < 2; ++j) F.b[s2][j] = read_frag(sb + OPB, wn * 64 + 32 * j, s2);
+      for (int j = 0; j < 2; ++j)
+        F.b[s2][j] = read_frag(sb + OPA, wn * 64 + 32 * j, s2, std::integral_constant<int, TN>());
     }
   };
   f32x16 acc[FM][2];
@@ -215,7 +227,7 @@ __global__ __launch_bounds__(WT * 2, WT == 128 ? 2 : 1) void wgrad_dma_kernel(
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.b[s2][j], F.a[s2][i], acc[i][j],
                                                               0, 0, 0);
   };
-  // Stage j lives in ring slot j % 4.  With prefetch, stage kt's fragments are
+  // Stage j lives in ring slot j % RING.  With prefetch, stage kt's fragments are
   // read during step kt - 1; without, at the start of step kt.  End of step
   // kt: wait for this wave's copies of stage kt + 2 (kt + 1 without
   // prefetch), barrier (that stage visible; slot kt % 4 no longer read),
@@ -223,22 +235,22 @@ __global__ __launch_bounds__(WT * 2, WT == 128 ? 2 : 1) void wgrad_dma_kernel(
   constexpr int AHEAD = kPrefetch ? 2 : 1;
   if (nk > 0) {
 #pragma unroll
-    for (int i = 0; i < kWRing; ++i)
+    for (int i = 0; i < RING; ++i)
       if (i < nk) issue(i);
     {  // stages 0 .. AHEAD - 1 visible, the later ones may still fly
-      const int later = min(nk - 1, kWRing - 1) - (AHEAD - 1);
+      const int later = min(nk - 1, RING - 1) - (AHEAD - 1);
       if (later <= 0) bw_wait_vm_barrier<0>();
-      else if (later == 1) bw_wait_vm_barrier<kWDpw>();
-      else if (later == 2) bw_wait_vm_barrier<2 * kWDpw>();
-      else bw_wait_vm_barrier<3 * kWDpw>();
+      else if (later == 1) bw_wait_vm_barrier<DPW>();
+      else if (later == 2) bw_wait_vm_barrier<2 * DPW>();
+      else bw_wait_vm_barrier<3 * DPW>();
     }
     auto finish = [&](int kt) {
       const int j = kt + AHEAD;  // the stage that must be visible next
-      const int later = j < nk ? min(nk - 1, kt + kWRing - 1) - j : 0;
+      const int later = j < nk ? min(nk - 1, kt + RING - 1) - j : 0;
       if (later <= 0) bw_wait_vm_barrier<0>();
-      else if (later == 1) bw_wait_vm_barrier<kWDpw>();
-      else bw_wait_vm_barrier<2 * kWDpw>();
-      if (kt + kWRing < nk) issue(kt + kWRing);
+      else if (later == 1) bw_wait_vm_barrier<DPW>();
+      else bw_wait_vm_barrier<2 * DPW>();
+      if (kt + RING < nk) issue(kt + RING);
     };
     if constexpr (kPrefetch) {
       Frags F0, F1;
@@ -262,13 +274,13 @@ __global__ __launch_bounds__(WT * 2, WT == 128 ? 2 : 1) void wgrad_dma_kernel(
     }
   }
 
-  // ---- epilogue: acc[i][j][4 gq + r] = C[m = wm*WT/2 + 32 i + (lane & 31)]
+  // ---- epilogue: acc[i][j][4 gq + r] = C[m = wm*TM/2 + 32 i + (lane & 31)]
   // [n = wn*64 + 32 j + 8 gq + 4 (lane >> 5) + r]
   uint16_t* cbase = c + (size_t)e * c_estride;
   const int lk = lane >> 5;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int m = wm * (WT / 2) + 32 * i + (lane & 31);
+    const int m = wm * (TM / 2) + 32 * i + (lane & 31);
     if (m >= m_lim) continue;
     uint16_t* crow = cbase + (size_t)(m0 + m) * ldc + n0;
 #pragma unroll
@@ -493,16 +505,22 @@ static hipError_t launch_dgrad(const GemmPart* parts, int nparts, const int32_t*
 static hipError_t launch_wgrad(const uint16_t* a, long lda, const uint16_t* b, long ldb,
                                const int32_t* offs, int E, int rows, int M, int N, uint16_t* c,
                                long ldc, long c_estride, hipStream_t st) {
-  // 256-wide tiles for long reductions (measured: faster from ~2048 rows per
-  // expert, slower at ~256, where the 128-wide tile's two blocks per CU hide
-  // each tile's start and end) when they still give every CU one
-  if (rows >= 1024L * E && (long)E * div_up(M, 256) * div_up(N, 256) >= kCUs) {
+  // Long reductions (from ~1024 rows per expert): 256 x 256 where such tiles
+  // fill the chip; short ones: 256 x 128 (two blocks per CU) where those
+  // fill it twice over; else 128 x 128.
+  const long t256 = (long)E * div_up(M, 256) * div_up(N, 256);
+  const long t256x128 = (long)E * div_up(M, 256) * div_up(N, 128);
+  if (rows >= 1024L * E && t256 >= kCUs) {
     const int mt = div_up(M, 256), nt = div_up(N, 256);
-    wgrad_dma_kernel<256><<<(int)((long)E * mt * nt), 512, 0, st>>>(
-        a, lda, b, ldb, offs, E, rows, M, N, mt, nt, c, ldc, c_estride);
+    wgrad_dma_kernel<256, 256><<<(int)t256, 512, 0, st>>>(a, lda, b, ldb, offs, E, rows, M, N,
+                                                          mt, nt, c, ldc, c_estride);
+  } else if (t256x128 >= 2L * kCUs) {
+    const int mt = div_up(M, 256), nt = div_up(N, 128);
+    wgrad_dma_kernel<256, 128><<<(int)t256x128, 256, 0, st>>>(a, lda, b, ldb, offs, E, rows, M,
+                                                              N, mt, nt, c, ldc, c_estride);
   } else {
     const int mt = div_up(M, 128), nt = div_up(N, 128);
-    wgrad_dma_kernel<128><<<(int)((long)E * mt * nt), 256, 0, st>>>(
+    wgrad_dma_kernel<128, 128><<<(int)((long)E * mt * nt), 256, 0, st>>>(
         a, lda, b, ldb, offs, E, rows, M, N, mt, nt, c, ldc, c_estride);
   }
   return hipGetLastError();
