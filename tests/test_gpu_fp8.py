@@ -124,3 +124,44 @@ def test_fp8_rejects_unsupported_rows():
                                                         device="cuda"),
                            torch.empty((4, 8256), dtype=torch.uint8, device="cuda"),
                            torch.empty((4, 2), dtype=torch.float32, device="cuda"))
+
+
+@pytest.mark.parametrize("ci", [2, 5], ids=["T1024-d4096", "T8192-d7168"])
+def test_fp8_full_size_sampled(ci):
+    """The benchmark's workloads at full size: 64 token rows' codes and
+    (scale, zero), and 64 expert-ordered decoded rows, bit-exact against the
+    oracle (row-local, so the sample is exact)."""
+    shape = C.CONFIGS[ci - 1]
+    log(f"[fp8] full {shape.name}")
+    inp = I.make_inputs(shape, seed=ci, with_experts=False)
+    dev = upload(inp)
+    cfg = B.config(shape)
+    T, d, k, E = shape.T, shape.d, shape.k, shape.E
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    B.moe_route(cfg, dev["x"], dev["w_router"], dev["bias"], logits, idx, w,
+                B.workspace(cfg, "route"))
+    offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    roffs = torch.empty(shape.ep_ranks + 1, dtype=torch.int32, device="cuda")
+    slot = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    src = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    B.moe_permute(cfg, None, idx, offs, roffs, slot, src, None, B.workspace(cfg, "permute"))
+    codes = torch.empty((T, d), dtype=torch.uint8, device="cuda")
+    sz = torch.empty((T, 2), dtype=torch.float32, device="cuda")
+    B.moe_quantize_fp8(cfg, dev["x"], codes, sz)
+    xp = torch.empty((T * k, d), dtype=torch.bfloat16, device="cuda")
+    B.moe_dequantize_fp8(cfg, codes, src, sz, xp)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(ci)
+    toks = np.sort(rng.choice(T, size=64, replace=False))
+    c_ref, s_ref, z_ref = om.quantize_rows_fp8(inp["x"][toks])
+    got_sz = host(sz)[toks]
+    assert np.array_equal(host(codes)[toks], c_ref)
+    assert np.array_equal(got_sz[:, 0].view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(got_sz[:, 1].view(np.uint32), z_ref.view(np.uint32))
+    rows = np.sort(rng.choice(T * k, size=64, replace=False))
+    tok_of = host(src)[rows] // k
+    c2, s2, z2 = om.quantize_rows_fp8(inp["x"][tok_of])
+    want = om.dequantize_rows_fp8(c2, s2, z2)
+    assert np.array_equal(host(xp)[rows].view(np.uint16), want)
