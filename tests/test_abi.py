@@ -3,6 +3,8 @@ declares, and rejects bad arguments on the host before any launch."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -187,3 +189,47 @@ def test_backward_entries_reject_before_launch():
     assert L.moe_unpermute_backward(bf(cfg), fake, fake, fake + 4, fake, None) == B.MOE_EINVAL
     assert L.moe_ffn_gate_up_packed_train(bf(cfg), fake, None, fake, fake, fake, None, fake,
                                           None) == B.MOE_EINVAL  # a missing
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include "moe.h"
+int main(void) {
+  moe_config c = {1024, 4096, 8, 2, 11008, 1, 1, 0, 1, 2, MOE_BF16};
+  size_t perm = 0, layer = 0, bwd = 0;
+  int s1 = moe_workspace_bytes(&c, MOE_ENTRY_PERMUTE, &perm);
+  int s2 = moe_workspace_bytes(&c, MOE_ENTRY_LAYER, &layer);
+  int s3 = moe_workspace_bytes(&c, MOE_ENTRY_FFN_BACKWARD, &bwd);
+  moe_config bad = c;
+  bad.k = 0;
+  printf("%d %d %d %zu %zu %zu %d %d %s\n", s1, s2, s3, perm, layer, bwd, moe_validate(&c),
+         moe_validate(&bad), moe_strerror(MOE_EUNSUPPORTED));
+  return 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_header_is_a_plain_c_abi(tmp_path):
+    """A C99 program (gcc -std=c99 -pedantic -Werror) includes the header,
+    links the library and gets the same answers as the Python binding from
+    the host-only entry points."""
+    src = tmp_path / "t.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "t"
+    libdir = os.path.dirname(B.LIB_PATH)
+    inc = os.path.join(os.path.dirname(libdir), "include")
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", f"-I{inc}",
+                        str(src), f"-L{libdir}", "-lmoe_mi355x", f"-Wl,-rpath,{libdir}", "-o",
+                        str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr[-2000:]
+    f = r.stdout.split(maxsplit=8)
+    cfg = B.config(C.E8_D4096)
+    assert [int(v) for v in f[:3]] == [B.MOE_OK] * 3
+    assert int(f[3]) == B.workspace_bytes(cfg, "permute")
+    assert int(f[4]) == B.workspace_bytes(cfg, "layer")
+    assert int(f[5]) == B.workspace_bytes(cfg, "ffn_backward")
+    assert int(f[6]) == B.MOE_OK and int(f[7]) == B.MOE_EINVAL
+    assert f[8].strip() == B.strerror(B.MOE_EUNSUPPORTED)
