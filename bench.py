@@ -313,12 +313,17 @@ def main():
             dx=torch.empty((T, d), dtype=dt, device="cuda"),
         )
         ws_fb, ws_rb = B.workspace(cfg, "ffn_backward"), B.workspace(cfg, "route_backward")
+        images = (None, None)
+        if a.ffn == "packed":  # the transposed images for dh and dx, packed once like pgu / pd
+            images = B.pack_weights_backward(cfg, dev["w_gate"], dev["w_up"], dev["w_down"],
+                                             stream=stream)
+            torch.cuda.synchronize()
         calls["combine_bwd"] = lambda: B.moe_combine_backward(
             cfg, grad["dout"], buf["y"], buf["slot"], buf["w"], grad["dy"], grad["dw"], stream)
         calls["ffn_bwd"] = lambda: B.moe_ffn_backward(
             cfg, buf["xp"], buf["offs"], dev["w_gate"], dev["w_up"], dev["w_down"], grad["dy"],
             grad["dxp"], grad["dwg"], grad["dwu"], grad["dwd"], ws_fb, stream, a=buf.get("a"),
-            u=buf.get("u"))
+            u=buf.get("u"), packed_dh=images[0], packed_dx=images[1])
         calls["route_bwd"] = lambda: B.moe_route_backward(
             cfg, dev["x"], dev["w_router"], buf["logits"], dev["bias"], buf["idx"], grad["dw"],
             grad["dz"], grad["dxr"], grad["dwr"], grad["db"], ws_rb, stream)

@@ -387,21 +387,45 @@ int moe_combine_backward(const moe_config* cfg, const void* d_out, const void* y
 
 /*
  * grouped SwiGLU FFN backward over the expert row segments of x_perm:
- *   a = x Wg_e^T, u = x Wu_e^T (recomputed: the forward keeps only h),
+ *   a = x Wg_e^T, u = x Wu_e^T (the training forward's, when a and u are
+ *     given, [T*k, f] bf16 each; else recomputed from x_perm),
  *   h = SiLU(a) u, dh = dy Wd_e, da = dh u SiLU'(a), du = dh SiLU(a),
  *   d_x_perm = da Wg_e + du Wu_e          [T*k, d] bf16 out
  *   d_w_gate[e] = da_e^T x_e              [E, f, d] bf16 out
  *   d_w_up[e]   = du_e^T x_e              [E, f, d] bf16 out
  *   d_w_down[e] = dy_e^T h_e              [E, d, f] bf16 out
  * x_perm [T*k, d] bf16 (the forward's dispatched rows), expert_offsets [E+1],
- * weights as in moe_grouped_ffn, d_y_perm [T*k, d] bf16.
- * ws: moe_workspace_bytes(MOE_ENTRY_FFN_BACKWARD) = 4 T k f bf16 (a/da,
- * u/du, h, dh), 256-byte aligned.
+ * weights as in moe_grouped_ffn, d_y_perm [T*k, d] bf16.  a and u are both
+ * given or both NULL.  packed_dh / packed_dx (each may be NULL): the images
+ * moe_pack_weights_backward wrote from these same weights; dh and d_x_perm
+ * are then computed on them by the packed kernel (same float32 sums over k
+ * in the same order, so the same results within accumulation rounding).
+ * ws: moe_workspace_bytes(MOE_ENTRY_FFN_BACKWARD) = 5 T k f bf16 (a, u,
+ * dh then h, and da | du side by side per row), 256-byte aligned.
  */
 int moe_ffn_backward(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
                      const void* w_gate, const void* w_up, const void* w_down, const void* a,
-                     const void* u, const void* d_y_perm, void* d_x_perm, void* d_w_gate,
-                     void* d_w_up, void* d_w_down, void* ws, size_t ws_bytes, void* stream);
+                     const void* u, const void* packed_dh, const void* packed_dx,
+                     const void* d_y_perm, void* d_x_perm, void* d_w_gate, void* d_w_up,
+                     void* d_w_down, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Packed images for the two activation-gradient products of the FFN
+ * backward: dh = dy Wd_e needs W_d^T ([E, f, d] view of w_down [E, d, f]),
+ * d_x_perm = [da du] [Wg_e; Wu_e] needs [W_g; W_u]^T ([E, d, 2 f] view).
+ * Both are written in the plain (down-projection) layout of
+ * moe_pack_weights, so the same packed kernel serves them.  Like the
+ * forward's images they are a load-time layout: after a weight update they
+ * must be written again.
+ * moe_packed_weight_bytes_backward: bytes of the two images (bf16 only).
+ * moe_pack_weights_backward: writes packed_dh from w_down and/or packed_dx
+ *   from w_gate and w_up; either output may be NULL.  Outputs 16-byte
+ *   aligned; enqueue-only.
+ */
+int moe_packed_weight_bytes_backward(const moe_config* cfg, size_t* dh_bytes, size_t* dx_bytes);
+int moe_pack_weights_backward(const moe_config* cfg, const void* w_gate, const void* w_up,
+                              const void* w_down, void* packed_dh, void* packed_dx,
+                              void* stream);
 
 /*
  * Training forward of the first FFN GEMM: moe_ffn_gate_up_packed (src_of ==

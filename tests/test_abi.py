@@ -163,17 +163,31 @@ def test_backward_entries_reject_before_launch():
     # FFN backward
     need = B.workspace_bytes(cfg, "ffn_backward")
     A, f = C.E8_D4096.T * C.E8_D4096.k, C.E8_D4096.f
-    assert need >= 4 * A * f * 2
+    assert need >= 5 * A * f * 2  # a, u, dh / h, da | du
     args = [fake, fake, fake, fake, fake]  # x_perm, offsets, w_gate, w_up, w_down
     outs = [fake, fake, fake, fake, fake]  # d_y_perm, d_x_perm, d_w_gate, d_w_up, d_w_down
-    assert L.moe_ffn_backward(bf(f32), *args, None, None, *outs, fake, 1 << 34,
+    assert L.moe_ffn_backward(bf(f32), *args, None, None, None, None, *outs, fake, 1 << 34,
                               None) == B.MOE_EUNSUPPORTED
-    assert L.moe_ffn_backward(bf(cfg), *args, fake, None, *outs, fake, need,
+    assert L.moe_ffn_backward(bf(cfg), *args, fake, None, None, None, *outs, fake, need,
                               None) == B.MOE_EINVAL  # a without u
-    assert L.moe_ffn_backward(bf(cfg), *args, None, None, *outs, fake, need - 1,
+    assert L.moe_ffn_backward(bf(cfg), *args, None, None, None, None, *outs, fake, need - 1,
                               None) == B.MOE_EINVAL  # workspace too small
-    assert L.moe_ffn_backward(bf(cfg), *args, None, None, *outs, fake + 16, need,
+    assert L.moe_ffn_backward(bf(cfg), *args, None, None, None, None, *outs, fake + 16, need,
                               None) == B.MOE_EINVAL  # workspace not 256-byte aligned
+    assert L.moe_ffn_backward(bf(cfg), *args, None, None, fake + 2, None, *outs, fake, need,
+                              None) == B.MOE_EINVAL  # misaligned packed image
+    # packed transposed images for the backward
+    dh_b, dx_b = B.packed_weight_bytes_backward(cfg)
+    assert dh_b >= C.E8_D4096.E * C.E8_D4096.f * C.E8_D4096.d * 2
+    assert dx_b >= C.E8_D4096.E * 2 * C.E8_D4096.f * C.E8_D4096.d * 2
+    assert L.moe_pack_weights_backward(bf(f32), fake, fake, fake, fake, fake,
+                                       None) == B.MOE_EUNSUPPORTED
+    assert L.moe_pack_weights_backward(bf(cfg), fake, fake, fake, None, None,
+                                       None) == B.MOE_EINVAL  # no output
+    assert L.moe_pack_weights_backward(bf(cfg), fake, fake, None, fake, None,
+                                       None) == B.MOE_EINVAL  # dh image without w_down
+    assert L.moe_pack_weights_backward(bf(cfg), None, fake, fake, None, fake,
+                                       None) == B.MOE_EINVAL  # dx image without w_gate
     # router backward
     rneed = B.workspace_bytes(cfg, "route_backward")
     assert rneed > 0

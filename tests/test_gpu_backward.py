@@ -38,8 +38,9 @@ TOL_NORM = 1.5e-2
 TOL_ELEM = 0.15
 
 
-def _backward(shape, dev, buf, d_out, a=None, u=None):
-    """combine -> FFN -> router -> dispatch backward through the C ABI."""
+def _backward(shape, dev, buf, d_out, a=None, u=None, packed=(None, None)):
+    """combine -> FFN -> router -> dispatch backward through the C ABI;
+    packed: the transposed weight images for dh and d_x_perm, or Nones."""
     cfg = B.config(shape)
     T, d, E, k, f = shape.T, shape.d, shape.E, shape.k, shape.f
     bf, f32 = torch.bfloat16, torch.float32
@@ -60,7 +61,8 @@ def _backward(shape, dev, buf, d_out, a=None, u=None):
                            g["d_y_perm"], g["d_topk_w"])
     B.moe_ffn_backward(cfg, buf["x_perm"], buf["expert_offsets"], dev["w_gate"], dev["w_up"],
                        dev["w_down"], g["d_y_perm"], g["d_x_perm"], g["d_w_gate"], g["d_w_up"],
-                       g["d_w_down"], B.workspace(cfg, "ffn_backward"), a=a, u=u)
+                       g["d_w_down"], B.workspace(cfg, "ffn_backward"), a=a, u=u,
+                       packed_dh=packed[0], packed_dx=packed[1])
     B.moe_route_backward(cfg, dev["x"], dev["w_router"], buf["logits"], dev["bias"],
                          buf["topk_idx"], g["d_topk_w"], g["d_logits"], g["d_x_router"],
                          g["d_w_router"], g["d_bias"], B.workspace(cfg, "route_backward"))
@@ -103,7 +105,7 @@ def norm_err(got, want, group):
     return float(np.max(num[~zero] / den[~zero])) if np.any(~zero) else 0.0
 
 
-def _check(shape, seed):
+def _check(shape, seed, packed=False):
     inp = I.make_inputs(shape, seed=seed)
     dout_bits = I.make_grad_out(shape, seed)
     dev, buf = upload(inp), alloc(shape)
@@ -112,7 +114,9 @@ def _check(shape, seed):
     ref_fwd = om.layer(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
                        inp["w_down"], ep_ranks=shape.ep_ranks, **kw)
     assert np.array_equal(host(buf["topk_idx"]), ref_fwd["topk_idx"])
-    g = _backward(shape, dev, buf, B.to_device(dout_bits))
+    images = (B.pack_weights_backward(B.config(shape), dev["w_gate"], dev["w_up"], dev["w_down"])
+              if packed else (None, None))
+    g = _backward(shape, dev, buf, B.to_device(dout_bits), packed=images)
     ref = om.layer_backward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
                             inp["w_down"], om.widen_bf16(dout_bits), fwd=ref_fwd,
                             ep_ranks=shape.ep_ranks, **kw)
@@ -188,6 +192,24 @@ def test_backward_empty_batch():
         assert torch.count_nonzero(t).item() == 0
 
 
+@pytest.mark.parametrize("key", ["e8", "e64", "e16", "e256"])
+def test_layer_backward_on_packed_transposed_weights(key):
+    """dh = dy W_d and d_x_perm = [da du] [W_g; W_u] on the packed images of
+    W_d^T and [W_g; W_u]^T (the forward's packed kernel), to the same bounds."""
+    shape = C.SMALL[key]
+    log(f"[backward] packed images {shape.name}")
+    _check(shape, seed=13, packed=True)
+
+
+def test_packed_transposed_images_ragged_f():
+    """f = 320 (not a whole 256-feature slab for dh, a ragged 128-wide k
+    iteration for d_x_perm's k = 2 f = 640) and d = 1088: the images' zero
+    padding and the kernel's clamped tails."""
+    shape = C.SMALL["e8"].replace(name="bwd-packed-ragged", d=1088, f=320)
+    log(f"[backward] {shape.name}")
+    _check(shape, seed=17, packed=True)
+
+
 @pytest.mark.parametrize("key,gather", [("e8", True), ("e16", False), ("e256", True)])
 def test_backward_on_saved_preactivations(key, gather):
     """Training forward: the packed first GEMM also writes a = x Wg^T and
@@ -237,7 +259,8 @@ def test_backward_on_saved_preactivations(key, gather):
 
 def test_backward_full_size_sampled():
     """T1024-d4096-E8-top2-f11008 in the benchmark's configuration (training
-    forward with the packed weights, saved pre-activations): two experts'
+    forward with the packed weights, saved pre-activations, backward on the
+    packed transposed images): two experts'
     whole row segments (every dx_perm row and the full dWg, dWu, dWd of each)
     and a sample of tokens (d_topk_w, dz, dz Wr, dx) against the oracle, on the
     GPU's routing (itself checked against the oracle's decision on the same
@@ -272,7 +295,9 @@ def test_backward_full_size_sampled():
     B.moe_combine(cfg, buf["y_perm"], buf["slot_of"], buf["topk_w"], buf["out"])
     del pgu, pd
     log("  backward")
-    g = _backward(shape, dev, buf, B.to_device(dout_bits), a=a, u=u)
+    images = B.pack_weights_backward(cfg, dev["w_gate"], dev["w_up"], dev["w_down"])
+    g = _backward(shape, dev, buf, B.to_device(dout_bits), a=a, u=u, packed=images)
+    del images
     del a, u
     idx, w = host(buf["topk_idx"]), host(buf["topk_w"]).astype(np.float64)
     logits = host(buf["logits"])

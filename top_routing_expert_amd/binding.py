@@ -33,7 +33,8 @@ EXPORTS = ("moe_strerror", "moe_validate", "moe_workspace_bytes", "moe_route", "
            "moe_ffn_gate_up_packed_gather", "moe_ffn_down_packed", "moe_layer_fwd_packed",
            "moe_route_stats", "moe_quantize_fp8", "moe_dequantize_fp8", "moe_combine_backward",
            "moe_ffn_backward", "moe_route_backward", "moe_unpermute_backward",
-           "moe_ffn_gate_up_packed_train")
+           "moe_ffn_gate_up_packed_train", "moe_packed_weight_bytes_backward",
+           "moe_pack_weights_backward")
 
 
 class MoEConfig(ctypes.Structure):
@@ -84,7 +85,10 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_down_packed.argtypes = [cfgp, vp, vp, vp, vp, vp]
         L.moe_combine_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_ffn_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                       sz, vp]
+                                       vp, vp, sz, vp]
+        L.moe_packed_weight_bytes_backward.argtypes = [cfgp, ctypes.POINTER(sz),
+                                                       ctypes.POINTER(sz)]
+        L.moe_pack_weights_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
         L.moe_ffn_gate_up_packed_train.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_route_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                          vp]
@@ -285,14 +289,40 @@ def moe_ffn_gate_up_packed_train(cfg, act, src_of, expert_offsets, packed_gate_u
 
 
 def moe_ffn_backward(cfg, x_perm, expert_offsets, w_gate, w_up, w_down, d_y_perm, d_x_perm,
-                     d_w_gate, d_w_up, d_w_down, ws=None, stream=None, a=None, u=None):
+                     d_w_gate, d_w_up, d_w_down, ws=None, stream=None, a=None, u=None,
+                     packed_dh=None, packed_dx=None):
     wp, wn = _ws(ws)
     _check("moe_ffn_backward",
            lib().moe_ffn_backward(ctypes.byref(cfg), _ptr(x_perm), _ptr(expert_offsets),
                                   _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(a), _ptr(u),
-                                  _ptr(d_y_perm),
+                                  _ptr(packed_dh), _ptr(packed_dx), _ptr(d_y_perm),
                                   _ptr(d_x_perm), _ptr(d_w_gate), _ptr(d_w_up), _ptr(d_w_down),
                                   wp, wn, _stream(stream)))
+
+
+def packed_weight_bytes_backward(cfg) -> tuple[int, int]:
+    dh, dx = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("moe_packed_weight_bytes_backward",
+           lib().moe_packed_weight_bytes_backward(ctypes.byref(cfg), ctypes.byref(dh),
+                                                  ctypes.byref(dx)))
+    return dh.value, dx.value
+
+
+def moe_pack_weights_backward(cfg, w_gate, w_up, w_down, packed_dh, packed_dx, stream=None):
+    _check("moe_pack_weights_backward",
+           lib().moe_pack_weights_backward(ctypes.byref(cfg), _ptr(w_gate), _ptr(w_up),
+                                           _ptr(w_down), _ptr(packed_dh), _ptr(packed_dx),
+                                           _stream(stream)))
+
+
+def pack_weights_backward(cfg, w_gate, w_up, w_down, device="cuda", stream=None):
+    """Allocates and fills the two transposed images the FFN backward's
+    activation-gradient products can run on (uint8 device tensors)."""
+    dh, dx = packed_weight_bytes_backward(cfg)
+    pdh = torch.empty(dh, dtype=torch.uint8, device=device)
+    pdx = torch.empty(dx, dtype=torch.uint8, device=device)
+    moe_pack_weights_backward(cfg, w_gate, w_up, w_down, pdh, pdx, stream)
+    return pdh, pdx
 
 
 def moe_route_backward(cfg, x, w_router, logits, bias, topk_idx, d_topk_w, d_logits, d_x_router,

@@ -363,6 +363,27 @@ int moe_pack_weights(const moe_config* cfg, const void* w_gate, const void* w_up
                                        static_cast<hipStream_t>(stream)));
 }
 
+int moe_packed_weight_bytes_backward(const moe_config* cfg, size_t* dh_bytes, size_t* dx_bytes) {
+  int s = check_packed(cfg);
+  if (s != MOE_OK) return s;
+  if (!dh_bytes || !dx_bytes) return MOE_EINVAL;
+  *dh_bytes = (size_t)cfg->E * pack_geom(cfg->f, cfg->d, false).expert_elems * 2;
+  *dx_bytes = (size_t)cfg->E * pack_geom(cfg->d, 2 * cfg->f, false).expert_elems * 2;
+  return MOE_OK;
+}
+
+int moe_pack_weights_backward(const moe_config* cfg, const void* w_gate, const void* w_up,
+                              const void* w_down, void* packed_dh, void* packed_dx,
+                              void* stream) {
+  int s = check_packed(cfg);
+  if (s != MOE_OK) return s;
+  if (!packed_dh && !packed_dx) return MOE_EINVAL;
+  if (packed_dh && (!w_down || !aligned16(packed_dh))) return MOE_EINVAL;
+  if (packed_dx && (!w_gate || !w_up || !aligned16(packed_dx))) return MOE_EINVAL;
+  return status_of(launch_pack_weights_t(*cfg, w_gate, w_up, w_down, packed_dh, packed_dx,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int moe_ffn_gate_up_packed(const moe_config* cfg, const void* x_perm,
                            const int32_t* expert_offsets, const void* packed_gate_up, void* h,
                            void* stream) {
@@ -485,8 +506,9 @@ int moe_combine_backward(const moe_config* cfg, const void* d_out, const void* y
 
 int moe_ffn_backward(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
                      const void* w_gate, const void* w_up, const void* w_down, const void* a,
-                     const void* u, const void* d_y_perm, void* d_x_perm, void* d_w_gate,
-                     void* d_w_up, void* d_w_down, void* ws, size_t ws_bytes, void* stream) {
+                     const void* u, const void* packed_dh, const void* packed_dx,
+                     const void* d_y_perm, void* d_x_perm, void* d_w_gate, void* d_w_up,
+                     void* d_w_down, void* ws, size_t ws_bytes, void* stream) {
   int s = check_core(cfg);
   if (s != MOE_OK) return s;
   if (cfg->dtype != MOE_BF16) return MOE_EUNSUPPORTED;
@@ -494,14 +516,14 @@ int moe_ffn_backward(const moe_config* cfg, const void* x_perm, const int32_t* e
     return MOE_EINVAL;
   if (cfg->T > 0 && (!x_perm || !d_y_perm || !d_x_perm)) return MOE_EINVAL;
   if (!a != !u) return MOE_EINVAL;
-  const void* al[] = {x_perm, w_gate, w_up, w_down, a, u, d_y_perm, d_x_perm, d_w_gate, d_w_up,
-                      d_w_down, ws};
+  const void* al[] = {x_perm, w_gate, w_up, w_down, a, u, packed_dh, packed_dx, d_y_perm,
+                      d_x_perm, d_w_gate, d_w_up, d_w_down, ws};
   for (const void* p : al)
     if (p && !aligned16(p)) return MOE_EINVAL;
   if ((s = check_ws(ffn_backward_ws_bytes(*cfg), ws, ws_bytes)) != MOE_OK) return s;
   return status_of(launch_ffn_backward(*cfg, x_perm, expert_offsets, w_gate, w_up, w_down, a, u,
-                                       d_y_perm, d_x_perm, d_w_gate, d_w_up, d_w_down, ws,
-                                       static_cast<hipStream_t>(stream)));
+                                       packed_dh, packed_dx, d_y_perm, d_x_perm, d_w_gate,
+                                       d_w_up, d_w_down, ws, static_cast<hipStream_t>(stream)));
 }
 
 int moe_route_backward(const moe_config* cfg, const void* x, const void* w_router,

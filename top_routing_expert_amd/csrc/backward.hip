@@ -567,16 +567,17 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
 }
 
 // ------------------------------------------------------------- SwiGLU backward
-// Per element: h = SiLU(a) u; da = dh u SiLU'(a); du = dh SiLU(a).  da and du
-// may overwrite a and u (same element, read before written).
-__global__ __launch_bounds__(256) void swiglu_backward_kernel(const u32x4* __restrict__ dh,
-                                                              const u32x4* a_in,
-                                                              const u32x4* u_in, u32x4* da_out,
-                                                              u32x4* du_out,
-                                                              u32x4* __restrict__ h, long nvec) {
+// Per element: h = SiLU(a) u; da = dh u SiLU'(a); du = dh SiLU(a).
+// dh and h share one buffer (element i read, then written, by one thread);
+// da and du go side by side into one [rows, 2 f] buffer (row r: da_r, du_r),
+// the activation operand of dx = [da du] [W_g; W_u].  fv = f / 8.
+__global__ __launch_bounds__(256) void swiglu_backward_kernel(const u32x4* a_in, const u32x4* u_in,
+                                                              u32x4* dh_h,
+                                                              u32x4* __restrict__ dadu, long fv,
+                                                              long nvec) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= nvec) return;
-  const u32x4 va = a_in[i], vu = u_in[i], vd = dh[i];
+  const u32x4 va = a_in[i], vu = u_in[i], vd = dh_h[i];
   u32x4 oh, oa, ou;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -596,9 +597,10 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(const u32x4* __res
     oa[q] = pack_bf16x2(r[0][1], r[1][1]);
     ou[q] = pack_bf16x2(r[0][2], r[1][2]);
   }
-  h[i] = oh;
-  da_out[i] = oa;
-  du_out[i] = ou;
+  const long r = i / fv, cv = i - r * fv;
+  dh_h[i] = oh;
+  dadu[r * 2 * fv + cv] = oa;
+  dadu[r * 2 * fv + fv + cv] = ou;
 }
 
 // ------------------------------------------------------------- gates backward
@@ -758,19 +760,20 @@ hipError_t launch_combine_backward(const moe_config& c, const void* d_out, const
 }
 
 size_t ffn_backward_ws_bytes(const moe_config& c) {
-  return 4 * (size_t)c.T * c.k * c.f * sizeof(uint16_t);
+  return 5 * (size_t)c.T * c.k * c.f * sizeof(uint16_t);  // a, u, dh / h, da | du
 }
 
 hipError_t launch_ffn_backward(const moe_config& c, const void* x_perm, const int32_t* offs,
                                const void* wg, const void* wu, const void* wd, const void* a_in,
-                               const void* u_in, const void* d_y_perm, void* d_x_perm,
-                               void* d_wg, void* d_wu, void* d_wd, void* ws, hipStream_t st) {
+                               const void* u_in, const void* packed_dh, const void* packed_dx,
+                               const void* d_y_perm, void* d_x_perm, void* d_wg, void* d_wu,
+                               void* d_wd, void* ws, hipStream_t st) {
   const int rows = c.T * c.k, d = c.d, f = c.f, E = c.E;
   const size_t af = (size_t)rows * f;
-  uint16_t* a = static_cast<uint16_t*>(ws);  // a, then da
-  uint16_t* u = a + af;                       // u, then du
-  uint16_t* h = u + af;
-  uint16_t* dh = h + af;
+  uint16_t* a = static_cast<uint16_t*>(ws);  // recomputed a
+  uint16_t* u = a + af;                       // recomputed u
+  uint16_t* h = u + af;                       // dh, then h
+  uint16_t* dadu = h + af;                    // [rows, 2 f]: da_r, du_r
   const auto* X = static_cast<const uint16_t*>(x_perm);
   const auto* dY = static_cast<const uint16_t*>(d_y_perm);
   const auto* Wg = static_cast<const uint16_t*>(wg);
@@ -797,37 +800,45 @@ hipError_t launch_ffn_backward(const moe_config& c, const void* x_perm, const in
     a_src = a;
     u_src = u;
   }
-  // dh = dy Wd_e   (Wd_e is [d, f])
-  {
+  // dh = dy Wd_e (Wd_e is [d, f]): on the packed image of W_d^T, else the dgrad
+  if (packed_dh) {
+    if ((err = launch_packed_linear(c, dY, offs, packed_dh, h, f, d, st)) != hipSuccess)
+      return err;
+  } else {
     GemmPart p{dY, Wd, d, f, (long)d * f, d};
-    if ((err = launch_dgrad(&p, 1, offs, E, rows, f, dh, f, st)) != hipSuccess) return err;
+    if ((err = launch_dgrad(&p, 1, offs, E, rows, f, h, f, st)) != hipSuccess) return err;
   }
-  // h, da, du
+  // h (over dh), da | du
   {
     const long nvec = (long)af / 8;
     swiglu_backward_kernel<<<div_up(nvec, 256), 256, 0, st>>>(
-        reinterpret_cast<const u32x4*>(dh), reinterpret_cast<const u32x4*>(a_src),
-        reinterpret_cast<const u32x4*>(u_src), reinterpret_cast<u32x4*>(a),
-        reinterpret_cast<u32x4*>(u), reinterpret_cast<u32x4*>(h), nvec);
+        reinterpret_cast<const u32x4*>(a_src), reinterpret_cast<const u32x4*>(u_src),
+        reinterpret_cast<u32x4*>(h), reinterpret_cast<u32x4*>(dadu), (long)f / 8, nvec);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   // dWd_e = dy_e^T h_e   [d, f]
   if ((err = launch_wgrad(dY, d, h, f, offs, E, rows, d, f, static_cast<uint16_t*>(d_wd), f,
                           (long)d * f, st)) != hipSuccess)
     return err;
-  // dx = da Wg_e + du Wu_e   (Wg_e, Wu_e are [f, d])
-  {
-    GemmPart p[2] = {{a, Wg, f, d, (long)f * d, f}, {u, Wu, f, d, (long)f * d, f}};
+  // dx = [da du] [Wg_e; Wu_e] (Wg_e, Wu_e are [f, d]): on the packed image of
+  // [W_g; W_u]^T (k = 2 f), else the dgrad over two parts
+  if (packed_dx) {
+    if ((err = launch_packed_linear(c, dadu, offs, packed_dx, d_x_perm, d, 2 * f, st)) !=
+        hipSuccess)
+      return err;
+  } else {
+    GemmPart p[2] = {{dadu, Wg, 2L * f, d, (long)f * d, f},
+                     {dadu + f, Wu, 2L * f, d, (long)f * d, f}};
     if ((err = launch_dgrad(p, 2, offs, E, rows, d, static_cast<uint16_t*>(d_x_perm), d, st)) !=
         hipSuccess)
       return err;
   }
   // dWg_e = da_e^T x_e, dWu_e = du_e^T x_e   [f, d]
-  if ((err = launch_wgrad(a, f, X, d, offs, E, rows, f, d, static_cast<uint16_t*>(d_wg), d,
-                          (long)f * d, st)) != hipSuccess)
+  if ((err = launch_wgrad(dadu, 2L * f, X, d, offs, E, rows, f, d, static_cast<uint16_t*>(d_wg),
+                          d, (long)f * d, st)) != hipSuccess)
     return err;
-  return launch_wgrad(u, f, X, d, offs, E, rows, f, d, static_cast<uint16_t*>(d_wu), d,
-                      (long)f * d, st);
+  return launch_wgrad(dadu + f, 2L * f, X, d, offs, E, rows, f, d,
+                      static_cast<uint16_t*>(d_wu), d, (long)f * d, st);
 }
 
 size_t route_backward_ws_bytes(const moe_config& c) {

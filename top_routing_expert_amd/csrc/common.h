@@ -85,6 +85,13 @@ hipError_t launch_ffn_gate_up_packed_save(const moe_config& c, const void* act,
                                           const int32_t* src_of, const int32_t* offs,
                                           const void* pgu, void* h, void* a, void* u,
                                           hipStream_t st);
+// out[rows, N] = act[rows, K] W'_e^T on a plain packed image of W' [E, N, K].
+hipError_t launch_packed_linear(const moe_config& c, const void* act, const int32_t* offs,
+                                const void* wp, void* out, int N, int K, hipStream_t st);
+// Plain packed images of W_d^T (N = f, K = d) and [W_g; W_u]^T (N = d, K = 2 f).
+hipError_t launch_pack_weights_t(const moe_config& c, const void* w_gate, const void* w_up,
+                                 const void* w_down, void* packed_dh, void* packed_dx,
+                                 hipStream_t st);
 hipError_t launch_ffn_down_packed(const moe_config& c, const void* h, const int32_t* offs,
                                   const void* packed_down, void* y, hipStream_t st);
 
@@ -111,8 +118,9 @@ hipError_t launch_combine_backward(const moe_config& c, const void* d_out, const
 size_t ffn_backward_ws_bytes(const moe_config& c);
 hipError_t launch_ffn_backward(const moe_config& c, const void* x_perm, const int32_t* offs,
                                const void* wg, const void* wu, const void* wd, const void* a_in,
-                               const void* u_in, const void* d_y_perm, void* d_x_perm,
-                               void* d_wg, void* d_wu, void* d_wd, void* ws, hipStream_t st);
+                               const void* u_in, const void* packed_dh, const void* packed_dx,
+                               const void* d_y_perm, void* d_x_perm, void* d_wg, void* d_wu,
+                               void* d_wd, void* ws, hipStream_t st);
 size_t route_backward_ws_bytes(const moe_config& c);
 hipError_t launch_route_backward(const moe_config& c, const void* x, const void* w_router,
                                  const float* logits, const float* bias, const int32_t* topk_idx,

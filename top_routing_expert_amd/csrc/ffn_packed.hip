@@ -111,6 +111,45 @@ __global__ void pack_weights_kernel(const uint16_t* __restrict__ w0, const uint1
   }
 }
 
+// The same plain (non-gated) image of a matrix W'[e][n][k] that is stored
+// transposed: W'[e][n][k] = src0[e][k][n] for k < K0, src1[e][k - K0][n] above
+// (src0 [E, K0, F], src1 [E, K - K0, F]).  The backward's activation-gradient
+// products use it: W_d^T (F = f, K = d) and [W_g; W_u]^T (F = d, K = 2 f).
+// A load-time layout like the forward's; the reads are strided.
+__global__ void pack_weights_t_kernel(const uint16_t* __restrict__ src0,
+                                      const uint16_t* __restrict__ src1, u32x4* __restrict__ dst,
+                                      int F, int K0, int K, int slabs, int kp, size_t total) {
+  const int nks = kp / 16;
+  for (size_t p = blockIdx.x * (size_t)blockDim.x + threadIdx.x; p < total;
+       p += (size_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(p & 63);
+    size_t r = p >> 6;
+    const int i = (int)(r & 1);
+    r >>= 1;
+    const int ks = (int)(r % nks);
+    r /= nks;
+    const int w = (int)(r & 3);
+    r >>= 2;
+    const int slab = (int)(r % slabs);
+    const size_t e = r / slabs;
+    const int feat = slab * 256 + w * 64 + i * 32 + (lane & 31);
+    const int k = ks * 16 + 8 * (lane >> 5);
+    uint16_t v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int kk = k + q;
+      v[q] = 0;
+      if (feat < F && kk < K)
+        v[q] = kk < K0 ? src0[(e * K0 + kk) * (size_t)F + feat]
+                       : src1[(e * (K - K0) + (kk - K0)) * (size_t)F + feat];
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = (uint32_t)v[2 * q] | ((uint32_t)v[2 * q + 1] << 16);
+    dst[p] = o;
+  }
+}
+
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time index).
 template <int N, typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
@@ -656,9 +695,8 @@ constexpr int kSizedMaxExperts = 16;
 template <bool GATED, int JMAX, int WF, bool GATHER, bool SAVE>
 static hipError_t launch_packed_t(const moe_config& c, const void* act, const int32_t* offs,
                                   const void* wp, void* out, const int32_t* src_of,
-                                  void* save_a, void* save_u, hipStream_t st) {
+                                  void* save_a, void* save_u, int N, int K, hipStream_t st) {
   const long rows = (long)c.T * c.k;
-  const int N = GATED ? c.f : c.d, K = GATED ? c.d : c.f;
   const PackGeom g = pack_geom(N, K, GATED);
   // one block per CU, never more blocks than the worst-case tile count
   const long worst = (long)g.slabs * (WF == 2 ? 1 : 2) * worst_row_tiles(rows, c.E, 32 * JMAX);
@@ -677,18 +715,26 @@ static hipError_t launch_packed_t(const moe_config& c, const void* act, const in
 // few experts with some hundred rows each: then half-slab tiles of up to 320
 // rows (WF = 1, JMAX = 10), which double the tile count and cover an expert of
 // up to 320 rows with one tile.
+// N output features over a k extent of K: (f, d) for the gate / up
+// projection, (d, f) for the down projection; others for the plain products
+// of the backward.
 template <bool GATED, bool GATHER, bool SAVE = false>
 static hipError_t launch_packed(const moe_config& c, const void* act, const int32_t* offs,
                                 const void* wp, void* out, const int32_t* src_of,
-                                hipStream_t st, void* save_a = nullptr, void* save_u = nullptr) {
+                                hipStream_t st, void* save_a = nullptr, void* save_u = nullptr,
+                                int N = 0, int K = 0) {
+  if (N == 0) {
+    N = GATED ? c.f : c.d;
+    K = GATED ? c.d : c.f;
+  }
   const long rows = (long)c.T * c.k;
-  const PackGeom g = pack_geom(GATED ? c.f : c.d, GATED ? c.d : c.f, GATED);
+  const PackGeom g = pack_geom(N, K, GATED);
   const long typical = (long)g.slabs * std::max<long>(c.E, (rows + 255) / 256);
   if (typical < 2L * device_cus())
     return launch_packed_t<GATED, 10, 1, GATHER, SAVE>(c, act, offs, wp, out, src_of, save_a,
-                                                       save_u, st);
+                                                       save_u, N, K, st);
   return launch_packed_t<GATED, 8, 2, GATHER, SAVE>(c, act, offs, wp, out, src_of, save_a, save_u,
-                                                    st);
+                                                    N, K, st);
 }
 
 hipError_t launch_ffn_gate_up_packed(const moe_config& c, const void* x_perm, const int32_t* offs,
@@ -708,6 +754,36 @@ hipError_t launch_ffn_gate_up_packed_save(const moe_config& c, const void* act,
                                           hipStream_t st) {
   if (src_of) return launch_packed<true, true, true>(c, act, offs, pgu, h, src_of, st, a, u);
   return launch_packed<true, false, true>(c, act, offs, pgu, h, nullptr, st, a, u);
+}
+
+// out[rows, N] = act[rows, K] W'_e^T on a plain image of W' [E, N, K]
+// (pack_geom(N, K, false)); act rows are K long.
+hipError_t launch_packed_linear(const moe_config& c, const void* act, const int32_t* offs,
+                                const void* wp, void* out, int N, int K, hipStream_t st) {
+  return launch_packed<false, false>(c, act, offs, wp, out, nullptr, st, nullptr, nullptr, N, K);
+}
+
+hipError_t launch_pack_weights_t(const moe_config& c, const void* w_gate, const void* w_up,
+                                 const void* w_down, void* packed_dh, void* packed_dx,
+                                 hipStream_t st) {
+  const int threads = 256, blocks = 4096;
+  if (packed_dh) {
+    const PackGeom g = pack_geom(c.f, c.d, false);
+    const size_t total = (size_t)c.E * g.expert_elems / 8;
+    pack_weights_t_kernel<<<blocks, threads, 0, st>>>(
+        static_cast<const uint16_t*>(w_down), nullptr, static_cast<u32x4*>(packed_dh), c.f, c.d,
+        c.d, g.slabs, g.kp, total);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (packed_dx) {
+    const PackGeom g = pack_geom(c.d, 2 * c.f, false);
+    const size_t total = (size_t)c.E * g.expert_elems / 8;
+    pack_weights_t_kernel<<<blocks, threads, 0, st>>>(
+        static_cast<const uint16_t*>(w_gate), static_cast<const uint16_t*>(w_up),
+        static_cast<u32x4*>(packed_dx), c.d, c.f, 2 * c.f, g.slabs, g.kp, total);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_ffn_down_packed(const moe_config& c, const void* h, const int32_t* offs,
