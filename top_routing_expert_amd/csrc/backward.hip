@@ -112,11 +112,13 @@ __device__ __forceinline__ uint32_t wg_piece(int r, int p) {
 // per flop.  256 x 128: four waves of 128 x 64, a ring of three (72 KB), two
 // blocks per CU, a quarter fewer operand bytes per flop.  The larger wave
 // tiles keep one fragment set (two would not fit their registers).
-template <int TM, int TN>
+// F32OUT: C is float32 (the partial sums of a reduction split over row
+// segments), else bf16.
+template <int TM, int TN, bool F32OUT = false>
 __global__ __launch_bounds__(TN == 256 ? 512 : 256, TN == 256 ? 1 : 2) void wgrad_dma_kernel(
     const uint16_t* __restrict__ a, long lda, const uint16_t* __restrict__ b, long ldb,
     const int32_t* __restrict__ offs, int E, int rows, int M, int N, int m_tiles, int n_tiles,
-    uint16_t* __restrict__ c, long ldc, long c_estride) {
+    void* __restrict__ c, long ldc, long c_estride) {
   constexpr int NW = TN == 256 ? 8 : 4;        // waves
   constexpr int WN = NW / 2;                   // waves along N; two along M
   constexpr int FM = TM / 64;                  // 32-column A fragments per wave
@@ -276,23 +278,31 @@ __global__ __launch_bounds__(TN == 256 ? 512 : 256, TN == 256 ? 1 : 2) void wgra
 
   // ---- epilogue: acc[i][j][4 gq + r] = C[m = wm*TM/2 + 32 i + (lane & 31)]
   // [n = wn*64 + 32 j + 8 gq + 4 (lane >> 5) + r]
-  uint16_t* cbase = c + (size_t)e * c_estride;
   const int lk = lane >> 5;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int m = wm * (TM / 2) + 32 * i + (lane & 31);
     if (m >= m_lim) continue;
-    uint16_t* crow = cbase + (size_t)(m0 + m) * ldc + n0;
+    const size_t crow = (size_t)e * c_estride + (size_t)(m0 + m) * ldc + n0;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int n = wn * 64 + 32 * j + 8 * gq + 4 * lk;
         if (n >= n_lim) continue;
-        u32x2 pk;
-        pk.x = pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]);
-        pk.y = pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
-        *reinterpret_cast<u32x2*>(crow + n) = pk;
+        if constexpr (F32OUT) {
+          float4 v;
+          v.x = acc[i][j][4 * gq];
+          v.y = acc[i][j][4 * gq + 1];
+          v.z = acc[i][j][4 * gq + 2];
+          v.w = acc[i][j][4 * gq + 3];
+          *reinterpret_cast<float4*>(static_cast<float*>(c) + crow + n) = v;
+        } else {
+          u32x2 pk;
+          pk.x = pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]);
+          pk.y = pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(c) + crow + n) = pk;
+        }
       }
   }
 }
@@ -841,11 +851,56 @@ hipError_t launch_ffn_backward(const moe_config& c, const void* x_perm, const in
                       static_cast<uint16_t*>(d_wu), d, (long)f * d, st);
 }
 
+// dWr = dz^T x has only E output rows and a reduction over all T tokens:
+// its 128 x 128 tiles are few (E = 16, d = 5120: 40), each with a long k
+// loop.  The reduction is split over S row segments so that S times the
+// tiles fill the chip about twice; each segment's tile writes float32
+// partial sums and router_split_sum_kernel adds the S partials (segment
+// order, float32) and rounds once to bf16.  S = 1 keeps the direct path.
+constexpr int kRouterMaxSplit = 16;
+constexpr int kRouterMinSegRows = 64;
+static int router_wgrad_split(const moe_config& c) {
+  const long tiles = (long)div_up(c.E, 128) * div_up(c.d, 128);
+  const long want = div_up(2L * kCUs, tiles);
+  const long cap = std::min<long>(kRouterMaxSplit, c.T / kRouterMinSegRows);
+  return (int)std::max<long>(1, std::min(want, cap));
+}
+
+__global__ void split_offsets_kernel(int32_t* __restrict__ offs, int S, int T) {
+  const int s = threadIdx.x;
+  if (s <= S) offs[s] = (int)((long)s * T / S);
+}
+
+// out[i] = bf16(part[0][i] + part[1][i] + ... + part[S-1][i]), 4 per thread.
+__global__ __launch_bounds__(256) void router_split_sum_kernel(const float4* __restrict__ part,
+                                                               int S, long n4,
+                                                               u32x2* __restrict__ out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float4 acc = part[i];
+  for (int s = 1; s < S; ++s) {
+    const float4 v = part[(long)s * n4 + i];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  u32x2 o;
+  o.x = pack_bf16x2(acc.x, acc.y);
+  o.y = pack_bf16x2(acc.z, acc.w);
+  out[i] = o;
+}
+
+static size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+// dz (bf16) | {0, T} | d_bias chunk partials | split offsets | dWr partials
 size_t route_backward_ws_bytes(const moe_config& c) {
-  const size_t dzb = ((size_t)c.T * c.E * sizeof(uint16_t) + 255) / 256 * 256;
+  const size_t dzb = round256((size_t)c.T * c.E * sizeof(uint16_t));
   const int T1 = c.T > 0 ? c.T : 1;
-  const size_t part = (size_t)div_up(T1, bias_chunk_rows(T1)) * c.E * sizeof(float);
-  return dzb + 256 + part;
+  const size_t part = round256((size_t)div_up(T1, bias_chunk_rows(T1)) * c.E * sizeof(float));
+  const int S = router_wgrad_split(c);
+  const size_t split = S > 1 ? 256 + (size_t)S * c.E * c.d * sizeof(float) : 0;
+  return dzb + 256 + part + split;
 }
 
 hipError_t launch_route_backward(const moe_config& c, const void* x, const void* w_router,
@@ -858,6 +913,9 @@ hipError_t launch_route_backward(const moe_config& c, const void* x, const void*
   const size_t dzb_bytes = ((size_t)T * E * sizeof(uint16_t) + 255) / 256 * 256;
   int32_t* offs = reinterpret_cast<int32_t*>(wsb + dzb_bytes);  // {0, T}
   float* part = reinterpret_cast<float*>(wsb + dzb_bytes + 256);
+  const int T1 = T > 0 ? T : 1;
+  char* split_base =
+      wsb + dzb_bytes + 256 + round256((size_t)div_up(T1, bias_chunk_rows(T1)) * E * sizeof(float));
   hipError_t err;
   if (T > 0) {
     const dim3 grid(div_up(T, 4));
@@ -892,8 +950,23 @@ hipError_t launch_route_backward(const moe_config& c, const void* x, const void*
       return err;
   }
   // dWr = dz^T x   [E, d]
-  return launch_wgrad(dzb, E, static_cast<const uint16_t*>(x), d, offs, 1, T, E, d,
-                      static_cast<uint16_t*>(d_w_router), d, 0, st);
+  const int S = router_wgrad_split(c);
+  if (S == 1)
+    return launch_wgrad(dzb, E, static_cast<const uint16_t*>(x), d, offs, 1, T, E, d,
+                        static_cast<uint16_t*>(d_w_router), d, 0, st);
+  int32_t* soffs = reinterpret_cast<int32_t*>(split_base);  // S + 1 <= 64 entries
+  float* rpart = reinterpret_cast<float*>(split_base + 256);
+  split_offsets_kernel<<<1, 64, 0, st>>>(soffs, S, T);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const int mt = div_up(E, 128), nt = div_up(d, 128);
+  wgrad_dma_kernel<128, 128, true><<<S * mt * nt, 256, 0, st>>>(
+      dzb, E, static_cast<const uint16_t*>(x), d, soffs, S, T, E, d, mt, nt, rpart, d,
+      (long)E * d);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  const long n4 = (long)E * d / 4;
+  router_split_sum_kernel<<<div_up(n4, 256), 256, 0, st>>>(
+      reinterpret_cast<const float4*>(rpart), S, n4, static_cast<u32x2*>(d_w_router));
+  return hipGetLastError();
 }
 
 hipError_t launch_unpermute_backward(const moe_config& c, const void* d_x_perm,
