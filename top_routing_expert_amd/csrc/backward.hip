@@ -279,37 +279,46 @@ __global__ __launch_bounds__(TN == 256 ? 512 : 256, TN == 256 ? 1 : 2) void wgra
   // ---- epilogue: acc[i][j][4 gq + r] = C[m = wm*TM/2 + 32 i + (lane & 31)]
   // [n = wn*64 + 32 j + 8 gq + 4 (lane >> 5) + r]
   const int lk = lane >> 5;
-  if constexpr (!F32OUT && TN == 128) {
+  if constexpr (!F32OUT) {
     // Staged through the (drained) ring: rows of TN bf16 padded to a 16-byte
-    // multiple, then every lane stores one 16-byte piece, 16 lanes per row,
-    // so a wave writes four whole rows per store instead of 16 bytes in each
-    // of 32 rows.
+    // multiple, then every lane stores one 16-byte piece, TN / 8 lanes per
+    // row, so a wave writes whole rows instead of 16 bytes in each of 32
+    // rows.  A tile that does not fit the ring goes in two halves of rows
+    // (the waves with wm = 0, then those with wm = 1).
     constexpr int PITCH = TN * 2 + 16;
     constexpr int PPR = TN / 8;  // 16-byte pieces per row
-    static_assert(TM * PITCH <= RING * STB, "the staged tile fits the ring");
-    __syncthreads();  // every wave is done reading the ring
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int m = wm * (TM / 2) + 32 * i + (lane & 31);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = wn * 64 + 32 * j + 8 * gq + 4 * lk;
-          u32x2 pk;
-          pk.x = pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]);
-          pk.y = pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
-          *reinterpret_cast<u32x2*>(ring + m * PITCH + n * 2) = pk;
-        }
-    }
-    __syncthreads();
+    constexpr int HALVES = TM * PITCH <= RING * STB ? 1 : 2;
+    constexpr int RH = TM / HALVES;  // rows per pass
+    static_assert(RH * PITCH <= RING * STB, "the staged rows fit the ring");
     uint16_t* cb = static_cast<uint16_t*>(c) + (size_t)e * c_estride + (size_t)m0 * ldc + n0;
     const int p = tid % PPR;
+    __syncthreads();  // every wave is done reading the ring
+#pragma unroll
+    for (int hv = 0; hv < HALVES; ++hv) {
+      if (HALVES == 1 || wm == hv) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int m = wm * (TM / 2) + 32 * i + (lane & 31) - hv * RH;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int n = wn * 64 + 32 * j + 8 * gq + 4 * lk;
+              u32x2 pk;
+              pk.x = pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]);
+              pk.y = pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
+              *reinterpret_cast<u32x2*>(ring + m * PITCH + n * 2) = pk;
+            }
+        }
+      }
+      __syncthreads();
 #pragma unroll 4
-    for (int r = tid / PPR; r < TM; r += NW * 64 / PPR)
-      if (r < m_lim && 8 * p < n_lim)
-        *reinterpret_cast<u32x4*>(cb + (size_t)r * ldc + 8 * p) =
-            *reinterpret_cast<const u32x4*>(ring + r * PITCH + 16 * p);
+      for (int r = tid / PPR; r < RH; r += NW * 64 / PPR)
+        if (hv * RH + r < m_lim && 8 * p < n_lim)
+          *reinterpret_cast<u32x4*>(cb + (size_t)(hv * RH + r) * ldc + 8 * p) =
+              *reinterpret_cast<const u32x4*>(ring + r * PITCH + 16 * p);
+      if (hv + 1 < HALVES) __syncthreads();  // the next half overwrites these rows
+    }
     return;
   }
 #pragma unroll
