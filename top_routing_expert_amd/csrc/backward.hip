@@ -504,24 +504,34 @@ __global__ __launch_bounds__(256, 2) void dgrad_dma_kernel(GemmArgs g) {
     }
   }
 
-  // ---- epilogue: C[row m0 + m][n0 + n]
+  // ---- epilogue: C[row m0 + m][n0 + n], staged through the drained ring
+  // like the wgrad's (rows padded to 272 bytes), then 16 lanes per row store
+  // it in 16-byte pieces.
+  constexpr int PITCH = WT * 2 + 16;
+  static_assert(WT * PITCH <= kWRing * STB, "the staged tile fits the ring");
+  __syncthreads();  // every wave is done reading the ring
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int m = wm * 64 + 32 * i + (lane & 31);
-    if (m >= m_lim) continue;
-    uint16_t* crow = g.c + (size_t)(m0 + m) * g.ldc + n0;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int n = wn * 64 + 32 * j + 8 * gq + 4 * lk;
-        if (n >= n_lim) continue;
         u32x2 pk;
         pk.x = pack_bf16x2(acc[i][j][4 * gq], acc[i][j][4 * gq + 1]);
         pk.y = pack_bf16x2(acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
-        *reinterpret_cast<u32x2*>(crow + n) = pk;
+        *reinterpret_cast<u32x2*>(ring + m * PITCH + n * 2) = pk;
       }
   }
+  __syncthreads();
+  uint16_t* cb = g.c + (size_t)m0 * g.ldc + n0;
+  const int p = tid % (WT / 8);
+#pragma unroll 4
+  for (int r = tid / (WT / 8); r < WT; r += 256 / (WT / 8))
+    if (r < m_lim && 8 * p < n_lim)
+      *reinterpret_cast<u32x4*>(cb + (size_t)r * g.ldc + 8 * p) =
+          *reinterpret_cast<const u32x4*>(ring + r * PITCH + 16 * p);
 }
 
 // dgrad: C[rows, N] = A[rows, K] B_e[K, N] (+ the second part), by expert
