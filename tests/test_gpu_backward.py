@@ -201,6 +201,16 @@ def test_layer_backward_on_packed_transposed_weights(key):
     _check(shape, seed=13, packed=True)
 
 
+@pytest.mark.parametrize("T", [127, 128, 200])
+def test_router_gradient_split_boundary(T):
+    """The router weight gradient dz^T x is summed over row segments of at
+    least 64 tokens with float32 partials: T = 127 keeps one segment (the
+    direct bf16 path), 128 and 200 take two and three (the last ragged)."""
+    shape = C.SMALL["e16"].replace(name=f"bwd-split-T{T}", T=T)
+    log(f"[backward] {shape.name}")
+    _check(shape, seed=19)
+
+
 def test_packed_transposed_images_ragged_f():
     """f = 320 (not a whole 256-feature slab for dh, a ragged 128-wide k
     iteration for d_x_perm's k = 2 f = 640) and d = 1088: the images' zero
