@@ -597,6 +597,11 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return v;
 }
 
+// One wave per token.  VR > 0 (rows of up to 64 VR vectors): the token's
+// d_out row stays in registers and each chosen row's vectors are all loaded
+// before they are used; VR = 0: one vector at a time.  Either way a lane
+// accumulates its dot product over the same vectors in the same order.
+template <int VR>
 __global__ __launch_bounds__(256) void combine_backward_kernel(
     const u32x4* __restrict__ dout, const u32x4* __restrict__ y, const int32_t* __restrict__ slot_of,
     const float* __restrict__ topk_w, u32x4* __restrict__ dy, float* __restrict__ dg, int T, int k,
@@ -605,26 +610,49 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave
   const u32x4* drow = dout + (size_t)t * nvec;
-  for (int j = 0; j < k; ++j) {
-    const int p = min(max(slot_of[(size_t)t * k + j], 0), A - 1);
-    const float w = topk_w[(size_t)t * k + j];
-    const u32x4* yrow = y + (size_t)p * nvec;
-    u32x4* dyrow = dy + (size_t)p * nvec;
-    float dot = 0.f;
-    for (int v = lane; v < nvec; v += 64) {
-      const u32x4 a = drow[v], b = yrow[v];
-      u32x4 o;
+  auto body = [&](const u32x4& a, const u32x4& b, float w, float& dot) {
+    u32x4 o;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float a0 = bf16_lo(a[q]), a1 = bf16_hi(a[q]);
-        dot = fmaf(a0, bf16_lo(b[q]), dot);
-        dot = fmaf(a1, bf16_hi(b[q]), dot);
-        o[q] = pack_bf16x2(w * a0, w * a1);
-      }
-      dyrow[v] = o;
+    for (int q = 0; q < 4; ++q) {
+      const float a0 = bf16_lo(a[q]), a1 = bf16_hi(a[q]);
+      dot = fmaf(a0, bf16_lo(b[q]), dot);
+      dot = fmaf(a1, bf16_hi(b[q]), dot);
+      o[q] = pack_bf16x2(w * a0, w * a1);
     }
-    dot = wave_sum_f(dot);
-    if (lane == 0) dg[(size_t)t * k + j] = dot;
+    return o;
+  };
+  if constexpr (VR > 0) {
+    u32x4 a[VR];
+#pragma unroll
+    for (int i = 0; i < VR; ++i)
+      if (lane + 64 * i < nvec) a[i] = drow[lane + 64 * i];
+    for (int j = 0; j < k; ++j) {
+      const int p = min(max(slot_of[(size_t)t * k + j], 0), A - 1);
+      const float w = topk_w[(size_t)t * k + j];
+      const u32x4* yrow = y + (size_t)p * nvec;
+      u32x4* dyrow = dy + (size_t)p * nvec;
+      u32x4 b[VR];
+#pragma unroll
+      for (int i = 0; i < VR; ++i)
+        if (lane + 64 * i < nvec) b[i] = yrow[lane + 64 * i];
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < VR; ++i)
+        if (lane + 64 * i < nvec) dyrow[lane + 64 * i] = body(a[i], b[i], w, dot);
+      dot = wave_sum_f(dot);
+      if (lane == 0) dg[(size_t)t * k + j] = dot;
+    }
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const int p = min(max(slot_of[(size_t)t * k + j], 0), A - 1);
+      const float w = topk_w[(size_t)t * k + j];
+      const u32x4* yrow = y + (size_t)p * nvec;
+      u32x4* dyrow = dy + (size_t)p * nvec;
+      float dot = 0.f;
+      for (int v = lane; v < nvec; v += 64) dyrow[v] = body(drow[v], yrow[v], w, dot);
+      dot = wave_sum_f(dot);
+      if (lane == 0) dg[(size_t)t * k + j] = dot;
+    }
   }
 }
 
@@ -815,9 +843,19 @@ hipError_t launch_combine_backward(const moe_config& c, const void* d_out, const
                                    const int32_t* slot_of, const float* topk_w, void* d_y_perm,
                                    float* d_topk_w, hipStream_t st) {
   const int nvec = c.d / 8;
-  combine_backward_kernel<<<div_up(c.T, 4), 256, 0, st>>>(
-      static_cast<const u32x4*>(d_out), static_cast<const u32x4*>(y_perm), slot_of, topk_w,
-      static_cast<u32x4*>(d_y_perm), d_topk_w, c.T, c.k, nvec, c.T * c.k);
+  const auto* dout = static_cast<const u32x4*>(d_out);
+  const auto* y = static_cast<const u32x4*>(y_perm);
+  auto* dy = static_cast<u32x4*>(d_y_perm);
+  const int blocks = div_up(c.T, 4), A = c.T * c.k;
+  if (nvec <= 64 * 4)
+    combine_backward_kernel<4><<<blocks, 256, 0, st>>>(dout, y, slot_of, topk_w, dy, d_topk_w,
+                                                       c.T, c.k, nvec, A);
+  else if (nvec <= 64 * 16)
+    combine_backward_kernel<16><<<blocks, 256, 0, st>>>(dout, y, slot_of, topk_w, dy, d_topk_w,
+                                                        c.T, c.k, nvec, A);
+  else
+    combine_backward_kernel<0><<<blocks, 256, 0, st>>>(dout, y, slot_of, topk_w, dy, d_topk_w,
+                                                       c.T, c.k, nvec, A);
   return hipGetLastError();
 }
 
