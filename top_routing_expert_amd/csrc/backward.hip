@@ -801,7 +801,10 @@ __global__ __launch_bounds__(256) void bias_final_kernel(const float* __restrict
 
 // ------------------------------------------------------------- dispatch backward
 // One wave per token: dx[t] = sum_j dx_perm[p(t,j)] (+ dx_router[t]), fp32 in
-// j order, one bf16 rounding.
+// j order, one bf16 rounding.  KU > 0 (k <= KU): the k row bases are read
+// once and the k loads of a vector are issued together; KU = 0: one row at a
+// time.  The sum runs in the same order either way.
+template <int KU>
 __global__ __launch_bounds__(256) void unpermute_sum_kernel(const u32x4* __restrict__ dxp,
                                                             const int32_t* __restrict__ slot_of,
                                                             const u32x4* __restrict__ dxr,
@@ -810,27 +813,38 @@ __global__ __launch_bounds__(256) void unpermute_sum_kernel(const u32x4* __restr
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  auto add = [](float* acc, const u32x4& r) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] += bf16_lo(r[q]);
+      acc[2 * q + 1] += bf16_hi(r[q]);
+    }
+  };
+  size_t base[KU > 0 ? KU : 1];
+  if constexpr (KU > 0) {
+#pragma unroll
+    for (int j = 0; j < KU; ++j)
+      base[j] = j < k ? (size_t)min(max(slot_of[(size_t)t * k + j], 0), A - 1) * nvec : 0;
+  }
   for (int v = lane; v < nvec; v += 64) {
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int p = min(max(slot_of[(size_t)t * k + j], 0), A - 1);
-      const u32x4 r = dxp[(size_t)p * nvec + v];
+    if constexpr (KU > 0) {
+      u32x4 r[KU];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += bf16_lo(r[q]);
-        acc[2 * q + 1] += bf16_hi(r[q]);
+      for (int j = 0; j < KU; ++j)
+        if (j < k) r[j] = dxp[base[j] + v];
+#pragma unroll
+      for (int j = 0; j < KU; ++j)
+        if (j < k) add(acc, r[j]);
+    } else {
+      for (int j = 0; j < k; ++j) {
+        const int p = min(max(slot_of[(size_t)t * k + j], 0), A - 1);
+        add(acc, dxp[(size_t)p * nvec + v]);
       }
     }
-    if (dxr) {
-      const u32x4 r = dxr[(size_t)t * nvec + v];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += bf16_lo(r[q]);
-        acc[2 * q + 1] += bf16_hi(r[q]);
-      }
-    }
+    if (dxr) add(acc, dxr[(size_t)t * nvec + v]);
     u32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
@@ -1063,9 +1077,16 @@ hipError_t launch_unpermute_backward(const moe_config& c, const void* d_x_perm,
                                      const int32_t* slot_of, const void* d_x_router, void* d_x,
                                      hipStream_t st) {
   const int nvec = c.d / 8;
-  unpermute_sum_kernel<<<div_up(c.T, 4), 256, 0, st>>>(
-      static_cast<const u32x4*>(d_x_perm), slot_of, static_cast<const u32x4*>(d_x_router),
-      static_cast<u32x4*>(d_x), c.T, c.k, nvec, c.T * c.k);
+  const auto* dxp = static_cast<const u32x4*>(d_x_perm);
+  const auto* dxr = static_cast<const u32x4*>(d_x_router);
+  auto* dx = static_cast<u32x4*>(d_x);
+  const int blocks = div_up(c.T, 4), A = c.T * c.k;
+  // the batched loads pay off for k <= 2 (T1024-E8: 29 -> 17 us); at k = 8
+  // (T8192-E256) they measured 5 % slower than one row at a time
+  if (c.k <= 2)
+    unpermute_sum_kernel<2><<<blocks, 256, 0, st>>>(dxp, slot_of, dxr, dx, c.T, c.k, nvec, A);
+  else
+    unpermute_sum_kernel<0><<<blocks, 256, 0, st>>>(dxp, slot_of, dxr, dx, c.T, c.k, nvec, A);
   return hipGetLastError();
 }
 
