@@ -9,6 +9,7 @@ SiLU/matmul), exact identities, and the pages' size/statistics statements.
 import json
 import math
 import os
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -382,6 +383,79 @@ def pin_fp8_row_quantization():
     assert np.all(np.abs(xr - xf) <= hr[:, None] / 16 + np.abs(xf) * 2.0 ** -8 + 1e-30)
 
 
+def pin_router_logits_hand_case():
+    """z = x Wr^T on a hand-worked case whose last logit needs 33 significant
+    bits (exact in float64, rounded by any float32 accumulation), given both
+    as float64 values and as the bf16 bit patterns of the same values."""
+    g = _golden("router_logits_case.json")
+    want = np.array(g["z"], dtype=np.float64)
+    z = om.router_logits(np.array(g["x"]), np.array(g["w_router"]))
+    assert z.shape == want.shape and np.array_equal(z, want), z
+    zb = om.router_logits(np.array(g["x_bf16_bits"], np.uint16),
+                          np.array(g["w_router_bf16_bits"], np.uint16))
+    assert np.array_equal(zb, want), zb
+
+
+def _bf16_values_torch(bits):
+    """bf16 bit patterns -> float64 through torch's own bfloat16 type (not the
+    oracle's widening)."""
+    t = torch.from_numpy(np.ascontiguousarray(np.asarray(bits, np.uint16)).view(np.int16).copy())
+    return t.view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _random_bf16_bits(rng, shape, spread=12):
+    """bf16 bit patterns of values with random signs, exponents over `spread`
+    binades and all 7 mantissa bits set at random."""
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint16) << 15
+    expo = (127 - spread // 2 + rng.integers(0, spread, size=shape)).astype(np.uint16) << 7
+    mant = rng.integers(0, 128, size=shape, dtype=np.uint16)
+    return (sign | expo | mant).astype(np.uint16)
+
+
+def pin_router_logits_exact_sum():
+    """Every logit against its exact rational value (brute-force triple loop
+    in Fractions), within the float64 summation bound d u sum|x w|."""
+    rng = np.random.default_rng(40)
+    T, E, d = 6, 5, 9
+    xb, wb = _random_bf16_bits(rng, (T, d)), _random_bf16_bits(rng, (E, d))
+    xv, wv = _bf16_values_torch(xb), _bf16_values_torch(wb)
+    z = om.router_logits(xb, wb)
+    for t in range(T):
+        for e in range(E):
+            exact = sum(Fraction(float(xv[t, i])) * Fraction(float(wv[e, i])) for i in range(d))
+            bound = d * 2.0 ** -53 * float(np.sum(np.abs(xv[t] * wv[e])))
+            assert abs(Fraction(float(z[t, e])) - exact) <= Fraction(bound), (t, e)
+
+
+def pin_bf16_bit_patterns_are_their_values():
+    """Every bf16 workload feeds the oracle uint16 bit patterns.  Routing,
+    FFN, combine and the whole layer must give exactly what they give on the
+    same numbers widened by torch's bfloat16 type and passed as float64."""
+    rng = np.random.default_rng(41)
+    T, d, f = 40, 16, 24
+    for m in ROUTING_MODES:
+        E = m["E"]
+        bits = dict(x=_random_bf16_bits(rng, (T, d), 6),
+                    w_router=_random_bf16_bits(rng, (E, d), 6),
+                    w_gate=_random_bf16_bits(rng, (E, f, d), 6),
+                    w_up=_random_bf16_bits(rng, (E, f, d), 6),
+                    w_down=_random_bf16_bits(rng, (E, d, f), 6))
+        vals = {n: _bf16_values_torch(b) for n, b in bits.items()}
+        b = rng.standard_normal(E).astype(np.float32) if m.get("bias") else None
+        rb = om.layer(bits["x"], bits["w_router"], b, bits["w_gate"], bits["w_up"],
+                      bits["w_down"], **_mode_kw(m))
+        rv = om.layer(vals["x"], vals["w_router"], b, vals["w_gate"], vals["w_up"],
+                      vals["w_down"], **_mode_kw(m))
+        for n in ("logits", "topk_idx", "topk_w", "h", "y_perm", "out"):
+            assert np.array_equal(rb[n], rv[n]), (m, n)
+        assert np.array_equal(_bf16_values_torch(rb["x_perm"]), rv["x_perm"]), m
+        # the combine alone on bf16 expert outputs
+        yb = _random_bf16_bits(rng, (T * m["k"], d), 6)
+        cb = om.combine(yb, rb["slot_of"], rb["topk_w"])
+        cv = om.combine(_bf16_values_torch(yb), rb["slot_of"], rb["topk_w"])
+        assert np.array_equal(cb, cv), m
+
+
 def pin_widen_bf16():
     bits = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x4049, 0x7F7F], np.uint16)
     got = om.widen_bf16(bits)
@@ -624,6 +698,19 @@ def _scatter_bwd_first_row_only(dx_perm, src_of, k, T):
     return dx
 
 
+def _router_logits_fp32_accumulate(x, w_router):
+    return (om._f64(x).astype(np.float32) @ om._f64(w_router).astype(np.float32).T).astype(np.float64)
+
+
+def _router_logits_scaled(x, w_router):
+    xf = om._f64(x)
+    return (xf @ om._f64(w_router).T) / math.sqrt(xf.shape[1])
+
+
+def _f64_without_widening(a):
+    return np.asarray(a).astype(np.float64)
+
+
 _ORIG_EXPERT_BWD = om.expert_ffn_backward
 _ORIG_GATES_BWD = om.gates_backward
 _ORIG_COMBINE_BWD = om.combine_backward
@@ -648,6 +735,9 @@ MUTANTS = {
     "bwd-softmax-sign": ("gates_backward", _gates_bwd_sign),
     "bwd-combine-without-gate": ("combine_backward", _combine_bwd_no_gate),
     "bwd-dispatch-first-copy-only": ("scatter_rows_backward", _scatter_bwd_first_row_only),
+    "logits-fp32-accumulation": ("router_logits", _router_logits_fp32_accumulate),
+    "logits-scaled-by-sqrt-d": ("router_logits", _router_logits_scaled),
+    "bf16-bits-not-widened": ("_f64", _f64_without_widening),
 }
 
 
