@@ -48,6 +48,7 @@ __all__ = [
     "permute", "silu", "expert_ffn", "grouped_ffn", "combine", "layer",
     "select_bruteforce", "dense_bruteforce", "combine_backward", "expert_ffn_backward",
     "grouped_ffn_backward", "scatter_rows_backward", "gates_backward", "layer_backward",
+    "swiglu_backward",
 ]
 
 
@@ -456,6 +457,16 @@ def combine_backward(d_out, y_perm, slot_of, topk_w):
     return dy, dg
 
 
+def swiglu_backward(a, u, dh):
+    """The activation step of the expert's backward: h = SiLU(a) * u, so a
+    gradient dh gives da = dh * u * SiLU'(a) and du = dh * SiLU(a), with
+    SiLU'(a) = sig(a) (1 + a (1 - sig(a))).  Returns (h, da, du), float64."""
+    a, u, dh = _f64(a), _f64(u), _f64(dh)
+    sig = 1.0 / (1.0 + np.exp(-a))
+    h = a * sig * u
+    return h, dh * u * sig * (1.0 + a * (1.0 - sig)), dh * a * sig
+
+
 def expert_ffn_backward(X, w_gate_e, w_up_e, w_down_e, dY):
     """Backward of y = (SiLU(a) * u) Wd^T with a = X Wg^T, u = X Wu^T:
     each product C = A B gives dA = dC B^T and dB = A^T dC ([V4-overlap], PP
@@ -465,12 +476,9 @@ def expert_ffn_backward(X, w_gate_e, w_up_e, w_down_e, dY):
     X, Wg, Wu, Wd, dY = (_f64(v) for v in (X, w_gate_e, w_up_e, w_down_e, dY))
     a = X @ Wg.T
     u = X @ Wu.T
-    sig = 1.0 / (1.0 + np.exp(-a))
-    h = a * sig * u
     dh = dY @ Wd                      # y = h Wd^T
+    h, da, du = swiglu_backward(a, u, dh)
     dWd = dY.T @ h
-    da = dh * u * sig * (1.0 + a * (1.0 - sig))
-    du = dh * a * sig
     dX = da @ Wg + du @ Wu
     dWg = da.T @ X
     dWu = du.T @ X

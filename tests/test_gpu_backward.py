@@ -378,3 +378,144 @@ def test_backward_long_reductions_take_the_wide_wgrad_tiles():
     assert shape.E * (shape.d // 256) * (shape.f // 256) >= 256
     log(f"[backward] {shape.name}")
     _check(shape, seed=11)
+
+
+# ---------------------------------------------------------------------------
+# Stage by stage: each backward step against the oracle fed the GPU's own bf16
+# inputs of that step, element by element.  Every stage output is one bf16
+# rounding (relative 2^-9) of a float32 result computed from those inputs, so
+# the elementwise bound max|got - want| / max(|want|, rms) is a few 2^-9 at
+# most: STAGE_TOL = 2e-2.  The FFN backward's intermediates are read from its
+# workspace after the call (a | u | dh then h | da, du side by side per row).
+STAGE_TOL = 2e-2
+
+
+def _per_expert_err(got, want, offs, rows_fn):
+    """Largest rel_err over the experts with rows (weight gradients: rms per expert)."""
+    errs = []
+    for e in range(len(offs) - 1):
+        if offs[e + 1] > offs[e]:
+            errs.append(rel_err(got[e], rows_fn(e)))
+    return max(errs, default=0.0)
+
+
+def _stage_check(shape, seed, experts=None):
+    """Training forward (packed weights, saved a and u), then the four
+    backward entry points (packed transposed images); every stage against the
+    oracle on the GPU's own inputs of that stage.  `experts`: the experts whose
+    weight gradients are checked (default all)."""
+    inp = I.make_inputs(shape, seed=seed)
+    dout_bits = I.make_grad_out(shape, seed)
+    dev, buf = upload(inp), alloc(shape)
+    cfg = B.config(shape)
+    T, d, E, k, f = shape.T, shape.d, shape.E, shape.k, shape.f
+    A = T * k
+    B.moe_route(cfg, dev["x"], dev["w_router"], dev["bias"], buf["logits"], buf["topk_idx"],
+                buf["topk_w"], B.workspace(cfg, "route"))
+    B.moe_permute(cfg, dev["x"], buf["topk_idx"], buf["expert_offsets"], buf["rank_offsets"],
+                  buf["slot_of"], buf["src_of"], buf["x_perm"], B.workspace(cfg, "permute"))
+    pgu, pd = B.pack_weights(cfg, dev["w_gate"], dev["w_up"], dev["w_down"])
+    a = torch.empty((A, f), dtype=torch.bfloat16, device="cuda")
+    u = torch.empty_like(a)
+    B.moe_ffn_gate_up_packed_train(cfg, buf["x_perm"], None, buf["expert_offsets"], pgu,
+                                   buf["h"], a, u)
+    B.moe_ffn_down_packed(cfg, buf["h"], buf["expert_offsets"], pd, buf["y_perm"])
+    B.moe_combine(cfg, buf["y_perm"], buf["slot_of"], buf["topk_w"], buf["out"])
+    del pgu, pd
+    images = B.pack_weights_backward(cfg, dev["w_gate"], dev["w_up"], dev["w_down"])
+    ws = B.workspace(cfg, "ffn_backward")
+    dout = B.to_device(dout_bits)
+    bf, f32 = torch.bfloat16, torch.float32
+    g = {n: torch.full(s, 3.0, dtype=t, device="cuda") for n, s, t in (
+        ("d_y_perm", (A, d), bf), ("d_topk_w", (T, k), f32), ("d_x_perm", (A, d), bf),
+        ("d_w_gate", (E, f, d), bf), ("d_w_up", (E, f, d), bf), ("d_w_down", (E, d, f), bf),
+        ("d_logits", (T, E), f32), ("d_x_router", (T, d), bf), ("d_w_router", (E, d), bf),
+        ("d_bias", (E,), f32), ("d_x", (T, d), bf))}
+    B.moe_combine_backward(cfg, dout, buf["y_perm"], buf["slot_of"], buf["topk_w"],
+                           g["d_y_perm"], g["d_topk_w"])
+    B.moe_ffn_backward(cfg, buf["x_perm"], buf["expert_offsets"], dev["w_gate"], dev["w_up"],
+                       dev["w_down"], g["d_y_perm"], g["d_x_perm"], g["d_w_gate"], g["d_w_up"],
+                       g["d_w_down"], ws, a=a, u=u, packed_dh=images[0], packed_dx=images[1])
+    B.moe_route_backward(cfg, dev["x"], dev["w_router"], buf["logits"], dev["bias"],
+                         buf["topk_idx"], g["d_topk_w"], g["d_logits"], g["d_x_router"],
+                         g["d_w_router"], g["d_bias"], B.workspace(cfg, "route_backward"))
+    B.moe_unpermute_backward(cfg, g["d_x_perm"], buf["slot_of"], g["d_x_router"], g["d_x"])
+    torch.cuda.synchronize()
+    del images
+    af = A * f
+    wsb = ws.view(torch.int16).view(torch.bfloat16)
+    h_ws = host(wsb[2 * af:3 * af].view(A, f))
+    dadu = host(wsb[3 * af:5 * af].view(A, 2 * f))
+    G = {n: host(t) for n, t in g.items()}
+    fw = {n: host(buf[n]) for n in ("logits", "topk_idx", "topk_w", "expert_offsets", "slot_of",
+                                    "src_of", "x_perm", "h", "y_perm")}
+    a_np, u_np = host(a), host(u)
+    del g, buf, a, u, ws, wsb
+    torch.cuda.empty_cache()
+    offs = fw["expert_offsets"].astype(np.int64)
+    experts = [e for e in (range(E) if experts is None else experts) if offs[e + 1] > offs[e]]
+    errs = {}
+
+    # combine backward on the forward's y_perm and gates
+    dy_ref, dg_ref = om.combine_backward(dout_bits, fw["y_perm"], fw["slot_of"], fw["topk_w"])
+    errs["d_y_perm"] = rel_err(G["d_y_perm"], dy_ref)
+    errs["d_topk_w"] = rel_err(G["d_topk_w"], dg_ref)
+    # FFN backward: the activation step on the saved a, u and the exact dh of the GPU's dy
+    dy = f64(G["d_y_perm"])
+    xp = f64(fw["x_perm"])
+    seg = [(e, int(offs[e]), int(offs[e + 1])) for e in range(E) if offs[e + 1] > offs[e]]
+    dh = np.zeros((A, f))
+    for e, r0, r1 in seg:
+        dh[r0:r1] = dy[r0:r1] @ f64(inp["w_down"][e])
+    h_ref, da_ref, du_ref = om.swiglu_backward(a_np, u_np, dh)
+    errs["h (backward's)"] = rel_err(h_ws, h_ref)
+    errs["da"] = rel_err(dadu[:, :f], da_ref)
+    errs["du"] = rel_err(dadu[:, f:], du_ref)
+    # the products on the GPU's own dy, h, da, du
+    da, du = f64(dadu[:, :f]), f64(dadu[:, f:])
+    h_b = f64(h_ws)
+    dxp = np.zeros((A, d))
+    for e, r0, r1 in seg:
+        dxp[r0:r1] = da[r0:r1] @ f64(inp["w_gate"][e]) + du[r0:r1] @ f64(inp["w_up"][e])
+    errs["d_x_perm"] = rel_err(G["d_x_perm"], dxp)
+    for name, fn in (("d_w_down", lambda r0, r1: dy[r0:r1].T @ h_b[r0:r1]),
+                     ("d_w_gate", lambda r0, r1: da[r0:r1].T @ xp[r0:r1]),
+                     ("d_w_up", lambda r0, r1: du[r0:r1].T @ xp[r0:r1])):
+        errs[name] = max(rel_err(G[name][e], fn(int(offs[e]), int(offs[e + 1])))
+                         for e in experts)
+    empty = np.flatnonzero(offs[1:] == offs[:-1])
+    for name in ("d_w_down", "d_w_gate", "d_w_up"):
+        assert np.all(G[name][empty] == 0), name
+    # router backward on the GPU's fp32 logits and gate gradients
+    kw = routing_kwargs(shape)
+    _, _, s = om.route(fw["logits"], inp["bias"], **kw)
+    sel = om.select(s, k, shape.n_group, shape.topk_group, shape.presel)
+    assert np.array_equal(sel[:, :k], fw["topk_idx"])
+    dz_ref = om.gates_backward(s, sel, G["d_topk_w"], k, shape.presel, shape.renorm)
+    errs["d_logits"] = rel_err(G["d_logits"], dz_ref)
+    dz = G["d_logits"].astype(np.float64)
+    errs["d_x_router"] = rel_err(G["d_x_router"], dz @ f64(inp["w_router"]))
+    errs["d_w_router"] = rel_err(G["d_w_router"], dz.T @ f64(inp["x"]))
+    if inp["bias"] is not None:
+        errs["d_bias"] = rel_err(G["d_bias"], dz.sum(axis=0))
+    # dispatch backward: the k rows of each token plus the router part
+    errs["d_x"] = rel_err(G["d_x"], om.scatter_rows_backward(G["d_x_perm"], fw["src_of"], k, T)
+                          + f64(G["d_x_router"]))
+    log(f"  stage errors {shape.name}: " + " ".join(f"{n}={v:.1e}" for n, v in errs.items()))
+    bad = {n: v for n, v in errs.items() if not v <= STAGE_TOL}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("key", ["e8", "e64", "e16", "e256"])
+def test_backward_stages_on_gpu_intermediates(key):
+    shape = C.SMALL[key]
+    log(f"[backward] stages {shape.name}")
+    _stage_check(shape, seed=23)
+
+
+def test_backward_stages_full_size():
+    """T1024-d4096-E8-top2-f11008 (the training step's configuration): every
+    row and every token; the weight gradients of three of the eight experts."""
+    shape = C.CONFIGS[1]
+    log(f"[backward] stages full {shape.name}")
+    _stage_check(shape, seed=2, experts=[0, 3, 7])

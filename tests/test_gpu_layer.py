@@ -8,12 +8,14 @@ Assignment flips (a token whose chosen set differs from the oracle's) are
 allowed only where the oracle's fp64 selection margin is below FLIP_MARGIN;
 they are counted and reported, left out of the value check, and re-checked
 against the oracle run on the GPU's own logits."""
+import concurrent.futures as cf
+
 import numpy as np
 import pytest
 import torch
 
-from _gpu import (FLIP_MARGIN, TOL_LAYER, alloc, f64, host, log, rel_err, routing_kwargs,
-                  run_stages, upload)
+from _gpu import (FLIP_MARGIN, GATE_TOL, TOL_LAYER, TOL_STAGE, alloc, f64, host, log, rel_err,
+                  routing_kwargs, run_stages, upload)
 from oracle import moe_oracle as om
 from top_routing_expert_amd import binding as B
 from top_routing_expert_amd import configs as C
@@ -102,69 +104,166 @@ def test_layer_empty_batch():
     torch.cuda.synchronize()
 
 
-def _sampled_outputs(shape, inp, idx, w, tokens):
-    """Oracle outputs of `tokens` with the given routing, expert by expert."""
-    d = shape.d
-    out = np.zeros((tokens.size, d))
-    need = {}
-    for r, t in enumerate(tokens):
-        for j in range(shape.k):
-            need.setdefault(int(idx[t, j]), []).append((r, t, j))
-    for e, items in need.items():
-        rows = np.array([t for _, t, _ in items])
-        y, _ = om.expert_ffn(inp["x"][rows], inp["w_gate"][e], inp["w_up"][e], inp["w_down"][e])
-        for (r, t, j), yr in zip(items, y):
-            out[r] += float(w[t, j]) * yr
-    return out
-
-
-FULL_SAMPLES = {1: 256, 2: 48, 3: 48, 4: 32, 5: 8}
-# the benchmark's layout (packed expert weights) on every bf16 workload, and
-# the plain weight layout on every workload
-FULL_CASES = [(ci, False) for ci in range(1, 6)] + [(ci, True) for ci in range(2, 6)]
-_inputs_cache = {}
+# Full size: the timed call sequence itself (bench.forward_calls), on the
+# packed expert weights with the dispatch gather inside the first GEMM (no
+# x_perm), and on the plain weights with x_perm materialised.  Checked:
+#  * the routing of every token against the oracle's float64 routing (flips
+#    only below the margin, counted and printed) and, bit for bit, against the
+#    oracle run on the GPU's own logits; the gates within 1e-4;
+#  * the dispatch layout of every token, bit for bit;
+#  * h and y_perm element by element on the first and last row of every row
+#    tile of every expert (for every tile height the kernels use) and on a
+#    random sample of rows: h against the oracle, y_perm against the oracle's
+#    down projection of the GPU's own h (one stage) and end to end;
+#  * `out` of every token on the three smaller workloads and of a sample of
+#    tokens on the two largest, against the oracle's whole layer.
+ALL_TOKENS = {1, 2, 3}
+FULL_SAMPLES = {4: 96, 5: 48}
+TILE_HEIGHTS = (128, 160, 256, 320)
+FULL_CASES = [(ci, "rowmajor") for ci in range(1, 6)] + [(ci, "packed") for ci in range(2, 6)]
+_cache = {}
 
 
 def _full_inputs(ci):
-    if ci not in _inputs_cache:
-        _inputs_cache.clear()  # one workload's inputs at a time (the largest is ~23 GB)
-        _inputs_cache[ci] = I.make_inputs(C.CONFIGS[ci - 1], seed=ci)
-    return _inputs_cache[ci]
+    key = ("inputs", ci)
+    if key not in _cache:
+        _cache.clear()  # one workload at a time (the largest holds ~23 GB of weights)
+        _cache[key] = I.make_inputs(C.CONFIGS[ci - 1], seed=ci)
+    return _cache[key]
 
 
-@pytest.mark.parametrize("ci,packed", sorted(FULL_CASES),
-                         ids=[f"{C.CONFIGS[c - 1].name}-{'packed' if p else 'rowmajor'}"
-                              for c, p in sorted(FULL_CASES)])
-def test_layer_full_size_sampled(ci, packed):
+def _tile_rows(offs, rng, extra):
+    """First and last row of every row tile of every expert, for every tile
+    height (an expert's rows are split evenly over ceil(c / TM) tiles), plus
+    `extra` random rows."""
+    rows = set()
+    for e in range(len(offs) - 1):
+        o0, o1 = int(offs[e]), int(offs[e + 1])
+        c = o1 - o0
+        for tm in TILE_HEIGHTS:
+            mt = -(-c // tm)
+            for m in range(mt):
+                r0, r1 = o0 + m * c // mt, o0 + (m + 1) * c // mt
+                rows.update((r0, r1 - 1))
+    A = int(offs[-1])
+    rows.update(rng.choice(A, size=min(A, extra), replace=False).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < A), dtype=np.int64)
+
+
+def _per_expert(offs, rows, fn):
+    """fn(e, positions of `rows` in expert e) for every expert holding some of
+    the rows, on a few threads (numpy releases the GIL in its array work)."""
+    ex = np.searchsorted(offs, rows, side="right") - 1
+    with cf.ThreadPoolExecutor(8) as pool:
+        list(pool.map(lambda e: fn(int(e), np.flatnonzero(ex == e)), np.unique(ex)))
+
+
+def _oracle_rows(shape, inp, offs, src_of, rows):
+    """Oracle h and y (float64) of the given expert-ordered rows, expert by expert."""
+    k = shape.k
+    h = np.zeros((rows.size, shape.f))
+    y = np.zeros((rows.size, shape.d))
+
+    def one(e, sel):
+        xr = inp["x"][src_of[rows[sel]] // k]
+        y[sel], h[sel] = om.expert_ffn(xr, inp["w_gate"][e], inp["w_up"][e], inp["w_down"][e])
+
+    _per_expert(offs, rows, one)
+    return h, y
+
+
+@pytest.mark.parametrize("ci,mode", sorted(FULL_CASES),
+                         ids=[f"{C.CONFIGS[c - 1].name}-{m}" for c, m in sorted(FULL_CASES)])
+def test_layer_full_size(ci, mode):
+    import bench
     shape = C.CONFIGS[ci - 1]
-    log(f"[layer] full {shape.name} ({'packed' if packed else 'row-major'} weights): inputs")
+    log(f"[layer] full {shape.name} ({mode}): inputs")
     inp = _full_inputs(ci)
-    log("  uploading")
-    dev, buf = upload(inp), alloc(shape)
-    log("  moe_layer_fwd" + ("_packed" if packed else ""))
-    _layer_fwd(shape, dev, buf, bufs=True, packed=packed)
-    del dev
-    idx, w_gpu, out = host(buf["topk_idx"]), host(buf["topk_w"]), host(buf["out"])
-    # routing of every token
-    log("  oracle routing")
+    log("  uploading, packing")
+    ctx = bench.prepare(shape, inp, ffn=mode, dispatch="gather")
+    assert (ctx["ffn"], ctx["dispatch"]) == bench.modes_for(shape, mode, "gather")
+    calls = bench.forward_calls(ctx)
+    log(f"  {' -> '.join(calls)} ({ctx['ffn']}, {ctx['dispatch']})")
+    for call in calls.values():
+        call()
+    torch.cuda.synchronize()
+    buf = ctx["buf"]
+    got = {n: host(buf[n]) for n in ("logits", "topk_idx", "topk_w", "expert_offsets",
+                                     "rank_offsets", "slot_of", "src_of", "h", "y_perm", "out")}
+    if ctx["dispatch"] == "gather":
+        # the whole-layer entry point takes the same gather branch and gives the same bits
+        out2 = torch.empty_like(buf["out"])
+        pgu, pd = ctx["packed"]
+        B.moe_layer_fwd_packed(ctx["cfg"], ctx["dev"]["x"], ctx["dev"]["w_router"],
+                               ctx["dev"]["bias"], pgu, pd, out2, None,
+                               B.workspace(ctx["cfg"], "layer"))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out2), got["out"]), "moe_layer_fwd_packed (gather) != staged"
+    del ctx, calls, buf
+    torch.cuda.empty_cache()
+    idx, w_gpu = got["topk_idx"], got["topk_w"]
+
+    # routing of every token against the oracle's float64 routing
     flip, margin, o_idx, o_w = _flips(shape, inp, idx)
+    log(f"  flips={int(flip.sum())} of {shape.T} (near-ties {int((margin < FLIP_MARGIN).sum())})")
     assert np.all(margin[flip] < FLIP_MARGIN), margin[flip]
-    log(f"  flips={int(flip.sum())} of {shape.T}")
+    keep = ~flip
+    same_order = np.all(idx == o_idx, axis=1) & keep
+    assert np.max(np.abs(w_gpu[same_order] - o_w[same_order]), initial=0.0) <= 1e-4
+    # ... and bit for bit against the oracle on the GPU's own logits
+    kw = routing_kwargs(shape)
+    r_idx, r_w, _ = om.route(got["logits"], inp["bias"], **kw)
+    assert np.array_equal(idx, r_idx)
+    assert np.max(np.abs(w_gpu - r_w), initial=0.0) <= GATE_TOL
+
     # dispatch layout of every token, bit-exact from the GPU's routing
     p = om.permute(idx, shape.E, shape.ep_ranks)
-    assert np.array_equal(host(buf["expert_offsets"]), p["offsets"])
-    assert np.array_equal(host(buf["rank_offsets"]), p["rank_offsets"])
-    assert np.array_equal(host(buf["slot_of"]), p["slot_of"])
-    # sampled outputs, computed by the oracle one token at a time
-    rng = np.random.default_rng(ci)
-    cand = np.flatnonzero(~flip)
-    tokens = np.sort(rng.choice(cand, size=min(FULL_SAMPLES[ci], cand.size), replace=False))
-    log(f"  oracle outputs of {tokens.size} tokens")
-    want = _sampled_outputs(shape, inp, o_idx, o_w, tokens)
-    err = rel_err(out[tokens], want)
-    log(f"  sampled err={err:.3e}")
-    assert err <= TOL_LAYER[shape.dtype]
-    # per-expert counts sum to T*k and match the histogram of the routing
-    counts = np.diff(host(buf["expert_offsets"]))
+    for n, pn in (("expert_offsets", "offsets"), ("rank_offsets", "rank_offsets"),
+                  ("slot_of", "slot_of"), ("src_of", "src_of")):
+        assert np.array_equal(got[n], p[pn]), n
+    counts = np.diff(got["expert_offsets"])
     assert counts.sum() == shape.T * shape.k
     assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=shape.E))
+
+    # h and y_perm on every tile's first and last rows (+ a sample)
+    rng = np.random.default_rng(ci)
+    offs = got["expert_offsets"].astype(np.int64)
+    src_of = got["src_of"].astype(np.int64)
+    if ci in ALL_TOKENS:
+        rows = np.arange(shape.A)
+    else:
+        rows = _tile_rows(offs, rng, 512)
+    # plus every row of the tokens whose `out` is checked below
+    cand = np.flatnonzero(keep)
+    tokens = cand if ci in ALL_TOKENS else np.sort(
+        rng.choice(cand, size=min(FULL_SAMPLES[ci], cand.size), replace=False))
+    tok_rows = got["slot_of"].reshape(shape.T, shape.k)[tokens].ravel().astype(np.int64)
+    rows = np.union1d(rows, tok_rows)
+    log(f"  oracle h, y_perm on {rows.size} rows; out on {tokens.size} tokens")
+    h_ref, y_ref = _oracle_rows(shape, inp, offs, src_of, rows)
+    tol_s, tol_l = TOL_STAGE[shape.dtype], TOL_LAYER[shape.dtype]
+    err_h = rel_err(got["h"][rows], h_ref)
+    y_stage = np.zeros_like(y_ref)
+    h_gpu = f64(got["h"][rows])
+
+    def down(e, sel):
+        y_stage[sel] = h_gpu[sel] @ f64(inp["w_down"][e]).T
+
+    _per_expert(offs, rows, down)
+    err_y1 = rel_err(got["y_perm"][rows], y_stage)
+    err_y = rel_err(got["y_perm"][rows], y_ref)
+    log(f"  h err={err_h:.3e}  y_perm err (on GPU h)={err_y1:.3e}  (end to end)={err_y:.3e}")
+    assert err_h <= tol_s
+    assert err_y1 <= tol_s
+    assert err_y <= tol_l
+
+    # out of the checked tokens, from the oracle's own routing and gates
+    pos = {int(r): i for i, r in enumerate(rows)}
+    want = np.zeros((tokens.size, shape.d))
+    for r, t in enumerate(tokens):
+        for j in range(shape.k):
+            jg = int(np.flatnonzero(idx[t] == o_idx[t, j])[0])
+            want[r] += o_w[t, j] * y_ref[pos[int(got["slot_of"][t * shape.k + jg])]]
+    err_o = rel_err(got["out"][tokens], want)
+    log(f"  out err={err_o:.3e} over {tokens.size} tokens")
+    assert err_o <= tol_l

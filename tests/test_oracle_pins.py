@@ -711,7 +711,13 @@ def _f64_without_widening(a):
     return np.asarray(a).astype(np.float64)
 
 
+def _swiglu_bwd_du_without_sigmoid(a, u, dh):
+    h, da, _ = _ORIG_SWIGLU_BWD(a, u, dh)
+    return h, da, om._f64(dh) * om._f64(a)
+
+
 _ORIG_EXPERT_BWD = om.expert_ffn_backward
+_ORIG_SWIGLU_BWD = om.swiglu_backward
 _ORIG_GATES_BWD = om.gates_backward
 _ORIG_COMBINE_BWD = om.combine_backward
 _ORIG_FP8_ENCODE = om.fp8_e4m3_encode
@@ -738,6 +744,7 @@ MUTANTS = {
     "logits-fp32-accumulation": ("router_logits", _router_logits_fp32_accumulate),
     "logits-scaled-by-sqrt-d": ("router_logits", _router_logits_scaled),
     "bf16-bits-not-widened": ("_f64", _f64_without_widening),
+    "bwd-swiglu-du-without-sigmoid": ("swiglu_backward", _swiglu_bwd_du_without_sigmoid),
 }
 
 

@@ -399,9 +399,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
                   (PAIR ? 2u : 1u) * sbytes);
     const uint32_t wl1 = wl + (PAIR ? sbytes : 0u);
     const int wfrag0 = WF == 2 ? 0 : half * 1024;
-    const uint32_t toff0 = ((uint32_t)(row0 + trow) * (uint32_t)K + 8u * lp) * 2u;
+    // Plain rows: the tile's first row goes into the 64-bit scalar base and
+    // the per-lane offsets stay inside the tile (< TM rows of K elements), so
+    // they fit 32 bits for any K (the backward's k = 2 f included).
+    const char* tbase = GATHER ? abase : abase + (size_t)row0 * K * 2;
+    const uint32_t toff0 = ((uint32_t)trow * (uint32_t)K + 8u * lp) * 2u;
     const uint32_t tofl =
-        ((uint32_t)(row0 + min(32 * (JN - 1) + trow, nrow - 1)) * (uint32_t)K + 8u * lp) * 2u;
+        ((uint32_t)min(32 * (JN - 1) + trow, nrow - 1) * (uint32_t)K + 8u * lp) * 2u;
     const size_t cstride = (size_t)64 * K;  // bytes of 32 rows
     // GATHER: byte offset of this lane's source row for every chunk
     uint32_t goff[GATHER ? JN : 1];
@@ -419,7 +423,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     auto copy_chunk = [&](int h, int c) {
-      const char* hb = abase + (size_t)min(h, hlast) * 128;
+      const char* hb = tbase + (size_t)min(h, hlast) * 128;
       const uint32_t lds = lds0 + (uint32_t)((h % NSLOT) * HB + (32 * c + 8 * wave) * 128);
       if constexpr (GATHER)
         dma_async(hb, goff[c], lds);
