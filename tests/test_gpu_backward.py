@@ -383,9 +383,10 @@ def test_backward_long_reductions_take_the_wide_wgrad_tiles():
 # ---------------------------------------------------------------------------
 # Stage by stage: each backward step against the oracle fed the GPU's own bf16
 # inputs of that step, element by element.  Every stage output is one bf16
-# rounding (relative 2^-9) of a float32 result computed from those inputs, so
-# the elementwise bound max|got - want| / max(|want|, rms) is a few 2^-9 at
-# most: STAGE_TOL = 2e-2.  The FFN backward's intermediates are read from its
+# rounding (8 significant bits: relative error at most 2^-8) of a float32
+# result computed from those inputs, so the elementwise bound
+# max|got - want| / max(|want|, rms) is a few 2^-8 at most: STAGE_TOL = 2e-2.
+# The FFN backward's intermediates are read from its
 # workspace after the call (a | u | dh then h | da, du side by side per row).
 STAGE_TOL = 2e-2
 
@@ -436,12 +437,16 @@ def _stage_check(shape, seed, experts=None):
     B.moe_ffn_backward(cfg, buf["x_perm"], buf["expert_offsets"], dev["w_gate"], dev["w_up"],
                        dev["w_down"], g["d_y_perm"], g["d_x_perm"], g["d_w_gate"], g["d_w_up"],
                        g["d_w_down"], ws, a=a, u=u, packed_dh=images[0], packed_dx=images[1])
+    ws_r = B.workspace(cfg, "route_backward")
     B.moe_route_backward(cfg, dev["x"], dev["w_router"], buf["logits"], dev["bias"],
                          buf["topk_idx"], g["d_topk_w"], g["d_logits"], g["d_x_router"],
-                         g["d_w_router"], g["d_bias"], B.workspace(cfg, "route_backward"))
+                         g["d_w_router"], g["d_bias"], ws_r)
     B.moe_unpermute_backward(cfg, g["d_x_perm"], buf["slot_of"], g["d_x_router"], g["d_x"])
     torch.cuda.synchronize()
     del images
+    # the router products run on a bf16 copy of dz, the first T E values of their workspace
+    dz_b = host(ws_r[:T * E * 2].view(torch.int16).view(torch.bfloat16).view(T, E))
+    del ws_r
     af = A * f
     wsb = ws.view(torch.int16).view(torch.bfloat16)
     h_ws = host(wsb[2 * af:3 * af].view(A, f))
@@ -494,8 +499,11 @@ def _stage_check(shape, seed, experts=None):
     dz_ref = om.gates_backward(s, sel, G["d_topk_w"], k, shape.presel, shape.renorm)
     errs["d_logits"] = rel_err(G["d_logits"], dz_ref)
     dz = G["d_logits"].astype(np.float64)
-    errs["d_x_router"] = rel_err(G["d_x_router"], dz @ f64(inp["w_router"]))
-    errs["d_w_router"] = rel_err(G["d_w_router"], dz.T @ f64(inp["x"]))
+    # the bf16 copy: one rounding of each fp32 value (8 significant bits: |err| <= 2^-8 |v|)
+    dzb = f64(dz_b)
+    assert np.all(np.abs(dzb - dz) <= 2.0 ** -8 * np.abs(dz)), "bf16 dz is not dz rounded"
+    errs["d_x_router"] = rel_err(G["d_x_router"], dzb @ f64(inp["w_router"]))
+    errs["d_w_router"] = rel_err(G["d_w_router"], dzb.T @ f64(inp["x"]))
     if inp["bias"] is not None:
         errs["d_bias"] = rel_err(G["d_bias"], dz.sum(axis=0))
     # dispatch backward: the k rows of each token plus the router part
@@ -519,3 +527,50 @@ def test_backward_stages_full_size():
     shape = C.CONFIGS[1]
     log(f"[backward] stages full {shape.name}")
     _stage_check(shape, seed=2, experts=[0, 3, 7])
+
+
+def test_backward_dx_product_past_32bit_row_offsets():
+    """d_x_perm = [da du] [W_g; W_u] on the packed image reads rows of 2 f
+    elements: with T k = 200000 rows and f = 8192 the byte offset of a row
+    passes 2^32 from row 131072 on.  Rows on both sides of that point against
+    the product of the GPU's own da, du (read from the workspace)."""
+    E, d, f, T, k = 2, 256, 8192, 100000, 2
+    A = T * k
+    assert A * 2 * f * 2 > 2 ** 32 and A * max(d, f) < 2 ** 31
+    shape = C.E8_D4096.replace(name="bwd-wide-rows", T=T, k=k, E=E, d=d, f=f, ep_ranks=1)
+    log(f"[backward] {shape.name}: {A} rows, dx rows of {2 * f} elements")
+    cfg = B.config(shape)
+    rows_shape = shape.replace(T=A)
+    x_perm = B.to_device(I.make_x(rows_shape, seed=61))
+    dy = B.to_device(I.make_x(rows_shape, seed=62))
+    wg_np = I.make_expert_weight(shape, 63, I.TID_GATE)
+    wu_np = I.make_expert_weight(shape, 63, I.TID_UP)
+    wd_np = I.make_expert_weight(shape, 63, I.TID_DOWN)
+    wg, wu, wd = (B.to_device(w) for w in (wg_np, wu_np, wd_np))
+    offs = torch.tensor([0, A // 2, A], dtype=torch.int32, device="cuda")
+    images = B.pack_weights_backward(cfg, wg, wu, wd)
+    bf = torch.bfloat16
+    dxp = torch.empty((A, d), dtype=bf, device="cuda")
+    dwg, dwu = torch.empty((E, f, d), dtype=bf, device="cuda"), torch.empty((E, f, d), dtype=bf, device="cuda")
+    dwd = torch.empty((E, d, f), dtype=bf, device="cuda")
+    ws = B.workspace(cfg, "ffn_backward")
+    B.moe_ffn_backward(cfg, x_perm, offs, wg, wu, wd, dy, dxp, dwg, dwu, dwd, ws,
+                       packed_dh=images[0], packed_dx=images[1])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(64)
+    edge = 2 ** 32 // (2 * f * 2)
+    rows = np.unique(np.concatenate([[0, edge - 1, edge, A // 2 - 1, A // 2, A - 1],
+                                     rng.choice(A, size=64, replace=False)]))
+    af = A * f
+    wsb = ws.view(torch.int16).view(bf)
+    dadu = host(wsb[3 * af:5 * af].view(A, 2 * f)[torch.from_numpy(rows).cuda()])
+    got = host(dxp[torch.from_numpy(rows).cuda()])
+    del ws, wsb, images
+    torch.cuda.empty_cache()
+    want = np.zeros((rows.size, d))
+    for i, r in enumerate(rows):
+        e = int(r >= A // 2)
+        want[i] = f64(dadu[i, :f]) @ f64(wg_np[e]) + f64(dadu[i, f:]) @ f64(wu_np[e])
+    err = rel_err(got, want)
+    log(f"  dx rows {rows.size} (edge {edge}) err={err:.2e}")
+    assert err <= STAGE_TOL
