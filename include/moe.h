@@ -64,7 +64,9 @@ enum moe_status {
   MOE_OK = 0,
   MOE_EINVAL = -1,       /* bad shape, flag, pointer or workspace size         */
   MOE_EUNSUPPORTED = -2, /* valid problem outside what the kernels implement   */
-  MOE_EHIP = -3          /* a HIP launch failed                                */
+  MOE_EHIP = -3,         /* a HIP launch failed                                */
+  MOE_ESCRATCH = -4      /* more scratch than the static array of the
+                            allocation-free entry point holds                  */
 };
 
 enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
@@ -189,6 +191,28 @@ int moe_route(const moe_config* cfg, const void* x, const void* w_router, const 
 int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
                 int32_t* expert_offsets, int32_t* rank_offsets, int32_t* slot_of,
                 int32_t* src_of, void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_permute_noalloc: moe_permute for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments and outputs as moe_permute, bit for bit,
+ * without `ws`: the per-chunk counts and pair ranks go to a static device
+ * array of moe_noalloc_scratch_bytes() bytes (16 MiB) that the library holds
+ * on every GPU it runs on until the process ends.  The call allocates and
+ * frees nothing; its first call on a device looks up that device's copy of
+ * the array (hipGetSymbolAddress).  A problem whose scratch (about
+ * 4 (ceil(T / 256) E + T k) bytes) exceeds the array returns MOE_ESCRATCH
+ * before anything is launched.  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller.  Nothing in the array
+ * needs to start at zero: every value a call reads it has written first.
+ */
+int moe_permute_noalloc(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                        int32_t* expert_offsets, int32_t* rank_offsets, int32_t* slot_of,
+                        int32_t* src_of, void* x_perm, void* stream);
+
+/* Bytes of the static scratch array behind moe_permute_noalloc. */
+size_t moe_noalloc_scratch_bytes(void);
 
 /*
  * Expert FFN, first half, grouped over experts: for every expert e and every

@@ -53,7 +53,7 @@ def test_binding_declares_every_signature():
 
 def test_strerror():
     assert B.strerror(0) == "ok"
-    for s in (-1, -2, -3):
+    for s in (-1, -2, -3, -4):
         assert B.strerror(s) and B.strerror(s) != "ok"
     assert B.strerror(12345) == "unknown status"
 
@@ -247,3 +247,17 @@ def test_header_is_a_plain_c_abi(tmp_path):
     assert int(f[5]) == B.workspace_bytes(cfg, "ffn_backward")
     assert int(f[6]) == B.MOE_OK and int(f[7]) == B.MOE_EINVAL
     assert f[8].strip() == B.strerror(B.MOE_EUNSUPPORTED)
+
+
+def test_noalloc_permute_rejects_beyond_its_scratch_before_launch():
+    """moe_permute_noalloc checks its scratch need against the static array on
+    the host (4 (ceil(T/256) E + T k) bytes > 16 MiB here) before any HIP call."""
+    L = B.lib()
+    assert L.moe_noalloc_scratch_bytes() == 16 << 20
+    cfg = B.config(C.E8_D4096.replace(T=1 << 20, k=8, d=64, f=64))
+    fake = ctypes.c_void_p(256)
+    st = L.moe_permute_noalloc(ctypes.byref(cfg), None, fake, fake, fake, fake, fake, None, None)
+    assert st == B.MOE_ESCRATCH
+    bad = B.config(C.E8_D4096.replace(k=0))
+    assert L.moe_permute_noalloc(ctypes.byref(bad), None, fake, fake, fake, fake, fake, None,
+                                 None) == B.MOE_EINVAL

@@ -16,7 +16,7 @@ from .configs import MoEShape
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ESCRATCH = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 ENTRY = {"route": 1, "permute": 2, "ffn": 3, "combine": 4, "layer": 5, "route_stats": 6,
          "ffn_backward": 7, "route_backward": 8}
@@ -34,7 +34,7 @@ EXPORTS = ("moe_strerror", "moe_validate", "moe_workspace_bytes", "moe_route", "
            "moe_route_stats", "moe_quantize_fp8", "moe_dequantize_fp8", "moe_combine_backward",
            "moe_ffn_backward", "moe_route_backward", "moe_unpermute_backward",
            "moe_ffn_gate_up_packed_train", "moe_packed_weight_bytes_backward",
-           "moe_pack_weights_backward")
+           "moe_pack_weights_backward", "moe_permute_noalloc", "moe_noalloc_scratch_bytes")
 
 
 class MoEConfig(ctypes.Structure):
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_bytes.argtypes = [cfgp, i32, ctypes.POINTER(sz)]
         L.moe_route.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_permute.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_permute_noalloc.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_noalloc_scratch_bytes.argtypes = []
         L.moe_ffn_gate_up.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
         L.moe_ffn_down.argtypes = [cfgp, vp, vp, vp, vp, vp]
         L.moe_grouped_ffn.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -97,6 +99,7 @@ def lib() -> ctypes.CDLL:
                                            ctypes.POINTER(MoELayerBufs), vp, sz, vp]
         for name in EXPORTS[1:]:
             getattr(L, name).restype = i32
+        L.moe_noalloc_scratch_bytes.restype = sz
         _lib = L
     return _lib
 
@@ -179,6 +182,17 @@ def moe_permute(cfg, x, topk_idx, expert_offsets, rank_offsets, slot_of, src_of,
                                             _ptr(expert_offsets), _ptr(rank_offsets),
                                             _ptr(slot_of), _ptr(src_of), _ptr(x_perm), wp, wn,
                                             _stream(stream)))
+
+
+def moe_permute_noalloc(cfg, x, topk_idx, expert_offsets, rank_offsets, slot_of, src_of, x_perm,
+                        stream=None):
+    _check("moe_permute_noalloc", lib().moe_permute_noalloc(
+        ctypes.byref(cfg), _ptr(x), _ptr(topk_idx), _ptr(expert_offsets), _ptr(rank_offsets),
+        _ptr(slot_of), _ptr(src_of), _ptr(x_perm), _stream(stream)))
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().moe_noalloc_scratch_bytes())
 
 
 def moe_ffn_gate_up(cfg, x_perm, expert_offsets, w_gate, w_up, h, stream=None):

@@ -215,6 +215,9 @@ const char* moe_strerror(int status) {
     case MOE_EINVAL: return "invalid argument (shape, flag, pointer or workspace)";
     case MOE_EUNSUPPORTED: return "valid problem outside what the kernels implement";
     case MOE_EHIP: return "HIP launch failed";
+    case MOE_ESCRATCH:
+      return "problem needs more scratch than the library's static scratch array holds "
+             "(moe_noalloc_scratch_bytes); use the entry point with a workspace";
     default: return "unknown status";
   }
 }
@@ -289,6 +292,25 @@ int moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
   return do_permute(c, x, topk_idx, expert_offsets, rank_offsets, slot_of, src_of, x_perm, ws,
                     static_cast<hipStream_t>(stream));
 }
+
+int moe_permute_noalloc(const moe_config* cfg, const void* x, const int32_t* topk_idx,
+                        int32_t* expert_offsets, int32_t* rank_offsets, int32_t* slot_of,
+                        int32_t* src_of, void* x_perm, void* stream) {
+  int s = check_routing(cfg);
+  if (s != MOE_OK) return s;
+  const moe_config& c = *cfg;
+  if (!expert_offsets || !rank_offsets) return MOE_EINVAL;
+  void* scratch_ptr = nullptr;
+  if (c.T > 0) {
+    if (!topk_idx || !slot_of || !src_of || (!x != !x_perm)) return MOE_EINVAL;
+    if (permute_ws_bytes(c) > kNoAllocScratchBytes) return MOE_ESCRATCH;
+    if (noalloc_scratch(&scratch_ptr) != hipSuccess) return MOE_EHIP;
+  }
+  return do_permute(c, x, topk_idx, expert_offsets, rank_offsets, slot_of, src_of, x_perm,
+                    scratch_ptr, static_cast<hipStream_t>(stream));
+}
+
+size_t moe_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 int moe_ffn_gate_up(const moe_config* cfg, const void* x_perm, const int32_t* expert_offsets,
                     const void* w_gate, const void* w_up, void* h, void* stream) {

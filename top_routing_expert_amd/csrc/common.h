@@ -58,6 +58,10 @@ hipError_t launch_permute(const moe_config& c, const void* x, const int32_t* top
                           int32_t* expert_offsets, int32_t* rank_offsets, int32_t* slot_of,
                           int32_t* src_of, void* x_perm, void* ws, hipStream_t st);
 size_t permute_ws_bytes(const moe_config& c);
+// The allocation-free permute's static scratch: its size, and the current
+// device's address of it (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+hipError_t noalloc_scratch(void** ptr);
 
 hipError_t launch_ffn_gate_up(const moe_config& c, const void* x_perm, const int32_t* offs,
                               const void* wg, const void* wu, void* h, hipStream_t st);

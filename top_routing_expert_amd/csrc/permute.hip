@@ -23,6 +23,8 @@
 //     src_of, reads the token row once and stores it to its k slots with
 //     16-byte vector accesses (x is read once; x_perm written once).  With no
 //     x_perm it writes the indices only.
+#include <mutex>
+
 #include "common.h"
 
 namespace moe {
@@ -274,6 +276,36 @@ hipError_t launch_permute(const moe_config& c, const void* x, const int32_t* top
       static_cast<const u32x4*>(x), topk_idx, rank, counts, expert_offsets, c.T, c.k, c.E, row_vecs,
       slot_of, src_of, static_cast<u32x4*>(x_perm));
   return hipGetLastError();
+}
+
+// ------------------------------------------------- allocation-free scratch
+// moe_permute_noalloc's scratch (the per-chunk counts and pair ranks that
+// moe_permute keeps in its caller's workspace): a static device array of
+// kNoAllocScratchBytes.  Every GPU the library runs on holds its own copy
+// from module load until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: the device address is looked
+// up once per device with hipGetSymbolAddress and only that address is used.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // the current device's copy
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace moe
