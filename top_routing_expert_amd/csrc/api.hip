@@ -20,7 +20,7 @@ int check_core(const moe_config* c) {
   if (c->T < 0 || c->d <= 0 || c->E <= 0 || c->k <= 0 || c->f <= 0) return MOE_EINVAL;
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_EINVAL;
   if (c->k > c->E) return MOE_EINVAL;
-  if (c->k > 16 || c->E > 1024) return MOE_EUNSUPPORTED;
+  if (c->k > 16 || c->E > kMaxExperts) return MOE_EUNSUPPORTED;
   if (c->dtype == MOE_BF16 && (c->d % 64 || c->f % 64)) return MOE_EUNSUPPORTED;
   if (c->dtype == MOE_F32 && (c->d % 4 || c->f % 4)) return MOE_EUNSUPPORTED;
   const long rows = (long)c->T * c->k;

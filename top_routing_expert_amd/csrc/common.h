@@ -10,6 +10,9 @@
 
 namespace moe {
 
+// Largest expert count the entry points accept (checked on the host).
+constexpr int kMaxExperts = 1024;
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
