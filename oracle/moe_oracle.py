@@ -48,7 +48,7 @@ __all__ = [
     "permute", "silu", "expert_ffn", "grouped_ffn", "combine", "layer",
     "select_bruteforce", "dense_bruteforce", "combine_backward", "expert_ffn_backward",
     "grouped_ffn_backward", "scatter_rows_backward", "gates_backward", "layer_backward",
-    "swiglu_backward",
+    "swiglu_backward", "quantize_weights_fp8", "gate_up_fp8",
 ]
 
 
@@ -346,6 +346,42 @@ def dequantize_rows_fp8(codes, scale, zero) -> np.ndarray:
     s = np.asarray(scale, np.float32)[:, None]
     z = np.asarray(zero, np.float32)[:, None]
     return round_bf16(((q * s).astype(np.float32) + z).astype(np.float32))
+
+
+def quantize_weights_fp8(w):
+    """Per-output-channel symmetric FP8 (E4M3) of expert weights [..., F, K]
+    (bf16 bit patterns or floats), for an FP8 first GEMM fed by the per-token
+    FP8 payload above ([SyncTax] §3.1 sends the dispatch payload in FP8; the
+    weights of the GEMM that consumes it are this path's reading).  Readings:
+    one scale per output feature n (a weight row), s_n = max_k |w[n, k]| / 448
+    in float32, so every row uses the whole E4M3 range and one large row does
+    not coarsen the others; weights are centred, so no zero point; v = w / s_n
+    in float32 (0 for an all-zero row, s_n = 0), clamped to +-448 and rounded
+    by fp8_e4m3_encode.  Returns (codes uint8 [..., F, K], scale float32
+    [..., F])."""
+    a = np.asarray(w)
+    x = (widen_bf16(a) if a.dtype == np.uint16 else a.astype(np.float64)).astype(np.float32)
+    m = np.abs(x).max(axis=-1)
+    s = (m / np.float32(F8_MAX)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = np.where(s[..., None] > 0, x / s[..., None], np.float32(0.0)).astype(np.float32)
+    v = np.clip(v, np.float32(-F8_MAX), np.float32(F8_MAX))
+    return fp8_e4m3_encode(v), s
+
+
+def gate_up_fp8(x_codes, x_scale, x_zero, wg_codes, wg_scale, wu_codes, wu_scale):
+    """The expert's first GEMM on FP8 operands, exactly: the token rows are
+    x^[k] = code * s_t + z_t (the per-token affine payload), the weights
+    w^[n, k] = code * s_n (per output feature); a = x^ . w^_g[n],
+    u = x^ . w^_u[n] and h = SiLU(a) * u, all in float64 on the decoded
+    values with no intermediate rounding.  Returns (h, a, u) [rows, F]."""
+    xd = (fp8_e4m3_decode(x_codes) * np.asarray(x_scale, np.float64)[:, None]
+          + np.asarray(x_zero, np.float64)[:, None])
+    wg = fp8_e4m3_decode(wg_codes) * np.asarray(wg_scale, np.float64)[:, None]
+    wu = fp8_e4m3_decode(wu_codes) * np.asarray(wu_scale, np.float64)[:, None]
+    a = xd @ wg.T
+    u = xd @ wu.T
+    return silu(a) * u, a, u
 
 
 def gather_rows(x, src_of, k: int) -> np.ndarray:

@@ -383,6 +383,63 @@ def pin_fp8_row_quantization():
     assert np.all(np.abs(xr - xf) <= hr[:, None] / 16 + np.abs(xf) * 2.0 ** -8 + 1e-30)
 
 
+def pin_fp8_weight_quantization():
+    """Per-output-channel E4M3 weights: each row's largest magnitude lands on
+    +-448 exactly (codes 0x7E / 0xFE), power-of-two ratios to it stay exact,
+    an all-zero row has scale 0 and zero codes, and the decoded weight is
+    within half an E4M3 step of the weight (3 mantissa bits: 2^-4 |v| for
+    normal codes, 2^-10 below 2^-6)."""
+    w = np.array([[1.0, -2.0, 0.5, 2.0, 0.25],
+                  [0.0, 0.0, 0.0, 0.0, 0.0],
+                  [-3.0, 0.75, 1.5, -0.375, 3.0]], np.float32)
+    codes, s = om.quantize_weights_fp8(w)
+    assert s.dtype == np.float32 and codes.dtype == np.uint8
+    assert s[0] == np.float32(2.0) / np.float32(448.0) and s[1] == 0.0
+    assert s[2] == np.float32(3.0) / np.float32(448.0)
+    # row 0: -2 and 2 are the extremes; 1 = 224, 0.5 = 112, 0.25 = 56 are exact E4M3 values
+    assert codes[0].tolist() == [0x76, 0xFE, 0x6E, 0x7E, 0x66]
+    assert not codes[1].any()
+    # row 2: 3 -> 448, -3 -> -448, 1.5 -> 224, 0.75 -> 112, -0.375 -> -56
+    assert codes[2].tolist() == [0xFE, 0x6E, 0x76, 0xE6, 0x7E]
+    rng = np.random.default_rng(43)
+    bits = om.round_bf16((0.02 * rng.standard_normal((3, 24, 200))).astype(np.float32))
+    codes, s = om.quantize_weights_fp8(bits)
+    assert codes.shape == bits.shape and s.shape == (3, 24)
+    wv = om.widen_bf16(bits)
+    back = om.fp8_e4m3_decode(codes) * s.astype(np.float64)[..., None]
+    v = np.abs(wv) / s.astype(np.float64)[..., None]
+    step = np.where(v >= 2.0 ** -6, 2.0 ** -4 * v, 2.0 ** -10) * s.astype(np.float64)[..., None]
+    assert np.all(np.abs(back - wv) <= step * (1 + 1e-6))
+    # the row maximum is +-448 in every row
+    assert np.all(np.max(np.abs(om.fp8_e4m3_decode(codes)), axis=-1) == 448.0)
+
+
+def pin_gate_up_fp8_on_exact_operands():
+    """When the FP8 operands decode to values that the bf16 path can hold
+    exactly, the FP8 first GEMM is the pinned SwiGLU first GEMM (expert_ffn)
+    on those values; a shift of every token row by c moves a by
+    c * sum_k w^[n, k] (the zero point enters linearly)."""
+    rng = np.random.default_rng(44)
+    T, F, K = 9, 6, 40
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F and ((c >> 3) & 0xF) <= 9],
+                      np.uint8)
+    xc = rng.choice(finite, size=(T, K))
+    gc, uc = rng.choice(finite, size=(F, K)), rng.choice(finite, size=(F, K))
+    xs = np.full(T, 0.5, np.float32)            # powers of two: x^ = code s + z stays exact
+    xz = np.array([0.0, 0.25, -1.0, 2.0, 0.0, -0.5, 1.0, 0.125, 0.0], np.float32)
+    gs, us = np.full(F, 0.25, np.float32), np.full(F, 2.0 ** -5, np.float32)
+    h, a, u = om.gate_up_fp8(xc, xs, xz, gc, gs, uc, us)
+    xd = om.fp8_e4m3_decode(xc) * 0.5 + xz.astype(np.float64)[:, None]
+    wg = om.fp8_e4m3_decode(gc) * 0.25
+    wu = om.fp8_e4m3_decode(uc) * 2.0 ** -5
+    _, h_ref = om.expert_ffn(xd, wg, wu, np.zeros((3, F)))
+    assert np.allclose(h, h_ref, rtol=1e-13, atol=1e-13)
+    assert np.allclose(a, xd @ wg.T, rtol=1e-13, atol=1e-13)
+    # zero point: shifting every row by c adds c * sum_k w^[n, k] to a
+    h2, a2, _ = om.gate_up_fp8(xc, xs, xz + np.float32(0.75), gc, gs, uc, us)
+    assert np.allclose(a2 - a, 0.75 * wg.sum(axis=1)[None, :], rtol=1e-12, atol=1e-12)
+
+
 def pin_router_logits_hand_case():
     """z = x Wr^T on a hand-worked case whose last logit needs 33 significant
     bits (exact in float64, rounded by any float32 accumulation), given both
@@ -716,8 +773,23 @@ def _swiglu_bwd_du_without_sigmoid(a, u, dh):
     return h, da, om._f64(dh) * om._f64(a)
 
 
+def _fp8_weight_scale_per_column(w):
+    a = np.asarray(w)
+    x = (om.widen_bf16(a) if a.dtype == np.uint16 else a.astype(np.float64)).astype(np.float32)
+    s = (np.abs(x).max(axis=-2) / np.float32(om.F8_MAX)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        v = np.where(s[..., None, :] > 0, x / s[..., None, :], np.float32(0.0)).astype(np.float32)
+    return om.fp8_e4m3_encode(np.clip(v, -448, 448).astype(np.float32)), s
+
+
+def _gate_up_fp8_no_zero_point(x_codes, x_scale, x_zero, wg_codes, wg_scale, wu_codes, wu_scale):
+    return _ORIG_GATE_UP_FP8(x_codes, x_scale, np.zeros_like(np.asarray(x_zero)), wg_codes,
+                             wg_scale, wu_codes, wu_scale)
+
+
 _ORIG_EXPERT_BWD = om.expert_ffn_backward
 _ORIG_SWIGLU_BWD = om.swiglu_backward
+_ORIG_GATE_UP_FP8 = om.gate_up_fp8
 _ORIG_GATES_BWD = om.gates_backward
 _ORIG_COMBINE_BWD = om.combine_backward
 _ORIG_FP8_ENCODE = om.fp8_e4m3_encode
@@ -745,6 +817,8 @@ MUTANTS = {
     "logits-scaled-by-sqrt-d": ("router_logits", _router_logits_scaled),
     "bf16-bits-not-widened": ("_f64", _f64_without_widening),
     "bwd-swiglu-du-without-sigmoid": ("swiglu_backward", _swiglu_bwd_du_without_sigmoid),
+    "fp8-weight-scale-per-column": ("quantize_weights_fp8", _fp8_weight_scale_per_column),
+    "fp8-gemm-zero-point-dropped": ("gate_up_fp8", _gate_up_fp8_no_zero_point),
 }
 
 
