@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 PHASES = ("route", "permute", "ffn_gate_up", "ffn_down", "combine")
 DOMINANT = "ffn_gate_up"
 FLIP_MARGIN = 1e-4
@@ -93,10 +94,12 @@ def parse(argv=None):
     ap.add_argument("--ffn", choices=sorted(FFN_KERNELS), default="packed",
                     help="expert-weight layout of the grouped FFN: packed once at load time "
                          "(moe_pack_weights) or the plain [E,f,d] / [E,d,f] arrays")
-    ap.add_argument("--dispatch", choices=("gather", "copy", "fp8"), default="gather",
+    ap.add_argument("--dispatch", choices=("gather", "copy", "fp8", "fp8gemm"), default="gather",
                     help="packed FFN: gather the token rows inside the first GEMM (the dispatch "
-                         "writes indices only), copy them to x_perm first, or send them as "
-                         "per-token FP8 (quantize, then decode into x_perm in expert order)")
+                         "writes indices only), copy them to x_perm first, send them as "
+                         "per-token FP8 (quantize, then decode into x_perm in expert order), or "
+                         "feed the per-token FP8 codes to an FP8 first GEMM on E4M3 weights "
+                         "(fp8gemm; the down projection stays bf16)")
     ap.add_argument("--diagnostics", action="store_true",
                     help="also time the routing diagnostics (moe_route_stats) after the dispatch; "
                          "reported as its own phase and included in the step")
@@ -139,13 +142,14 @@ def prepare(shape, inp, ffn="packed", dispatch="gather", backward=False, keep_pl
     T, E, k, d, f, R = shape.T, shape.E, shape.k, shape.d, shape.f, shape.ep_ranks
     A = T * k
     dt = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
-    gather, fp8 = dispatch == "gather", dispatch == "fp8"
+    gather, fp8 = dispatch == "gather", dispatch in ("fp8", "fp8gemm")
+    fp8gemm = dispatch == "fp8gemm"
     e = lambda *s, t=dt: torch.empty(s, dtype=t, device="cuda")
     buf = dict(
         logits=e(T, E, t=torch.float32), topk_idx=e(T, k, t=torch.int32),
         topk_w=e(T, k, t=torch.float32), expert_offsets=e(E + 1, t=torch.int32),
         rank_offsets=e(R + 1, t=torch.int32), slot_of=e(A, t=torch.int32),
-        src_of=e(A, t=torch.int32), x_perm=None if gather else e(A, d),
+        src_of=e(A, t=torch.int32), x_perm=None if (gather or fp8gemm) else e(A, d),
         codes=e(T, d, t=torch.uint8) if fp8 else None,
         scale_zero=e(T, 2, t=torch.float32) if fp8 else None,
         h=e(A, f), y_perm=e(A, d), out=e(T, d))
@@ -154,7 +158,11 @@ def prepare(shape, inp, ffn="packed", dispatch="gather", backward=False, keep_pl
                ws_permute=B.workspace(cfg, "permute"), packed=None)
     if ffn == "packed":
         log("packing expert weights")
-        ctx["packed"] = B.pack_weights(cfg, dev["w_gate"], dev["w_up"], dev["w_down"])
+        if fp8gemm:  # E4M3 gate/up image; the down projection keeps its bf16 image
+            ctx["fp8_image"] = B.pack_weights_fp8(cfg, dev["w_gate"], dev["w_up"])
+            ctx["packed"] = B.pack_weights(cfg, None, None, dev["w_down"])
+        else:
+            ctx["packed"] = B.pack_weights(cfg, dev["w_gate"], dev["w_up"], dev["w_down"])
         torch.cuda.synchronize()
         if not (backward or keep_plain):  # the plain arrays are then dropped
             dev["w_gate"] = dev["w_up"] = dev["w_down"] = None
@@ -169,7 +177,8 @@ def forward_calls(ctx, stream=None):
 
     stream = torch.cuda.current_stream() if stream is None else stream
     cfg, dev, buf = ctx["cfg"], ctx["dev"], ctx["buf"]
-    gather, fp8 = ctx["dispatch"] == "gather", ctx["dispatch"] == "fp8"
+    gather, fp8 = ctx["dispatch"] == "gather", ctx["dispatch"] in ("fp8", "fp8gemm")
+    fp8gemm = ctx["dispatch"] == "fp8gemm"
     calls = {
         "route": lambda: B.moe_route(cfg, dev["x"], dev["w_router"], dev["bias"], buf["logits"],
                                      buf["topk_idx"], buf["topk_w"], ctx["ws_route"], stream),
@@ -181,11 +190,16 @@ def forward_calls(ctx, stream=None):
     if fp8:
         calls["fp8_quantize"] = lambda: B.moe_quantize_fp8(cfg, dev["x"], buf["codes"],
                                                            buf["scale_zero"], stream)
+    if fp8 and not fp8gemm:
         calls["fp8_dequantize"] = lambda: B.moe_dequantize_fp8(
             cfg, buf["codes"], buf["src_of"], buf["scale_zero"], buf["x_perm"], stream)
     if ctx["ffn"] == "packed":
         pgu, pd = ctx["packed"]
-        if ctx["backward"]:  # training forward: also keep the pre-activations a and u
+        if fp8gemm:
+            calls["ffn_gate_up"] = lambda: B.moe_ffn_gate_up_fp8_gather(
+                cfg, buf["codes"], buf["scale_zero"], buf["src_of"], buf["expert_offsets"],
+                ctx["fp8_image"], buf["h"], stream)
+        elif ctx["backward"]:  # training forward: also keep the pre-activations a and u
             calls["ffn_gate_up"] = lambda: B.moe_ffn_gate_up_packed_train(
                 cfg, buf["x_perm"], None, buf["expert_offsets"], pgu, buf["h"], buf["a"],
                 buf["u"], stream)
@@ -209,7 +223,7 @@ def forward_calls(ctx, stream=None):
 
 
 # ----------------------------------------------------------------------------- accounting
-def algorithmic(shape, counts, gather=False):
+def algorithmic(shape, counts, gather=False, fp8gemm=False):
     """Algorithmic HBM bytes and flops of one launch of every phase.  With the
     gather fused into the first GEMM, the dispatch writes indices only and the
     first GEMM reads the token rows (and src_of) instead of x_perm."""
@@ -245,6 +259,13 @@ def algorithmic(shape, counts, gather=False):
         "route_bwd": dict(bytes=T * E * 4 * 2 + T * E * 2 + 8 * A + T * d * s * 2
                           + 2 * E * d * s, flops=4 * T * E * d),
         "unpermute_bwd": dict(bytes=A * d * s + 2 * T * d * s + 4 * A, flops=A * d),
+    } if not fp8gemm else {
+        **algorithmic(shape, counts, gather=True),
+        # E4M3 weight codes of every expert with rows (read once) and their per-row scale and
+        # code sum, the token codes gathered through src_of (one row each, plus src_of and the
+        # token's scale and centre), h out
+        "ffn_gate_up": dict(bytes=2 * e_nz * f * d + 2 * e_nz * f * 8 + A * d + 12 * A
+                            + A * f * s, flops=2 * A * d * 2 * f, peak="fp8"),
     }
 
 
@@ -253,6 +274,8 @@ def roofline_of(work, ms, dtype="bf16"):
     selects (HBM below the ridge, the matrix-core or vector peak above)."""
     sec = ms * 1e-3
     peak_fl = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_FP32_TFLOPS
+    if work.get("peak") == "fp8":
+        peak_fl = PEAK_FP8_TFLOPS
     ai = work["flops"] / work["bytes"] if work["bytes"] else float("inf")
     ridge = peak_fl * 1e12 / (PEAK_HBM_GBS * 1e9)
     gbs = work["bytes"] / sec / 1e9
@@ -260,7 +283,8 @@ def roofline_of(work, ms, dtype="bf16"):
     if ai < ridge:
         return dict(bound="hbm", achieved=gbs, peak=PEAK_HBM_GBS, unit="GB/s", frac=gbs / PEAK_HBM_GBS,
                     tflops=tfl, mfma_frac=tfl / peak_fl, ai=ai)
-    return dict(bound="mfma" if dtype == "bf16" else "alu", achieved=tfl, peak=peak_fl,
+    return dict(bound="mfma" if (dtype == "bf16" or work.get("peak") == "fp8") else "alu",
+                achieved=tfl, peak=peak_fl,
                 unit="TFLOP/s", frac=tfl / peak_fl, gbs=gbs, hbm_frac=gbs / PEAK_HBM_GBS, ai=ai)
 
 
@@ -487,7 +511,7 @@ def run_forward(shape, a, inp, copy_gbs=None, headline=True):
     counts = np.diff(B.to_host_bits(buf["expert_offsets"]).astype(np.int64))
     idx_gpu = B.to_host_bits(buf["topk_idx"])
     gather = ctx["dispatch"] == "gather"
-    work = algorithmic(shape, counts, gather)
+    work = algorithmic(shape, counts, gather, fp8gemm=ctx["dispatch"] == "fp8gemm")
     if a.backward and ctx["ffn"] == "packed":  # the saved pre-activations, written by the forward
         work["ffn_gate_up"]["bytes"] += 2 * A * f * (2 if shape.dtype == "bf16" else 4)
         # and read by the backward instead of the recompute (no weight re-read, 4 A d f fewer flops)
@@ -500,8 +524,9 @@ def run_forward(shape, a, inp, copy_gbs=None, headline=True):
     roofline = {"bound": dom["bound"], "achieved": round(dom["achieved"], 3),
                 "peak": dom["peak"], "unit": dom["unit"], "frac": round(dom["frac"], 4),
                 "traffic": traffic,
-                "kernel": FFN_KERNELS[ctx["ffn"]][2].replace(
-                    ")", "_gather)" if gather else ("_train)" if a.backward and ctx["ffn"] == "packed" else ")")),
+                "kernel": ("gate_up_fp8_kernel (moe_ffn_gate_up_fp8_gather)"
+                           if ctx["dispatch"] == "fp8gemm" else FFN_KERNELS[ctx["ffn"]][2].replace(
+                    ")", "_gather)" if gather else ("_train)" if a.backward and ctx["ffn"] == "packed" else ")"))),
                 "algorithmic_bytes": work[DOMINANT]["bytes"],
                 "algorithmic_flops": work[DOMINANT]["flops"],
                 "avg_launch_ms": round(dom["ms"], 5)}

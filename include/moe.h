@@ -373,6 +373,39 @@ int moe_ffn_gate_up_packed_gather(const moe_config* cfg, const void* x, const in
                                   void* h, void* stream);
 
 /*
+ * ------------------------------------------------------ FP8 first GEMM
+ * The first GEMM consuming the per-token FP8 dispatch payload
+ * (moe_quantize_fp8: codes c[t, k], (s_t, z_t)) directly, against expert
+ * weights quantised once to E4M3 with one scale per output feature
+ * ([SyncTax] §3.1: the dispatch payload travels as per-token FP8; the
+ * weights' FP8 form is this library's reading):
+ *   x^[t, k] = c[t, k] s_t + z_t,   w^[n, k] = q[n, k] s_n,
+ *   s_n = max_k |w[n, k]| / 448 (float32), q = E4M3(w / s_n), nearest-even,
+ *   h = SiLU(x^ . w^_gate[n]) * (x^ . w^_up[n])     [T*k, f] bf16 out.
+ * The matrix instruction multiplies raw codes with float32 accumulation; the
+ * epilogue applies s_t s_n and the centre's term z_t s_n sum_k q[n, k].
+ * bf16 problems with d a multiple of 128 (MOE_EUNSUPPORTED otherwise).
+ *
+ * moe_fp8_weight_bytes: bytes of the FP8 gate/up image.
+ * moe_pack_weights_fp8: writes the image from w_gate, w_up [E, f, d] bf16
+ *   (16-byte aligned; image 256-byte aligned): codes [E][2 f][d] uint8 (per
+ *   group of 16 features its 16 gate rows, then its 16 up rows), the float
+ *   scales s_n and the float code sums sum_k q[n, k] (exact, then one
+ *   float rounding) of the same rows.  A load-time layout, like
+ *   moe_pack_weights.
+ * moe_ffn_gate_up_fp8_gather: h row p from token src_of[p] / k's codes
+ *   (x_codes [T, d] uint8, 16-byte aligned; scale_zero [T, 2] float, from
+ *   moe_quantize_fp8), expert_offsets [E+1] as for the grouped FFN.
+ */
+int moe_fp8_weight_bytes(const moe_config* cfg, size_t* bytes);
+int moe_pack_weights_fp8(const moe_config* cfg, const void* w_gate, const void* w_up,
+                         void* image, void* stream);
+int moe_ffn_gate_up_fp8_gather(const moe_config* cfg, const uint8_t* x_codes,
+                               const float* scale_zero, const int32_t* src_of,
+                               const int32_t* expert_offsets, const void* image, void* h,
+                               void* stream);
+
+/*
  * moe_layer_fwd_packed: when bufs->x_perm is NULL (or bufs is NULL), the
  * dispatch writes indices only and the first GEMM gathers its rows
  * (moe_ffn_gate_up_packed_gather); a given bufs->x_perm is written as by

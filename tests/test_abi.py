@@ -261,3 +261,26 @@ def test_noalloc_permute_rejects_beyond_its_scratch_before_launch():
     bad = B.config(C.E8_D4096.replace(k=0))
     assert L.moe_permute_noalloc(ctypes.byref(bad), None, fake, fake, fake, fake, fake, None,
                                  None) == B.MOE_EINVAL
+
+
+def test_fp8_gemm_entries_reject_before_launch():
+    """The FP8 first GEMM takes bf16 problems with d a multiple of 128 only,
+    and checks its pointers and alignments on the host."""
+    L = B.lib()
+    fake = ctypes.c_void_p(4096)
+    n = ctypes.c_size_t(0)
+    ok = B.config(C.E8_D4096.replace(d=256, f=128))
+    assert L.moe_fp8_weight_bytes(ctypes.byref(ok), ctypes.byref(n)) == B.MOE_OK and n.value > 0
+    for bad, want in ((C.E8_D4096.replace(d=192), B.MOE_EUNSUPPORTED),
+                      (C.TINY_F32, B.MOE_EUNSUPPORTED)):
+        cfg = B.config(bad)
+        assert L.moe_fp8_weight_bytes(ctypes.byref(cfg), ctypes.byref(n)) == want
+        assert L.moe_pack_weights_fp8(ctypes.byref(cfg), fake, fake, fake, None) == want
+        assert L.moe_ffn_gate_up_fp8_gather(ctypes.byref(cfg), fake, fake, fake, fake, fake, fake,
+                                            None) == want
+    assert L.moe_fp8_weight_bytes(ctypes.byref(ok), None) == B.MOE_EINVAL
+    assert L.moe_pack_weights_fp8(ctypes.byref(ok), fake, None, fake, None) == B.MOE_EINVAL
+    assert L.moe_pack_weights_fp8(ctypes.byref(ok), fake, fake, ctypes.c_void_p(4096 + 16),
+                                  None) == B.MOE_EINVAL  # image not 256-byte aligned
+    assert L.moe_ffn_gate_up_fp8_gather(ctypes.byref(ok), fake, fake, None, fake, fake, fake,
+                                        None) == B.MOE_EINVAL

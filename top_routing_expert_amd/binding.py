@@ -34,7 +34,8 @@ EXPORTS = ("moe_strerror", "moe_validate", "moe_workspace_bytes", "moe_route", "
            "moe_route_stats", "moe_quantize_fp8", "moe_dequantize_fp8", "moe_combine_backward",
            "moe_ffn_backward", "moe_route_backward", "moe_unpermute_backward",
            "moe_ffn_gate_up_packed_train", "moe_packed_weight_bytes_backward",
-           "moe_pack_weights_backward", "moe_permute_noalloc", "moe_noalloc_scratch_bytes")
+           "moe_pack_weights_backward", "moe_permute_noalloc", "moe_noalloc_scratch_bytes",
+           "moe_fp8_weight_bytes", "moe_pack_weights_fp8", "moe_ffn_gate_up_fp8_gather")
 
 
 class MoEConfig(ctypes.Structure):
@@ -71,6 +72,9 @@ def lib() -> ctypes.CDLL:
         L.moe_permute.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_permute_noalloc.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_noalloc_scratch_bytes.argtypes = []
+        L.moe_fp8_weight_bytes.argtypes = [cfgp, ctypes.POINTER(sz)]
+        L.moe_pack_weights_fp8.argtypes = [cfgp, vp, vp, vp, vp]
+        L.moe_ffn_gate_up_fp8_gather.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_ffn_gate_up.argtypes = [cfgp, vp, vp, vp, vp, vp, vp]
         L.moe_ffn_down.argtypes = [cfgp, vp, vp, vp, vp, vp]
         L.moe_grouped_ffn.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -265,6 +269,31 @@ def moe_ffn_gate_up_packed_gather(cfg, x, src_of, expert_offsets, packed_gate_up
            lib().moe_ffn_gate_up_packed_gather(ctypes.byref(cfg), _ptr(x), _ptr(src_of),
                                                _ptr(expert_offsets), _ptr(packed_gate_up), _ptr(h),
                                                _stream(stream)))
+
+
+def fp8_weight_bytes(cfg) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_fp8_weight_bytes", lib().moe_fp8_weight_bytes(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def moe_pack_weights_fp8(cfg, w_gate, w_up, image, stream=None):
+    _check("moe_pack_weights_fp8", lib().moe_pack_weights_fp8(
+        ctypes.byref(cfg), _ptr(w_gate), _ptr(w_up), _ptr(image), _stream(stream)))
+
+
+def pack_weights_fp8(cfg, w_gate, w_up, device="cuda", stream=None):
+    """The FP8 gate/up image of the weights (a load-time layout)."""
+    image = torch.empty(fp8_weight_bytes(cfg), dtype=torch.uint8, device=device)
+    moe_pack_weights_fp8(cfg, w_gate, w_up, image, stream)
+    return image
+
+
+def moe_ffn_gate_up_fp8_gather(cfg, x_codes, scale_zero, src_of, expert_offsets, image, h,
+                               stream=None):
+    _check("moe_ffn_gate_up_fp8_gather", lib().moe_ffn_gate_up_fp8_gather(
+        ctypes.byref(cfg), _ptr(x_codes), _ptr(scale_zero), _ptr(src_of), _ptr(expert_offsets),
+        _ptr(image), _ptr(h), _stream(stream)))
 
 
 def moe_route_stats(cfg, logits, bias, expert_offsets, rank_offsets, hist, rank_load, stats,

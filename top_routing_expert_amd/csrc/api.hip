@@ -466,6 +466,51 @@ int moe_ffn_gate_up_packed_gather(const moe_config* cfg, const void* x, const in
                        static_cast<hipStream_t>(stream));
 }
 
+// FP8 first GEMM: bf16 problems whose hidden size is a multiple of 128 (the
+// kernel's k loop takes two 64-wide FP8 steps at a time) and whose rows fit
+// the per-token quantiser.
+int check_fp8_gemm(const moe_config* cfg) {
+  int s = check_packed(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->d % 128 || !fp8_row_supported(*cfg)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+int moe_fp8_weight_bytes(const moe_config* cfg, size_t* bytes) {
+  int s = check_fp8_gemm(cfg);
+  if (s != MOE_OK) return s;
+  if (!bytes) return MOE_EINVAL;
+  *bytes = fp8_geom(*cfg).total;
+  return MOE_OK;
+}
+
+int moe_pack_weights_fp8(const moe_config* cfg, const void* w_gate, const void* w_up,
+                         void* image, void* stream) {
+  int s = check_fp8_gemm(cfg);
+  if (s != MOE_OK) return s;
+  if (!w_gate || !w_up || !image || !aligned16(w_gate) || !aligned16(w_up) ||
+      reinterpret_cast<uintptr_t>(image) % 256)
+    return MOE_EINVAL;
+  return status_of(launch_pack_weights_fp8(*cfg, w_gate, w_up, image,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int moe_ffn_gate_up_fp8_gather(const moe_config* cfg, const uint8_t* x_codes,
+                               const float* scale_zero, const int32_t* src_of,
+                               const int32_t* expert_offsets, const void* image, void* h,
+                               void* stream) {
+  int s = check_fp8_gemm(cfg);
+  if (s != MOE_OK) return s;
+  if (cfg->T == 0) return MOE_OK;
+  if (!x_codes || !scale_zero || !src_of || !expert_offsets || !image || !h ||
+      !aligned16(x_codes) || reinterpret_cast<uintptr_t>(scale_zero) % 8 ||
+      reinterpret_cast<uintptr_t>(image) % 256 || !aligned16(h))
+    return MOE_EINVAL;
+  return status_of(launch_ffn_gate_up_fp8_gather(*cfg, x_codes, scale_zero, src_of,
+                                                 expert_offsets, image, h,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 int moe_ffn_gate_up_packed_train(const moe_config* cfg, const void* act, const int32_t* src_of,
                                  const int32_t* expert_offsets, const void* packed_gate_up,
                                  void* h, void* a, void* u, void* stream) {

@@ -111,6 +111,22 @@ hipError_t launch_fp8_quantize(const moe_config& c, const void* x, void* codes, 
                                hipStream_t st);
 hipError_t launch_fp8_dequantize(const moe_config& c, const void* codes, const int32_t* src_of,
                                  const float* scale_zero, void* x_perm, hipStream_t st);
+// FP8 first GEMM (ffn_fp8.hip): the weight image's geometry, its packing
+// and the gather GEMM on per-token FP8 codes.
+struct Fp8Geom {
+  long rows;           // packed rows per expert (2 f: gate and up)
+  size_t codes_bytes;  // E * rows * d
+  size_t scale_off;    // byte offset of the per-row scales
+  size_t csum_off;     // byte offset of the per-row code sums
+  size_t total;        // image bytes
+};
+Fp8Geom fp8_geom(const moe_config& c);
+hipError_t launch_pack_weights_fp8(const moe_config& c, const void* wg, const void* wu,
+                                   void* image, hipStream_t st);
+hipError_t launch_ffn_gate_up_fp8_gather(const moe_config& c, const void* x_codes,
+                                         const float* scale_zero, const int32_t* src_of,
+                                         const int32_t* offs, const void* image, void* h,
+                                         hipStream_t st);
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_of,
                           const float* topk_w, void* out, hipStream_t st);
 

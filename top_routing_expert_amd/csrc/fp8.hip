@@ -27,6 +27,7 @@
 #include <cmath>
 
 #include "common.h"
+#include "fp8_codec.h"
 
 #pragma clang fp contract(off)
 
@@ -38,31 +39,6 @@ __device__ __forceinline__ float f32_mul(float a, float b) { return a * b; }
 __device__ __forceinline__ float f32_div(float a, float b) { return a / b; }  // correctly rounded
 
 constexpr int kF8VecsPerThread = 4;  // d <= 256 threads * 4 vectors * 8 = 8192
-constexpr float kF8Max = 448.0f;       // largest finite E4M3 value
-
-// |v| <= 448 -> E4M3 code, nearest with ties to even.  Below 2^-6 the code
-// is the number of 2^-9 steps.  Above, the float32 bit pattern already holds
-// the E4M3 fields: keep its top 3 mantissa bits, round the 20 dropped ones to
-// nearest even (a carry out of the mantissa moves to the next binade by
-// itself) and rebias the exponent from 127 to 7.
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a < 0x3C800000u)  // 2^-6
-    code = (uint32_t)rintf(f32_mul(__uint_as_float(a), 512.0f));
-  else
-    code = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
-  return code | sign;
-}
-
-__device__ __forceinline__ float e4m3_decode(uint32_t c) {
-  const uint32_t e4 = (c >> 3) & 15u, m3 = c & 7u;
-  const float mag = e4 == 0 ? ldexpf((float)m3, -9) : ldexpf((float)(8u + m3), (int)e4 - 10);
-  return (c & 0x80u) ? -mag : mag;
-}
-
 __device__ __forceinline__ float f8_wave_min(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
