@@ -417,6 +417,32 @@ int moe_layer_fwd_packed(const moe_config* cfg, const void* x, const void* w_rou
                          void* stream);
 
 /*
+ * moe_layer_fwd_packed_waved: moe_layer_fwd_packed with the experts in
+ * n_waves waves ([V4-overlap] Waved-EP section: the experts are split into
+ * waves; inside a wave dispatch, L1 + Act + L2 and combine run in order, and
+ * different waves run side by side).  On one GPU there is no exchange to
+ * hide, so what the waves overlap is the GEMMs' ragged last rounds and the
+ * combine: after the route and the index-only dispatch on `stream`, wave w
+ * (experts [w E / n_waves, (w + 1) E / n_waves), their packed images and
+ * offsets taken as a sub-table) runs its gather first GEMM, its second GEMM
+ * and the combine of the tokens whose highest-numbered chosen expert is in
+ * the wave, on `stream` for even w and `aux_stream` for odd w; before that
+ * combine the stream waits for wave w - 1, so every token is combined once,
+ * after all of its experts, exactly as moe_combine computes it.  On return
+ * `stream` waits for every wave (the call is as asynchronous as the others).
+ * Outputs are bit for bit those of moe_layer_fwd_packed.
+ * n_waves >= 1 and dividing E (MOE_EINVAL otherwise); bufs->x_perm must be
+ * NULL (the waves gather their rows); aux_stream NULL or equal to `stream`
+ * runs every wave on `stream`.  ws as for moe_layer_fwd_packed.  The call
+ * creates and destroys its n_waves + 1 HIP events.
+ */
+int moe_layer_fwd_packed_waved(const moe_config* cfg, const void* x, const void* w_router,
+                               const float* bias, const void* packed_gate_up,
+                               const void* packed_down, void* out, const moe_layer_bufs* bufs,
+                               void* ws, size_t ws_bytes, int n_waves, void* stream,
+                               void* aux_stream);
+
+/*
  * ---------------------------------------------------------------- backward
  * The layer's backward on the routing of its forward pass: the forward's
  * routing indices (topk_idx, slot_of, src_of, expert_offsets) are reused, not

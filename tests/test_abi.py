@@ -284,3 +284,18 @@ def test_fp8_gemm_entries_reject_before_launch():
                                   None) == B.MOE_EINVAL  # image not 256-byte aligned
     assert L.moe_ffn_gate_up_fp8_gather(ctypes.byref(ok), fake, fake, None, fake, fake, fake,
                                         None) == B.MOE_EINVAL
+
+
+def test_waved_layer_rejects_before_launch():
+    """Wave counts that do not divide E, a caller x_perm (the waves gather
+    their rows) and fp32 problems are refused on the host."""
+    L = B.lib()
+    fake = ctypes.c_void_p(4096)
+    cfg = B.config(C.SMALL["e8"])
+    bufs = B.MoELayerBufs(x_perm=4096)
+    for n_waves, b in ((0, None), (3, None), (16, None), (2, ctypes.byref(bufs))):
+        assert L.moe_layer_fwd_packed_waved(ctypes.byref(cfg), fake, fake, None, fake, fake, fake,
+                                            b, fake, 1 << 30, n_waves, None, None) == B.MOE_EINVAL
+    f32 = B.config(C.TINY_F32)
+    assert L.moe_layer_fwd_packed_waved(ctypes.byref(f32), fake, fake, None, fake, fake, fake,
+                                        None, fake, 1 << 30, 2, None, None) == B.MOE_EUNSUPPORTED

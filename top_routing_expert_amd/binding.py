@@ -35,7 +35,8 @@ EXPORTS = ("moe_strerror", "moe_validate", "moe_workspace_bytes", "moe_route", "
            "moe_ffn_backward", "moe_route_backward", "moe_unpermute_backward",
            "moe_ffn_gate_up_packed_train", "moe_packed_weight_bytes_backward",
            "moe_pack_weights_backward", "moe_permute_noalloc", "moe_noalloc_scratch_bytes",
-           "moe_fp8_weight_bytes", "moe_pack_weights_fp8", "moe_ffn_gate_up_fp8_gather")
+           "moe_fp8_weight_bytes", "moe_pack_weights_fp8", "moe_ffn_gate_up_fp8_gather",
+           "moe_layer_fwd_packed_waved")
 
 
 class MoEConfig(ctypes.Structure):
@@ -101,6 +102,8 @@ def lib() -> ctypes.CDLL:
         L.moe_unpermute_backward.argtypes = [cfgp, vp, vp, vp, vp, vp]
         L.moe_layer_fwd_packed.argtypes = [cfgp, vp, vp, vp, vp, vp, vp,
                                            ctypes.POINTER(MoELayerBufs), vp, sz, vp]
+        L.moe_layer_fwd_packed_waved.argtypes = [cfgp, vp, vp, vp, vp, vp, vp,
+                                                 ctypes.POINTER(MoELayerBufs), vp, sz, i32, vp, vp]
         for name in EXPORTS[1:]:
             getattr(L, name).restype = i32
         L.moe_noalloc_scratch_bytes.restype = sz
@@ -403,6 +406,21 @@ def moe_layer_fwd_packed(cfg, x, w_router, bias, packed_gate_up, packed_down, ou
 
 
 # ------------------------------------------------------------ device tensors
+def moe_layer_fwd_packed_waved(cfg, x, w_router, bias, packed_gate_up, packed_down, out,
+                               bufs: dict | None = None, ws=None, n_waves=2, stream=None,
+                               aux_stream=None):
+    b = None
+    if bufs is not None:
+        b = MoELayerBufs(**{n: _ptr(bufs.get(n)) for n in LAYER_BUF_FIELDS})
+    wp, wn = _ws(ws)
+    aux = None if aux_stream is None else (aux_stream if isinstance(aux_stream, int)
+                                           else aux_stream.cuda_stream)
+    _check("moe_layer_fwd_packed_waved", lib().moe_layer_fwd_packed_waved(
+        ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(packed_gate_up),
+        _ptr(packed_down), _ptr(out), ctypes.byref(b) if b is not None else None, wp, wn,
+        int(n_waves), _stream(stream), aux))
+
+
 def to_device(a, device="cuda") -> torch.Tensor:
     """numpy array -> device tensor; uint16 arrays are bf16 bit patterns."""
     import numpy as np

@@ -2,6 +2,8 @@
 // checks, workspace layout and the launch sequence of each entry point.
 // Nothing here allocates, frees or synchronises; every check runs before the
 // first launch, so a rejected call writes no output.
+#include <vector>
+
 #include "common.h"
 
 using namespace moe;
@@ -168,6 +170,47 @@ int do_combine(const moe_config& c, const void* y, const int32_t* slot, const fl
   return status_of(launch_combine(c, y, slot, w, out, st));
 }
 
+// The intermediates of one layer call: the caller's buffers where given,
+// else slices of ws.
+struct LayerPtrs {
+  float* logits;
+  int32_t *idx, *offs, *roffs, *slot, *src;
+  float* w;
+  void *xperm, *h, *y;
+  bool gather;  // the first GEMM gathers its rows (no x_perm is written)
+};
+
+// Route and dispatch of moe_layer_fwd / moe_layer_fwd_packed(_waved), after
+// every argument check passed: with `gather` and no caller x_perm the
+// dispatch writes indices only.
+int layer_front(const moe_config& c, const void* x, const void* w_router, const float* bias,
+                const moe_layer_bufs* bufs, void* ws, size_t ws_bytes, hipStream_t st,
+                bool gather, LayerPtrs* P) {
+  const LayerLayout L = layer_layout(c, bufs);
+  int s;
+  if ((s = check_ws(L.total, ws, ws_bytes)) != MOE_OK) return s;
+  char* base = static_cast<char*>(ws);
+  auto pick = [&](void* given, size_t at) -> void* { return given ? given : base + at; };
+  const moe_layer_bufs none{};
+  const moe_layer_bufs& b = bufs ? *bufs : none;
+  void* scratch = base + L.scratch;
+  P->logits = static_cast<float*>(pick(b.logits, L.logits));
+  P->idx = static_cast<int32_t*>(pick(b.topk_idx, L.idx));
+  P->w = static_cast<float*>(pick(b.topk_w, L.w));
+  P->offs = static_cast<int32_t*>(pick(b.expert_offsets, L.offs));
+  P->roffs = static_cast<int32_t*>(pick(b.rank_offsets, L.roffs));
+  P->slot = static_cast<int32_t*>(pick(b.slot_of, L.slot));
+  P->src = static_cast<int32_t*>(pick(b.src_of, L.src));
+  P->xperm = pick(b.x_perm, L.xperm);
+  P->h = pick(b.h, L.h);
+  P->y = pick(b.y_perm, L.y);
+  P->gather = gather && !b.x_perm;
+  if ((s = do_route(c, x, w_router, bias, P->logits, P->idx, P->w, scratch, st)) != MOE_OK)
+    return s;
+  return do_permute(c, P->gather ? nullptr : x, P->idx, P->offs, P->roffs, P->slot, P->src,
+                    P->gather ? nullptr : P->xperm, scratch, st);
+}
+
 // moe_layer_fwd body shared by the row-major and packed-weight variants;
 // `ffn(act, src, offs, h, y, stream)` runs the grouped FFN on act = x_perm
 // (src NULL) or, with `gather` and no caller x_perm, on act = x with the rows
@@ -177,32 +220,68 @@ template <typename Ffn>
 int run_layer(const moe_config& c, const void* x, const void* w_router, const float* bias,
               void* out, const moe_layer_bufs* bufs, void* ws, size_t ws_bytes, void* stream,
               bool gather, Ffn&& ffn) {
-  const LayerLayout L = layer_layout(c, bufs);
-  int s;
-  if ((s = check_ws(L.total, ws, ws_bytes)) != MOE_OK) return s;
-  char* base = static_cast<char*>(ws);
-  auto pick = [&](void* given, size_t at) -> void* { return given ? given : base + at; };
-  const moe_layer_bufs none{};
-  const moe_layer_bufs& b = bufs ? *bufs : none;
-  void* scratch = base + L.scratch;
-  float* logits = static_cast<float*>(pick(b.logits, L.logits));
-  int32_t* idx = static_cast<int32_t*>(pick(b.topk_idx, L.idx));
-  float* w = static_cast<float*>(pick(b.topk_w, L.w));
-  int32_t* offs = static_cast<int32_t*>(pick(b.expert_offsets, L.offs));
-  int32_t* roffs = static_cast<int32_t*>(pick(b.rank_offsets, L.roffs));
-  int32_t* slot = static_cast<int32_t*>(pick(b.slot_of, L.slot));
-  int32_t* src = static_cast<int32_t*>(pick(b.src_of, L.src));
-  void* xperm = pick(b.x_perm, L.xperm);
-  void* h = pick(b.h, L.h);
-  void* y = pick(b.y_perm, L.y);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((s = do_route(c, x, w_router, bias, logits, idx, w, scratch, st)) != MOE_OK) return s;
-  const bool g = gather && !b.x_perm;
-  if ((s = do_permute(c, g ? nullptr : x, idx, offs, roffs, slot, src, g ? nullptr : xperm,
-                      scratch, st)) != MOE_OK)
+  LayerPtrs P;
+  int s;
+  if ((s = layer_front(c, x, w_router, bias, bufs, ws, ws_bytes, st, gather, &P)) != MOE_OK)
     return s;
-  if ((s = ffn(g ? x : xperm, g ? src : nullptr, offs, h, y, st)) != MOE_OK) return s;
-  return do_combine(c, y, slot, w, out, st);
+  if ((s = ffn(P.gather ? x : P.xperm, P.gather ? P.src : nullptr, P.offs, P.h, P.y, st)) !=
+      MOE_OK)
+    return s;
+  return do_combine(c, P.y, P.slot, P.w, out, st);
+}
+
+// Events of one waved call, destroyed on every path out.
+struct EventSet {
+  std::vector<hipEvent_t> ev;
+  ~EventSet() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);  // released once their waits are done
+  }
+  bool make(int n) {
+    for (int i = 0; i < n; ++i) {
+      hipEvent_t e;
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return false;
+      ev.push_back(e);
+    }
+    return true;
+  }
+};
+
+// Expert waves after the dispatch: wave w = experts [w per, (w + 1) per) runs
+// its first GEMM (rows gathered), its second GEMM and then the combine of the
+// tokens whose highest-numbered expert is in the wave, on stream ss[w % 2];
+// before that combine the stream waits for wave w - 1 (the other stream), so
+// every token is combined once, after all of its experts, exactly as the
+// serial combine computes it.  The caller's stream waits for the last wave.
+int run_waves(const moe_config& c, const void* x, const LayerPtrs& P, const void* pgu,
+              const void* pd, void* out, int n_waves, hipStream_t st, hipStream_t aux) {
+  if (c.T == 0) return MOE_OK;
+  const int per = c.E / n_waves;
+  const bool two = aux && aux != st;
+  hipStream_t ss[2] = {st, two ? aux : st};
+  EventSet E;
+  if (!E.make(n_waves + 1)) return MOE_EHIP;
+  hipEvent_t dispatched = E.ev[n_waves];
+  if (two && (hipEventRecord(dispatched, st) != hipSuccess ||
+              hipStreamWaitEvent(aux, dispatched, 0) != hipSuccess))
+    return MOE_EHIP;
+  const size_t gu_e = packed_bytes(c, true) / c.E, dn_e = packed_bytes(c, false) / c.E;
+  moe_config sub = c;
+  sub.E = per;
+  for (int w = 0; w < n_waves; ++w) {
+    hipStream_t s = ss[w & 1];
+    const int32_t* offs_w = P.offs + (size_t)w * per;
+    const char* pgu_w = static_cast<const char*>(pgu) + (size_t)w * per * gu_e;
+    const char* pd_w = static_cast<const char*>(pd) + (size_t)w * per * dn_e;
+    if (launch_ffn_gate_up_packed_gather(sub, x, P.src, offs_w, pgu_w, P.h, s) != hipSuccess ||
+        launch_ffn_down_packed(sub, P.h, offs_w, pd_w, P.y, s) != hipSuccess)
+      return MOE_EHIP;
+    if (two && w > 0 && hipStreamWaitEvent(s, E.ev[w - 1], 0) != hipSuccess) return MOE_EHIP;
+    if (launch_combine(c, P.y, P.slot, P.w, out, s, P.idx, w, per) != hipSuccess) return MOE_EHIP;
+    if (hipEventRecord(E.ev[w], s) != hipSuccess) return MOE_EHIP;
+  }
+  if (two && hipStreamWaitEvent(st, E.ev[n_waves - 1], 0) != hipSuccess) return MOE_EHIP;
+  return MOE_OK;
 }
 
 }  // namespace
@@ -555,6 +634,30 @@ int moe_layer_fwd_packed(const moe_config* cfg, const void* x, const void* w_rou
                      return do_ffn_packed(*cfg, act, src, offs, packed_gate_up, packed_down, h, y,
                                           st);
                    });
+}
+
+int moe_layer_fwd_packed_waved(const moe_config* cfg, const void* x, const void* w_router,
+                               const float* bias, const void* packed_gate_up,
+                               const void* packed_down, void* out, const moe_layer_bufs* bufs,
+                               void* ws, size_t ws_bytes, int n_waves, void* stream,
+                               void* aux_stream) {
+  int s = check_routing(cfg);
+  if (s != MOE_OK) return s;
+  if ((s = check_packed(cfg)) != MOE_OK) return s;
+  if (n_waves < 1 || cfg->E % n_waves) return MOE_EINVAL;
+  if (bufs && bufs->x_perm) return MOE_EINVAL;  // the waves gather their rows
+  if (cfg->T > 0 && (!x || !w_router || !packed_gate_up || !packed_down || !out || !aligned16(x) ||
+                     !aligned16(packed_gate_up) || !aligned16(packed_down)))
+    return MOE_EINVAL;
+  if (bufs && ((bufs->h && !aligned16(bufs->h)) || (bufs->y_perm && !aligned16(bufs->y_perm))))
+    return MOE_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  LayerPtrs P;
+  if ((s = layer_front(*cfg, x, w_router, bias, bufs, ws, ws_bytes, st, /*gather=*/true, &P)) !=
+      MOE_OK)
+    return s;
+  return run_waves(*cfg, x, P, packed_gate_up, packed_down, out, n_waves, st,
+                   static_cast<hipStream_t>(aux_stream));
 }
 
 int moe_combine_backward(const moe_config* cfg, const void* d_out, const void* y_perm,

@@ -17,15 +17,26 @@ constexpr int kMaxKC = 16;
 // KC: k rounded up to 1, 2, 4, 8 or kMaxKC; U: 16-byte vectors per lane in
 // flight per expert row, so that every lane keeps U * KC <= 8 loads in flight
 // (a token's row is read in few memory round trips).
+// wave >= 0: only the tokens whose highest-numbered chosen expert lies in
+// experts [wave * per, (wave + 1) * per) -- the tokens whose last expert wave
+// that is (the waved layer combines each token once, after that wave).
 template <int KC, int U>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(const u32x4* __restrict__ y,
                                                            const int32_t* __restrict__ slot_of,
                                                            const float* __restrict__ topk_w,
                                                            u32x4* __restrict__ out, int T, int k,
-                                                           int row_vecs) {
+                                                           int row_vecs,
+                                                           const int32_t* __restrict__ topk_idx,
+                                                           int wave, int per) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  if (wave >= 0) {  // wave-uniform test of the token's last expert wave
+    int e = lane < k ? topk_idx[(size_t)t * k + lane] : 0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) e = max(e, __shfl_xor(e, o));
+    if (e / per != wave) return;
+  }
   int p = 0;
   float g = 0.f;
   if (lane < k) {
@@ -113,22 +124,27 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float4* __restri
 }
 
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_of,
-                          const float* topk_w, void* out, hipStream_t st) {
+                          const float* topk_w, void* out, hipStream_t st,
+                          const int32_t* topk_idx, int wave, int per) {
   const dim3 grid(div_up(c.T, 4));
   if (c.dtype == MOE_BF16) {
     auto* yv = static_cast<const u32x4*>(y_perm);
     auto* ov = static_cast<u32x4*>(out);
     const int rv = c.d / 8;
+#define MOE_COMBINE(KC, U)                                                               \
+  combine_bf16_kernel<KC, U><<<grid, 256, 0, st>>>(yv, slot_of, topk_w, ov, c.T, c.k, rv, \
+                                                   topk_idx, wave, per)
     if (c.k <= 1)
-      combine_bf16_kernel<1, 8><<<grid, 256, 0, st>>>(yv, slot_of, topk_w, ov, c.T, c.k, rv);
+      MOE_COMBINE(1, 8);
     else if (c.k <= 2)
-      combine_bf16_kernel<2, 4><<<grid, 256, 0, st>>>(yv, slot_of, topk_w, ov, c.T, c.k, rv);
+      MOE_COMBINE(2, 4);
     else if (c.k <= 4)
-      combine_bf16_kernel<4, 2><<<grid, 256, 0, st>>>(yv, slot_of, topk_w, ov, c.T, c.k, rv);
+      MOE_COMBINE(4, 2);
     else if (c.k <= 8)
-      combine_bf16_kernel<8, 1><<<grid, 256, 0, st>>>(yv, slot_of, topk_w, ov, c.T, c.k, rv);
+      MOE_COMBINE(8, 1);
     else
-      combine_bf16_kernel<kMaxKC, 1><<<grid, 256, 0, st>>>(yv, slot_of, topk_w, ov, c.T, c.k, rv);
+      MOE_COMBINE(kMaxKC, 1);
+#undef MOE_COMBINE
   } else {
     combine_f32_kernel<<<grid, 256, 0, st>>>(static_cast<const float4*>(y_perm), slot_of, topk_w,
                                              static_cast<float4*>(out), c.T, c.k, c.d / 4);

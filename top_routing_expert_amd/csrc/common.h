@@ -127,8 +127,11 @@ hipError_t launch_ffn_gate_up_fp8_gather(const moe_config& c, const void* x_code
                                          const float* scale_zero, const int32_t* src_of,
                                          const int32_t* offs, const void* image, void* h,
                                          hipStream_t st);
+// topk_idx != NULL and wave >= 0 (bf16 only): combine only the tokens whose
+// highest-numbered chosen expert is in experts [wave * per, (wave + 1) * per).
 hipError_t launch_combine(const moe_config& c, const void* y_perm, const int32_t* slot_of,
-                          const float* topk_w, void* out, hipStream_t st);
+                          const float* topk_w, void* out, hipStream_t st,
+                          const int32_t* topk_idx = nullptr, int wave = -1, int per = 1);
 
 hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t st);
 
