@@ -582,6 +582,63 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // epilogue: acc[ii][jj][4 g + r] = C[fragment row 8 g + 4 lk + r][token lane & 31]
+    if constexpr (WF == 2 && !SAVE) {
+      // Whole-slab tiles: the bf16 output tile goes through the (now idle)
+      // LDS ring, rows of TN features, 16-byte pieces XOR-swizzled with the
+      // row so that a store's 32 rows land on different banks, then out in
+      // whole row segments: every store instruction writes 64 / PPR full
+      // rows of the tile instead of 16 bytes in each of 32 rows.
+      constexpr int RB = TN * 2;    // bytes of one row of the output tile
+      constexpr int PPR = RB / 16;  // 16-byte pieces per row
+      constexpr int RPI = 64 / PPR; // rows per store instruction
+      static_assert(TM * RB <= NSLOT * HB, "the output tile must fit the ring");
+      __syncthreads();  // every wave's last fragment reads of the ring are done
+      auto put = [&](int r, int nl, u32x2 v) {  // tile row r, tile feature nl (a multiple of 4)
+        const int q = nl >> 3;
+        *reinterpret_cast<u32x2*>(tokb + r * RB + ((q ^ (r & (PPR - 1))) << 4) +
+                                  ((nl >> 2) & 1) * 8) = v;
+      };
+#pragma unroll
+      for (int jj = 0; jj < JW; ++jj) {
+        const int r = 32 * jj + (lane & 31);
+#pragma unroll
+        for (int ii = 0; ii < WL; ++ii) {
+          if (GATED) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+              float hv[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float gt = acc[ii][jj][4 * g + q], up = acc[ii][jj][4 * g + 8 + q];
+                hv[q] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+              }
+              u32x2 pk;
+              pk.x = pack_bf16x2(hv[0], hv[1]);
+              pk.y = pack_bf16x2(hv[2], hv[3]);
+              put(r, wave * (TN / 4) + 16 * ii + 8 * g + 4 * lk, pk);
+            }
+          } else {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              u32x2 pk;
+              pk.x = pack_bf16x2(acc[ii][jj][4 * g], acc[ii][jj][4 * g + 1]);
+              pk.y = pack_bf16x2(acc[ii][jj][4 * g + 2], acc[ii][jj][4 * g + 3]);
+              put(r, wave * (TN / 4) + 32 * ii + 8 * g + 4 * lk, pk);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      const int q = lane % PPR;
+      const int n = slab * TN + 8 * q;
+      for (int rb = wave * RPI; rb < 32 * JW; rb += 4 * RPI) {
+        const int r = rb + lane / PPR;
+        if (r < nrow && n < N)
+          *reinterpret_cast<u32x4*>(out + (size_t)(row0 + r) * N + n) =
+              *reinterpret_cast<const u32x4*>(tokb + r * RB + ((q ^ (r & (PPR - 1))) << 4));
+      }
+      return;
+    }
 #pragma unroll
     for (int jj = 0; jj < JW; ++jj) {
       const int p = row0 + 32 * (jb + jj) + (lane & 31);
