@@ -96,6 +96,9 @@ ROUTING_CASES = [
     dict(E=12, k=3, renorm=0),
     dict(E=100, k=5, presel=20, renorm=1),
     dict(E=32, k=4, n_group=32, topk_group=4),
+    # 64 < E <= 256 runs 32 lanes per token when n_group <= 32, else 64
+    dict(E=128, k=6, n_group=32, topk_group=8),
+    dict(E=192, k=8, n_group=64, topk_group=16),
 ]
 
 

@@ -15,8 +15,8 @@
 //    products that the top-k kernel sums in a fixed order, so logits stay
 //    bitwise reproducible (no float atomics) while the grid still covers the
 //    256 CUs.
-//  * Top-k: a group of LPT = min(64, pow2 >= E) lanes per token; each lane
-//    holds E/LPT scores.  Every selection round is one argmax over 64-bit keys
+//  * Top-k: a group of LPT = min(64, pow2 >= E) lanes per token (32 for
+//    64 < E <= 256 with at most 32 groups); each lane holds E/LPT scores.  Every selection round is one argmax over 64-bit keys
 //    (order-preserving score bits, then inverted index), reduced with xor
 //    shuffles: highest score wins, ties go to the lowest expert index.
 #include "common.h"
@@ -69,49 +69,55 @@ __global__ __launch_bounds__(256) void router_gemm_bf16_kernel(const uint16_t* _
 #pragma unroll
   for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 wreg[WLOADS];
-  u32x4 xv[2], xn[2];
+  // Chunks are loaded two ahead through a ring of three register slots:
+  // chunk c sits in slot (c - c_beg) % 3, its W half in LDS stage (c - c_beg) & 1.
+  // In iteration c, slot (c+2) is refilled (its chunk c-1 is consumed), chunk
+  // c is computed, then chunk c+1's W moves to the other LDS stage.  The loop
+  // is unrolled by three so that every slot index is static.
+  u32x4 wreg[3][WLOADS];
+  u32x4 xr[3][2];
+  auto issue = [&](int slot, int c) {
+#pragma unroll
+    for (int i = 0; i < WLOADS; ++i)
+      if (wact[i]) wreg[slot][i] = wrow[i][c * 8];
+    xr[slot][0] = xrow[c * 8 + 2 * g];
+    xr[slot][1] = xrow[c * 8 + 2 * g + 1];
+  };
   if (c_beg < c_end) {
+    issue(0, c_beg);
+    if (c_beg + 1 < c_end) issue(1, c_beg + 1);
 #pragma unroll
     for (int i = 0; i < WLOADS; ++i)
-      if (wact[i]) wreg[i] = wrow[i][c_beg * 8];
-    xv[0] = xrow[c_beg * 8 + 2 * g];
-    xv[1] = xrow[c_beg * 8 + 2 * g + 1];
-#pragma unroll
-    for (int i = 0; i < WLOADS; ++i)
-      if (wact[i]) sW[0][wdst[i]] = wreg[i];
+      if (wact[i]) sW[0][wdst[i]] = wreg[0][i];
   }
   __syncthreads();
 
-  for (int c = c_beg; c < c_end; ++c) {
-    const int st = (c - c_beg) & 1;
-    const bool more = c + 1 < c_end;
-    if (more) {
+  for (int c0 = c_beg; c0 < c_end; c0 += 3) {
 #pragma unroll
-      for (int i = 0; i < WLOADS; ++i)
-        if (wact[i]) wreg[i] = wrow[i][(c + 1) * 8];
-      xn[0] = xrow[(c + 1) * 8 + 2 * g];
-      xn[1] = xrow[(c + 1) * 8 + 2 * g + 1];
-    }
+    for (int r = 0; r < 3; ++r) {
+      const int c = c0 + r;
+      if (c < c_end) {  // block-uniform
+        const int st = (c - c_beg) & 1;
+        if (c + 2 < c_end) issue((r + 2) % 3, c + 2);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bf16x8 b = as_bf16x8(xv[s]);
-      const int q = 2 * g + s;
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8 b = as_bf16x8(xr[r][s]);
+          const int q = 2 * g + s;
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int r = f * 16 + (lane & 15);
-        const bf16x8 a = as_bf16x8(sW[st][r * 8 + (q ^ (r & 7))]);
-        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[f], 0, 0, 0);
+          for (int f = 0; f < NF; ++f) {
+            const int row = f * 16 + (lane & 15);
+            const bf16x8 a = as_bf16x8(sW[st][row * 8 + (q ^ (row & 7))]);
+            acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[f], 0, 0, 0);
+          }
+        }
+        if (c + 1 < c_end) {
+#pragma unroll
+          for (int i = 0; i < WLOADS; ++i)
+            if (wact[i]) sW[st ^ 1][wdst[i]] = wreg[(r + 1) % 3][i];
+        }
+        __syncthreads();
       }
     }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < WLOADS; ++i)
-        if (wact[i]) sW[st ^ 1][wdst[i]] = wreg[i];
-      xv[0] = xn[0];
-      xv[1] = xn[1];
-    }
-    __syncthreads();
   }
 
   // acc[f][i] = z[token = lane&15][expert = e0 + 16f + 4(lane>>4) + i]
@@ -473,6 +479,10 @@ hipError_t launch_topk(const moe_config& c, const float* partial, int splits, co
   int lpt = 1;
   while (lpt < c.E && lpt < 64) lpt <<= 1;
   if (lpt < 2) lpt = 2;
+  // 64 < E <= 256: 32 lanes of 8 scores each, two tokens per wave (fewer
+  // shuffle steps per selection round; E=256: 97 -> 92 us for T=8192).  The
+  // group maxima sit one per lane, so this needs n_group <= 32.
+  if (c.E > 64 && c.E <= 256 && c.n_group <= 32) lpt = 32;
   const int tpb = 4 * (64 / lpt);
   const dim3 grid(div_up(c.T, tpb));
 #define MOE_TOPK(L, P)                                                                        \
@@ -484,12 +494,15 @@ hipError_t launch_topk(const moe_config& c, const float* partial, int splits, co
     case 4: MOE_TOPK(4, 1); break;
     case 8: MOE_TOPK(8, 1); break;
     case 16: MOE_TOPK(16, 1); break;
-    case 32: MOE_TOPK(32, 1); break;
+    case 32:
+      if (c.E > 64)
+        MOE_TOPK(32, 8);
+      else
+        MOE_TOPK(32, 1);
+      break;
     default:
       if (c.E <= 64)
         MOE_TOPK(64, 1);
-      else if (c.E <= 256)
-        MOE_TOPK(64, 4);
       else
         MOE_TOPK(64, kMaxEPL);
       break;
