@@ -83,6 +83,8 @@ BAD = [
     (dict(E=2048, k=2), B.MOE_EUNSUPPORTED),
     (dict(k=17, E=64), B.MOE_EUNSUPPORTED),
     (dict(T=1 << 20, d=4096), B.MOE_EUNSUPPORTED),  # (T*k)*max(d,f) >= 2^31
+    # (T*k)*max(d,f) = 2^64 would wrap in 64-bit arithmetic
+    (dict(T=1 << 30, k=8, E=8, d=1 << 30, f=64), B.MOE_EUNSUPPORTED),
 ]
 
 

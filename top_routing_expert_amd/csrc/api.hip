@@ -25,9 +25,11 @@ int check_core(const moe_config* c) {
   if (c->k > 16 || c->E > kMaxExperts) return MOE_EUNSUPPORTED;
   if (c->dtype == MOE_BF16 && (c->d % 64 || c->f % 64)) return MOE_EUNSUPPORTED;
   if (c->dtype == MOE_F32 && (c->d % 4 || c->f % 4)) return MOE_EUNSUPPORTED;
-  const long rows = (long)c->T * c->k;
+  const long rows = (long)c->T * c->k;  // < 2^35 (k <= 16)
   const long wide = c->d > c->f ? c->d : c->f;
-  if (rows * wide > kI32Max || (long)c->T * c->E > kI32Max) return MOE_EUNSUPPORTED;
+  // rows * wide > kI32Max, without forming the product (it can pass 2^63)
+  if ((rows > 0 && wide > kI32Max / rows) || (long)c->T * c->E > kI32Max)
+    return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
