@@ -324,11 +324,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char tokb[NSLOT * HB];
   __shared__ int s_tile[4];
   __shared__ int s_total;
+  // expert order: every expert's rows and first tile, built once (wave 0)
+  __shared__ int s_o0[kTileTableMax], s_o1[kTileTableMax], s_start[kTileTableMax];
 
   const int G = (int)gridDim.x;
   const int qp = (G >> 3) * (int)(blockIdx.x & 7) + (int)(blockIdx.x >> 3);
   if (threadIdx.x < 64) {
-    const int n = count_row_tiles<TM>(offs, E, rows, (int)threadIdx.x) * slabs * NT;
+    const int n = sized ? count_row_tiles<TM>(offs, E, rows, (int)threadIdx.x) * slabs * NT
+                        : build_tile_table<TM>(offs, E, rows, slabs * NT, (int)threadIdx.x, s_o0,
+                                               s_o1, s_start);
     if (threadIdx.x == 0) s_total = n;
   }
   const uint32_t lds0 = (uint32_t)(size_t)(const __attribute__((address_space(3))) void*)tokb;
@@ -342,7 +346,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
   if (wave == 0) {  // s_total and s_tile: written and read in order by this one wave
     const int L = round * G + ((round & 1) ? G - 1 - qp : qp);
     if (lane == 0) s_tile[0] = -1;
-    if (L < s_total) locate_tile<TM>(offs, E, rows, slabs * NT, band, L, lane, s_tile, sized);
+    if (L < s_total) {
+      if (sized)
+        locate_tile<TM>(offs, E, rows, slabs * NT, band, L, lane, s_tile, true);
+      else
+        locate_in_table<TM>(s_o0, s_o1, s_start, E, slabs * NT, band, L, lane, s_tile);
+    }
   }
   __syncthreads();
   const int e = __builtin_amdgcn_readfirstlane(s_tile[0]);

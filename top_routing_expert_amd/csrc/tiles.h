@@ -100,6 +100,62 @@ __device__ __forceinline__ void locate_tile(const int32_t* __restrict__ offs, in
   }
 }
 
+// Expert-order tile table of a persistent block, built once per launch by ONE
+// whole wave: for every expert its row range [o0, o1) (clamped as above) and
+// the number of tiles before it (`start`, non-decreasing).  Returns the total
+// tile count.  Locating a tile is then a search over LDS (locate_in_table)
+// instead of a walk over the offsets in global memory.
+constexpr int kTileTableMax = 1024;  // experts the table holds (every E accepted)
+template <int TM>
+__device__ __forceinline__ int build_tile_table(const int32_t* __restrict__ offs, int E, int rows,
+                                                int n_tiles, int lane, int* t_o0, int* t_o1,
+                                                int* t_start) {
+  int carry = 0;
+  for (int b0 = 0; b0 < E; b0 += 64) {
+    const int e = b0 + lane;
+    int o0 = 0, o1 = 0;
+    if (e < E) {
+      o0 = min(max(offs[e], 0), rows);
+      o1 = min(max(offs[e + 1], o0), rows);
+    }
+    const int cnt = (o1 - o0 + TM - 1) / TM * n_tiles;
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (e < E) {
+      t_o0[e] = o0;
+      t_o1[e] = o1;
+      t_start[e] = carry + incl - cnt;
+    }
+    carry += __shfl(incl, 63);
+  }
+  return carry;
+}
+
+// Tile L (0 <= L < total) of the table, expert order: its expert is the last
+// one whose start is <= L (empty experts before it share its start, those
+// after it start past L), found by counting with ballots.  ONE whole wave.
+template <int TM>
+__device__ __forceinline__ void locate_in_table(const int* t_o0, const int* t_o1,
+                                                const int* t_start, int E, int n_tiles, int band,
+                                                int L, int lane, int* s_tile) {
+  int n = 0;
+  for (int b0 = 0; b0 < E; b0 += 64) {
+    const int e = b0 + lane;
+    const int c = __popcll(__ballot(e < E && t_start[e] <= L));
+    n += c;
+    if (c < 64) break;  // wave-uniform: start is non-decreasing
+  }
+  const int e = max(n - 1, 0);
+  if (lane == 0) {
+    const int o0 = t_o0[e], o1 = t_o1[e];
+    expert_tile(e, o0, o1, (o1 - o0 + TM - 1) / TM, n_tiles, band, L - t_start[e], s_tile);
+  }
+}
+
 // One block per tile of a grid sized for the worst case, called by ONE whole
 // wave.  The actual tile count (known only on the device) is dealt to the 8
 // XCDs (the hardware hands blocks to XCDs round-robin) in equal contiguous
