@@ -640,11 +640,26 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_packed_kernel(
       __syncthreads();
       const int q = lane % PPR;
       const int n = slab * TN + 8 * q;
-      for (int rb = wave * RPI; rb < 32 * JW; rb += 4 * RPI) {
-        const int r = rb + lane / PPR;
-        if (r < nrow && n < N)
-          *reinterpret_cast<u32x4*>(out + (size_t)(row0 + r) * N + n) =
-              *reinterpret_cast<const u32x4*>(tokb + r * RB + ((q ^ (r & (PPR - 1))) << 4));
+      // Pass i of this wave covers tile rows wave RPI + 4 RPI i + [0, RPI): every
+      // row read lies inside the staged tile.  Eight reads go out before their
+      // stores (a read-wait-store loop waited for every LDS read in turn).
+      constexpr int STEP = 4 * RPI, PASSES = 32 * JW / STEP, BATCH = 8;
+      static_assert(32 * JW % STEP == 0, "whole passes");
+#pragma unroll
+      for (int i0 = 0; i0 < PASSES; i0 += BATCH) {
+        u32x4 v[BATCH];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          const int r = wave * RPI + (i0 + i) * STEP + lane / PPR;
+          if (i0 + i < PASSES)
+            v[i] = *reinterpret_cast<const u32x4*>(tokb + r * RB + ((q ^ (r & (PPR - 1))) << 4));
+        }
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+          const int r = wave * RPI + (i0 + i) * STEP + lane / PPR;
+          if (i0 + i < PASSES && r < nrow && n < N)
+            *reinterpret_cast<u32x4*>(out + (size_t)(row0 + r) * N + n) = v[i];
+        }
       }
       return;
     }
