@@ -58,6 +58,40 @@ def test_packed_ffn_matches_oracle(case):
     _check(shape, xp_np, offs_np, wg, wu, wd, h, y)
 
 
+def _counts_many(E):
+    counts = np.zeros(E, dtype=np.int64)
+    if E == 1024:  # mostly empty; live experts on both sides of 64-expert chunk edges
+        for e, c in {0: 3, 63: 300, 64: 1, 65: 256, 127: 17, 128: 0, 500: 40, 1023: 5}.items():
+            counts[e] = c
+    elif E == 200:  # a partial last chunk and a run of empty experts across a chunk edge
+        counts[:] = np.random.default_rng(200).integers(0, 40, size=E)
+        counts[60:70] = 0
+        counts[199] = 0
+    else:  # 256 one-row experts and a large one
+        counts[:] = 1
+        counts[E - 1] = 600
+    return counts
+
+
+@pytest.mark.parametrize("E", [1024, 200, 256])
+def test_packed_many_experts(E):
+    """Layers of more than 16 experts find their tiles in a per-launch table of
+    expert rows and first tiles: up to 1024 experts, empty runs on chunk
+    edges, a partial last chunk, many one-row experts."""
+    d, f = 128, 192
+    counts = _counts_many(E)
+    log(f"[ffn-packed] {E} experts, {int((counts > 0).sum())} with rows")
+    A = int(counts.sum())
+    shape = C.E8_D4096.replace(name="ffn-packed-many", T=A, k=1, E=E, d=d, f=f, ep_ranks=1)
+    offs_np = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    xp_np = I.make_x(shape, seed=81)
+    wg, wu, wd = _weights(shape, 82)
+    dev = [B.to_device(a) for a in (xp_np, wg, wu, wd)]
+    offs = torch.from_numpy(offs_np).cuda()
+    h, y = _run_packed(shape, dev[0], offs, *dev[1:])
+    _check(shape, xp_np, offs_np, wg, wu, wd, h, y)
+
+
 # Problems with enough tiles to fill the chip run whole-slab tiles of up to
 # 256 rows (the others half-slab tiles of up to 320 rows): these two shapes
 # reach the whole-slab kernel for both GEMMs (E=64) and for the gate/up GEMM
