@@ -54,6 +54,23 @@ def test_route_gemm_expert_blocks(over):
     _check_route(shape, inp, buf)
 
 
+# The E <= 16 stream over x: one k-pair, a split count that does not divide
+# d's k-pairs, many splits of short k ranges, and a very wide d (1152 k-pairs
+# over 16 splits) with a handful of tokens
+SKINNY_SHAPES = [dict(E=8, k=2, T=70, d=64), dict(E=16, k=2, T=333, d=4160),
+                 dict(E=6, k=2, T=1500, d=2048), dict(E=8, k=2, T=5, d=73728)]
+
+
+@pytest.mark.parametrize("over", SKINNY_SHAPES, ids=[str(o) for o in SKINNY_SHAPES])
+def test_route_skinny_shapes(over):
+    shape = C.E8_D4096.replace(name="route-skinny", ep_ranks=1, renorm=1, **over)
+    log(f"[route] E <= 16 stream {over}")
+    inp = I.make_inputs(shape, seed=29, with_experts=False)
+    dev, buf = upload(inp), alloc(shape)
+    _route(shape, dev, buf)
+    _check_route(shape, inp, buf)
+
+
 @pytest.mark.parametrize("key", list(C.SMALL), ids=list(C.SMALL))
 def test_route_small_shapes(key):
     shape = C.SMALL[key]
