@@ -16,7 +16,8 @@ Default workload (the line's `value`): T=8192 tokens, d=7168, E=256 experts
 in 8 groups of 32 with the best 4 groups kept, top-8, SwiGLU f=2048, bf16 --
 the largest of the five workloads.  The four others (the fp32 tiny layer, the
 E=8, E=64 and E=16 layers) are run after it, each timed the same way, and
-reported under "workloads".
+reported under "workloads", and the FP8 first GEMM and the expert waves
+are timed on the default workload under "variants".
 
 `forward_calls` is the one definition of the timed call sequence; the
 full-size parity tests run the same function.
@@ -110,11 +111,18 @@ def parse(argv=None):
                     help="skip the extra pass that evicts the 256 MB MALL before every step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--variants", default="auto", choices=("auto", "none", "all"),
+                    help="also time, on the line's workload, the FP8 first GEMM path and the "
+                         "expert waves (reported under \"variants\"); 'auto' = with the default "
+                         "line only")
     a = ap.parse_args(argv)
     a.shape = shape_of(a.config)
+    default_line = not (a.config != str(HEADLINE) or a.backward or a.diagnostics
+                        or a.dispatch != "gather" or a.ffn != "packed")
+    if a.variants == "auto":
+        a.variants = "all" if default_line else "none"
     if a.also == "auto":
-        a.also = "none" if (a.config != str(HEADLINE) or a.backward or a.diagnostics
-                            or a.dispatch != "gather" or a.ffn != "packed") else "1,2,3,4"
+        a.also = "1,2,3,4" if default_line else "none"
     a.others = [] if a.also == "none" else [shape_of(s) for s in a.also.split(",") if s]
     return a
 
@@ -561,6 +569,73 @@ def run_forward(shape, a, inp, copy_gbs=None, headline=True):
     return rec, idx_gpu
 
 
+def time_variants(shape, a, inp, copy_gbs):
+    """The rows built beside the timed path, timed on the same workload: the FP8
+    first GEMM (per-token FP8 codes x E4M3 expert weights; a different model,
+    so never the line's value) and the layer in expert waves (bit for bit the
+    serial layer).  A failure is recorded, not raised: the line stays."""
+    import argparse as _ap
+    import torch
+    from top_routing_expert_amd import binding as B
+
+    out = {}
+    if shape.dtype != "bf16":
+        return out
+    try:
+        va = _ap.Namespace(**vars(a))
+        va.dispatch, va.no_flush_pass = "fp8gemm", True
+        va.steps, va.warmup = min(a.steps, 10), min(a.warmup, 3)
+        rec, _ = run_forward(shape, va, inp, copy_gbs, headline=False)
+        ph = rec["phases"]["ffn_gate_up"]
+        out["fp8_first_gemm"] = dict(
+            value=rec["value"], unit="tokens/s", ms_per_step=rec["ms_per_step"],
+            ffn_gate_up_ms=ph["ms"], ffn_gate_up_tflops=ph.get("tflops", ph.get("achieved")),
+            ffn_gate_up_frac_of_fp8_peak=ph.get("mfma_frac", ph.get("frac")),
+            roofline=rec["roofline"], steps=va.steps,
+            note="per-token E4M3 codes x per-output-channel E4M3 gate/up weights; bf16 down")
+    except Exception as e:  # pragma: no cover
+        out["fp8_first_gemm"] = {"error": repr(e)}
+    try:
+        log(f"{shape.name}: expert waves")
+        ctx = prepare(shape, inp)
+        cfg, dev, buf = ctx["cfg"], ctx["dev"], ctx["buf"]
+        pgu, pd = ctx["packed"]
+        ws = B.workspace(cfg, "layer")
+        bufs = {n: buf[n] for n in ("logits", "topk_idx", "topk_w", "expert_offsets",
+                                    "rank_offsets", "slot_of", "src_of", "h", "y_perm")}
+        aux = torch.cuda.Stream()  # default priority
+        runs = {"serial": lambda: B.moe_layer_fwd_packed(cfg, dev["x"], dev["w_router"],
+                                                         dev["bias"], pgu, pd, buf["out"], bufs,
+                                                         ws)}
+        for W in (2, 4):
+            if shape.E % W == 0:
+                runs[f"{W}_waves"] = (lambda W=W: B.moe_layer_fwd_packed_waved(
+                    cfg, dev["x"], dev["w_router"], dev["bias"], pgu, pd, buf["out"], bufs, ws,
+                    n_waves=W, aux_stream=aux))
+        for f in runs.values():
+            f()
+            f()
+        torch.cuda.synchronize()
+        ms = {k: [] for k in runs}
+        for _ in range(5):
+            for k, f in runs.items():
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                ev[0].record()
+                for _ in range(4):
+                    f()
+                ev[1].record()
+                torch.cuda.synchronize()
+                ms[k].append(ev[0].elapsed_time(ev[1]) / 4)
+        med = {k: round(sorted(v)[len(v) // 2], 5) for k, v in ms.items()}
+        out["expert_waves"] = dict(ms_per_layer=med, unit="ms",
+                                   note="moe_layer_fwd_packed vs moe_layer_fwd_packed_waved "
+                                        "(two streams), median of 5 x 4 calls")
+        del ctx
+    except Exception as e:  # pragma: no cover
+        out["expert_waves"] = {"error": repr(e)}
+    return out
+
+
 def main(argv=None):
     a = parse(argv)
     if a.gpus != 1:
@@ -582,6 +657,7 @@ def main(argv=None):
     log(f"workload {shape.name}: generating inputs")
     inp = I.make_inputs(shape, seed=seed_of(shape))
     rec, idx_gpu = run_forward(shape, a, inp, copy_gbs)
+    variants = time_variants(shape, a, inp, copy_gbs) if a.variants == "all" else None
     cpu = flips = None
     if a.cpu_tokens > 0:
         log(f"oracle leg: CPU baseline on {a.cpu_tokens} tokens, routing flips over all tokens")
@@ -627,6 +703,8 @@ def main(argv=None):
         "measured_copy_gbs": round(copy_gbs, 1),
         "workloads": others,
     }
+    if variants is not None:
+        res["variants"] = variants
     print(json.dumps(res), flush=True)
 
 
