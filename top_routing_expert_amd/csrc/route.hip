@@ -16,9 +16,10 @@
 //    bitwise reproducible (no float atomics) while the grid still covers the
 //    256 CUs.
 //  * Top-k: a group of LPT = min(64, pow2 >= E) lanes per token (32 for
-//    64 < E <= 256 with at most 32 groups); each lane holds E/LPT scores.  Every selection round is one argmax over 64-bit keys
-//    (order-preserving score bits, then inverted index), reduced with xor
-//    shuffles: highest score wins, ties go to the lowest expert index.
+//    64 < E <= 256 with at most 32 groups); each lane holds E/LPT scores.
+//    Every selection round is one argmax over 64-bit keys (order-preserving
+//    score bits, then inverted index), reduced with xor shuffles: highest
+//    score wins, ties go to the lowest expert index.
 #include "common.h"
 
 namespace moe {
