@@ -138,6 +138,8 @@ CASES = [
     (8, 256, 448, 700, 2),
     (64, 128, 192, 1500, 2),
     (16, 512, 1088, 2048, 2),
+    # many experts over several 64-expert chunks, most with a few rows or none
+    (512, 128, 128, 600, 4),
 ]
 
 
