@@ -71,6 +71,25 @@ def test_route_skinny_shapes(over):
     _check_route(shape, inp, buf)
 
 
+# E <= 16 routers on short batches: one token, a ragged last block of tokens,
+# wide and narrow d, bias without renormalisation, every lane count of the
+# selection
+SMALL_BATCH_SHAPES = [dict(E=8, k=2, T=1, d=512), dict(E=3, k=2, T=7, d=1024),
+                      dict(E=16, k=2, T=2048, d=4096), dict(E=12, k=3, T=333, d=3584, renorm=0, bias="normal"),
+                      dict(E=2, k=1, T=64, d=1536), dict(E=5, k=4, T=1030, d=2560)]
+
+
+@pytest.mark.parametrize("over", SMALL_BATCH_SHAPES, ids=[str(o) for o in SMALL_BATCH_SHAPES])
+def test_route_short_batches(over):
+    over = dict(over)
+    shape = C.E8_D4096.replace(name="route-small", ep_ranks=1, **{"renorm": 1, **over})
+    log(f"[route] short batch {over}")
+    inp = I.make_inputs(shape, seed=31, with_experts=False)
+    dev, buf = upload(inp), alloc(shape)
+    _route(shape, dev, buf)
+    _check_route(shape, inp, buf)
+
+
 @pytest.mark.parametrize("key", list(C.SMALL), ids=list(C.SMALL))
 def test_route_small_shapes(key):
     shape = C.SMALL[key]
