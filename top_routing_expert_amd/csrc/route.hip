@@ -273,7 +273,7 @@ int router_splits(const moe_config& c) {
     return (int)(s < 1 ? 1 : s);
   }
   const int nch = c.d / 64;
-  const int ec = c.E <= 16 ? 16 : c.E <= 32 ? 32 : c.E <= 64 ? 64 : c.E <= 128 ? 128 : 256;
+  const int ec = c.E <= 32 ? 32 : c.E <= 64 ? 64 : c.E <= 128 ? 128 : 256;
   const long tiles = (long)div_up(c.T, 64) * div_up(c.E, ec);
   // blocks to aim for: each split adds T x E fp32 partials that the top-k
   // kernel reads back (measured best: 256 for E <= 64, 512 for E = 256)
@@ -292,10 +292,9 @@ hipError_t launch_router_gemm_bf16(const uint16_t* x, const uint16_t* wr, float*
                                                                            splits);
     return hipGetLastError();
   }
-  const int ec = E <= 16 ? 16 : E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256;
+  const int ec = E <= 32 ? 32 : E <= 64 ? 64 : E <= 128 ? 128 : 256;  // E > 16 here
   dim3 grid(div_up(T, 64), splits, div_up(E, ec));
   switch (ec) {
-    case 16: router_gemm_bf16_kernel<16><<<grid, 256, 0, st>>>(x, wr, dst, T, d, E, splits); break;
     case 32: router_gemm_bf16_kernel<32><<<grid, 256, 0, st>>>(x, wr, dst, T, d, E, splits); break;
     case 64: router_gemm_bf16_kernel<64><<<grid, 256, 0, st>>>(x, wr, dst, T, d, E, splits); break;
     case 128: router_gemm_bf16_kernel<128><<<grid, 256, 0, st>>>(x, wr, dst, T, d, E, splits); break;
