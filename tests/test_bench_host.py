@@ -94,3 +94,19 @@ def test_committed_traffic_is_used_only_for_its_workload_dispatch_and_sources(tm
     p.write_text(json.dumps(stale))
     monkeypatch.setitem(bench.FFN_KERNELS, "packed", (str(p), srcs, name))
     assert bench.measured_traffic("packed", E256, "gather") is None
+
+
+def test_a_failing_variant_is_recorded_not_raised(monkeypatch):
+    """The variants run after the line's own measurement: an error in one of
+    them is written into the record and the line is still printed."""
+    def boom(*a, **k):
+        raise RuntimeError("variant failed")
+
+    monkeypatch.setattr(bench, "run_forward", boom)
+    monkeypatch.setattr(bench, "prepare", boom)
+    a = bench.parse([])
+    out = bench.time_variants(C.BY_NAME[E256], a, None, None)
+    assert set(out) == {"fp8_first_gemm", "expert_waves"}
+    assert all("variant failed" in v["error"] for v in out.values())
+    # the fp32 workload has no bf16 variants
+    assert bench.time_variants(C.CONFIGS[0], a, None, None) == {}
